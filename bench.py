@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark of the SSD hot path on one MI355X (gfx950).
+
+A step is one ssd_chunk_scan_fwd call (discretisation, in-chunk decay scan, steps 1-4
+of the chunked SSD algorithm) over the Mamba-2-2.7B-shaped layer at L=2048
+(batch 4, 80 heads, headdim 64, dstate 128, 1 group, chunk 256, bf16 I/O, fp32
+state).  Inputs are seeded synthetic data resident in HBM before timing starts.  To
+keep the 256 MB Infinity Cache from serving a step's inputs out of cache, the steps
+rotate over several identical copies of the inputs whose total exceeds the cache.
+
+Printed: one JSON line with the contract fields plus
+  roofline      algorithmic bytes of one call / its mean event-timed duration
+                (the call's kernels run back to back on one stream), against 8 TB/s
+  cpu_baseline  the fp64 CPU oracle timed on this host's cores
+  L16k          the long-context layer (L=16384, nonzero initial state)
+  verify        the K=4 verify step (GB/s of algorithmic bytes)
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SSD fwd tokens/s per layer at L=2k/16k; % MFMA/HBM roofline; verify-step GB/s"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 << 20
+
+
+def scan_alg_bytes(d, io_bytes, init):
+    """Bytes the method must move: x, y, dt, B, C, A, D, final state (+ initial state)."""
+    tokens = d["b"] * d["L"]
+    per_tok = d["H"] * d["P"] * io_bytes * 2 + 4 * d["H"] + 2 * d["G"] * d["N"] * io_bytes
+    state = d["b"] * d["H"] * d["P"] * d["N"] * 4
+    return tokens * per_tok + 8 * d["H"] + state * (2 if init else 1)
+
+
+def scan_alg_flops(d):
+    """2 x MACs of the causal chunked algorithm (C B^T per group, Y_diag, S, Y_off)."""
+    b, L, H, P, N, G, Q = (d[k] for k in ("b", "L", "H", "P", "N", "G", "Q"))
+    macs = 0
+    for c in range(math.ceil(L / Q)):
+        q = min(Q, L - c * Q)
+        tri = q * (q + 1) // 2
+        macs += G * tri * N + H * (tri * P + 2 * q * P * N)
+    return 2 * b * macs
+
+
+def verify_alg_bytes(d, io_bytes):
+    b, K, H, P, N, G = (d[k] for k in ("b", "K", "H", "P", "N", "G"))
+    state = b * H * P * N * 4
+    return (2 * state + 2 * b * K * H * P * io_bytes + b * K * H * 4 +
+            2 * b * K * G * N * io_bytes + 4 * b + 8 * H)
+
+
+def _copies(inp, count, bd):
+    sets = []
+    for _ in range(count):
+        sets.append({k: bd.to_device(getattr(inp, k))
+                     for k in ("x", "dt", "A", "B", "C", "D", "init_state")})
+    return sets
+
+
+def time_scan(name, steps, warmup, bd, inputs, torch):
+    inp = inputs.make_workload(name)
+    d = inp.dims
+    io_bytes = 2 if inp.io == "bf16" else 4
+    alg = scan_alg_bytes(d, io_bytes, inp.init_state is not None)
+    footprint = alg + d["b"] * d["L"] * d["H"] * d["P"] * io_bytes
+    nsets = max(2, math.ceil(3 * MALL_BYTES / footprint))
+    sets = _copies(inp, nsets, bd)
+    ys = [torch.empty_like(s["x"]) for s in sets]
+    fss = [torch.empty((d["b"], d["H"], d["P"], d["N"]), dtype=torch.float32, device="cuda")
+           for _ in sets]
+    ws = bd.chunk_scan_workspace(sets[0]["x"], sets[0]["B"], d["Q"])
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        s = sets[i % nsets]
+        bd.ssd_chunk_scan_fwd(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"], s["init_state"],
+                              ys[i % nsets], fss[i % nsets], d["Q"], ws, stream)
+
+    for i in range(warmup):
+        call(i)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        call(warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = sorted(a.elapsed_time(b) for a, b in ev)          # ms
+    mean_ms = sum(durs) / len(durs)
+    return dict(inp=inp, dims=d, alg_bytes=alg, flops=scan_alg_flops(d), wall_s=wall,
+                ms_per_step=wall * 1e3 / steps, call_ms_mean=mean_ms,
+                call_ms_median=durs[len(durs) // 2], nsets=nsets)
+
+
+def time_verify(steps, warmup, bd, inputs, torch):
+    v = inputs.make_workload("verify_b32_K4")
+    d = v.dims
+    io_bytes = 2 if v.io == "bf16" else 4
+    alg = verify_alg_bytes(d, io_bytes)
+    nsets = max(2, math.ceil(3 * MALL_BYTES / alg))
+    sets = []
+    for _ in range(nsets):
+        t = {k: bd.to_device(getattr(v, k)) for k in ("state", "x", "dt", "A", "B", "C", "D",
+                                                       "accept_len")}
+        t["y"] = torch.empty_like(t["x"])
+        t["out"] = torch.empty_like(t["state"])
+        sets.append(t)
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        t = sets[i % nsets]
+        bd.ssd_verify_step(t["state"], t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"],
+                           t["accept_len"], t["y"], t["out"], None, None, stream)
+
+    for i in range(warmup):
+        call(i)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        call(warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    durs = sorted(a.elapsed_time(b) for a, b in ev)
+    mean_ms = sum(durs) / len(durs)
+    return dict(dims=d, alg_bytes=alg, call_ms_mean=mean_ms, call_ms_median=durs[len(durs) // 2],
+                gbs=alg / (mean_ms * 1e-3) / 1e9)
+
+
+def cpu_baseline(inp, max_units=None):
+    """The fp64 oracle (as is) over (batch, head) units on a thread pool of host cores."""
+    import concurrent.futures
+
+    import oracle
+    d = inp.dims
+    units = d["b"] * d["H"]
+    sample = units if max_units is None else min(units, max_units)
+    threads = max(1, min(16, os.cpu_count() or 1, sample))
+    x, dt, A, B, C, D = (getattr(inp, k).f64() for k in ("x", "dt", "A", "B", "C", "D"))
+    init = None if inp.init_state is None else inp.init_state.f64()
+    oracle.scan_f64(x[:, :8], dt[:, :8], A, B[:, :8], C[:, :8], D, init, bh_range=(0, 1))
+    t0 = time.perf_counter()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(lambda u: oracle.scan_f64(x, dt, A, B, C, D, init, bh_range=(u, u + 1)),
+                    range(sample)))
+    wall = time.perf_counter() - t0
+    tokens = d["b"] * d["L"] * sample / units
+    return {"value": tokens / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{sample} of {units} (batch, head) units of the same workload, "
+                      f"tokens scaled by {sample}/{units}; wall {wall:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mamba2_2p7b_L2k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the L=16k and verify-step measurements")
+    ap.add_argument("--sweep", action="store_true", help="also time the dstate sweep")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from selective_state_space_ssd_amd import binding as bd
+    from selective_state_space_ssd_amd import inputs
+    bd.lib()
+    torch.cuda.set_device(0)
+
+    r = time_scan(args.workload, args.steps, args.warmup, bd, inputs, torch)
+    d = r["dims"]
+    tokens = d["b"] * d["L"]
+    achieved = r["alg_bytes"] / (r["call_ms_mean"] * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": tokens / (r["ms_per_step"] * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if r["inp"].io == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": d["b"], "seqlen": d["L"],
+                   "nheads": d["H"], "headdim": d["P"], "dstate": d["N"], "ngroups": d["G"],
+                   "chunk": d["Q"], "io": r["inp"].io, "state": "f32",
+                   "input_copies_rotated": r["nsets"]},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "ssd_chunk_scan_fwd (k_chunk_state + k_state_pass + k_chunk_out)",
+                     "alg_bytes_per_launch": r["alg_bytes"],
+                     "call_ms_mean": r["call_ms_mean"], "call_ms_median": r["call_ms_median"],
+                     "mfma_tflops_alg": r["flops"] / (r["call_ms_mean"] * 1e-3) / 1e12,
+                     "mfma_frac_alg": r["flops"] / (r["call_ms_mean"] * 1e-3) / 1e12 /
+                     BF16_PEAK_TFLOPS},
+    }
+    if not args.no_extra:
+        r2 = time_scan("mamba2_2p7b_L16k", max(5, args.steps // 3), 2, bd, inputs, torch)
+        d2 = r2["dims"]
+        a2 = r2["alg_bytes"] / (r2["call_ms_mean"] * 1e-3) / 1e9
+        out["L16k"] = {"tokens_per_s": d2["b"] * d2["L"] / (r2["call_ms_mean"] * 1e-3),
+                       "call_ms_mean": r2["call_ms_mean"], "achieved_GBs": a2,
+                       "hbm_frac": a2 / HBM_PEAK_GBS}
+        rv = time_verify(max(10, args.steps), 3, bd, inputs, torch)
+        out["verify"] = {"workload": "verify_b32_K4", "GB_per_s": rv["gbs"],
+                         "hbm_frac": rv["gbs"] / HBM_PEAK_GBS, "call_ms_mean": rv["call_ms_mean"],
+                         "alg_bytes": rv["alg_bytes"]}
+    if args.sweep:
+        sw = {}
+        for n in (16, 64, 128, 256):
+            rs = time_scan(f"dstate_sweep_N{n}", max(5, args.steps // 3), 2, bd, inputs, torch)
+            ds = rs["dims"]
+            a = rs["alg_bytes"] / (rs["call_ms_mean"] * 1e-3) / 1e9
+            sw[f"N{n}"] = {"tokens_per_s": ds["b"] * ds["L"] / (rs["call_ms_mean"] * 1e-3),
+                           "call_ms_mean": rs["call_ms_mean"], "hbm_frac": a / HBM_PEAK_GBS}
+        out["dstate_sweep"] = sw
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(r["inp"])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,159 @@
+/*
+ * ssd_mi355x.h -- C ABI of the MI355X (gfx950) SSD hot-path library.
+ *
+ * Two operations of a Mamba-2 SSD (state space duality) layer:
+ *
+ *   ssd_chunk_scan_fwd  the selective scan of a whole sequence, computed with the
+ *                       chunked block decomposition of the semiseparable sequence
+ *                       map (Mamba-2 article (msbhsh.com), «SSD 算法：分块矩阵分解»
+ *                       and «SSD 算法：分块和形态传递»);
+ *   ssd_verify_step     the recurrent update over K draft tokens that a target model
+ *                       runs when it verifies speculative-decoding drafts, handing
+ *                       back the state at the accepted position ("如何将 Llama 变成
+ *                       Mamba？研究人员推出新工作并提高推理速度", «推测解码»).
+ *
+ * Both compute, per batch row b and head h (group g = h / (H/G)):
+ *
+ *   h_t = exp(dt_t * A_h) * h_{t-1} + dt_t * x_t (outer) B_t      state [P x N]
+ *   y_t = C_t . h_t + D_h * x_t                                    (sum over N)
+ *
+ * ("另辟蹊径--Mamba介绍", «The Recurrent Representation»: the output reads the
+ * updated state; «What is a State Space Model?»: D is a skip term; Bi-Mamba page,
+ * «Preliminary: Mamba Series»: in SSD, A is one scalar per head.)  dt is taken as
+ * given: no softplus, bias or clamp is applied inside the library.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every array pointer is a DEVICE pointer to row-major contiguous memory, owned
+ *   by the caller.  The library never allocates or frees device memory and keeps
+ *   no global state; calls are re-entrant and thread-safe.
+ * - x, B, C and y have the I/O element type `io` (fp32 or bf16 bit patterns);
+ *   dt, A, D and every state are fp32; accept_len is int32.
+ * - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream) and
+ *   the call returns without waiting.  Kernel faults surface on a later
+ *   synchronisation, as for any HIP launch.
+ * - Arguments are checked on the host before anything is enqueued; a failed
+ *   check returns its status and enqueues nothing.  SSD_ERR_HIP reports a launch
+ *   error returned by the HIP runtime.  No C++ exception crosses the ABI.
+ * - NaN or Inf in the inputs propagate to the outputs; they are not checked.
+ */
+#ifndef SSD_MI355X_H
+#define SSD_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL_ARG = 1,     /* a required pointer is NULL                          */
+    SSD_ERR_BAD_DIM = 2,      /* a dimension is negative / zero where it must not be */
+    SSD_ERR_GROUPS = 3,       /* H is not a multiple of G                            */
+    SSD_ERR_UNSUPPORTED = 4,  /* shape / chunk size / dtype this build does not run  */
+    SSD_ERR_ALIGN = 5,        /* a pointer is not 16-byte aligned                    */
+    SSD_ERR_WORKSPACE = 6,    /* workspace missing or smaller than required          */
+    SSD_ERR_ALIAS = 7,        /* outputs overlap inputs in a way that is not allowed */
+    SSD_ERR_HIP = 8           /* the HIP runtime reported an error                   */
+} ssd_status_t;
+
+typedef enum {
+    SSD_DTYPE_F32 = 0,        /* x, B, C, y are float                                */
+    SSD_DTYPE_BF16 = 1        /* x, B, C, y are bfloat16 (uint16 bit patterns); the
+                                 MFMA operands are bf16 with fp32 accumulation       */
+} ssd_dtype_t;
+
+/*
+ * Workspace size in bytes that ssd_chunk_scan_fwd needs for these dimensions
+ * (0 for an empty problem).  Returns (size_t)-1 when the dimensions are invalid.
+ */
+size_t ssd_chunk_scan_workspace_bytes(int b, int L, int H, int P, int N, int G, int Q,
+                                      ssd_dtype_t io);
+
+/*
+ * ssd_chunk_scan_fwd -- SSD chunked scan over a whole sequence.
+ *
+ * Method (Mamba-2 article, «SSD 算法：分块和形态传递»): the sequence is cut into
+ * chunks of Q tokens; (1) inside each chunk the outputs are the quadratic,
+ * attention-like masked form (C B^T o L)(dt o x); (2) each chunk's own state
+ * contribution sum_s exp(sum of a after s) dt_s x_s (outer) B_s; (3) a short scan
+ * over chunks passes the state on, H_c = exp(sum of a over chunk c) H_{c-1} + S_c;
+ * (4) the state entering a chunk reaches its outputs through C.  Steps 1, 2 and 4
+ * run on the matrix cores, step 3 is the only sequential part.  The result equals
+ * the token-by-token recurrence above for every Q (up to rounding).
+ *
+ * Arguments (all device pointers):
+ *   x          [b, L, H, P]  io       input per token and head
+ *   dt         [b, L, H]     fp32     step size per token and head (> 0 expected)
+ *   A          [H]           fp32     scalar state decay rate per head (< 0 expected)
+ *   B, C       [b, L, G, N]  io       input / output projections, shared by the H/G
+ *                                     heads of each group (head h reads group h/(H/G))
+ *   D          [H]           fp32     skip term per head
+ *   init_state [b, H, P, N]  fp32     state before token 0; NULL means zeros
+ *   y          [b, L, H, P]  io       output (written)
+ *   final_state[b, H, P, N]  fp32     state after token L-1 (written); NULL = skip
+ *   Q                                 chunk length: 64, 128 or 256 (the last chunk
+ *                                     may be shorter: L need not be a multiple of Q)
+ *   workspace, workspace_bytes        scratch of at least
+ *                                     ssd_chunk_scan_workspace_bytes(...) bytes,
+ *                                     16-byte aligned; its contents on entry are
+ *                                     ignored and on exit undefined
+ * Supported on this build: P in {16, 32, 64, 128}, N a multiple of 16 in [16, 256],
+ * and the chunk tiles must fit the 160 KiB LDS of one CU (else
+ * SSD_ERR_UNSUPPORTED).  b == 0 or L == 0 is a valid empty problem (final_state
+ * then equals init_state, or zeros).  Every pointer must be 16-byte aligned except
+ * dt, A, D (4-byte).  y must not overlap any input.
+ */
+ssd_status_t ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, const void *B,
+                                const void *C, const float *D, const float *init_state, void *y,
+                                float *final_state, int b, int L, int H, int P, int N, int G,
+                                int Q, ssd_dtype_t io, void *workspace, size_t workspace_bytes,
+                                void *hip_stream);
+
+/*
+ * ssd_verify_step -- K draft tokens applied to an existing state.
+ *
+ * Mamba keeps only its current state, so a verifier that may reject part of the
+ * draft must keep the state at the accepted position for rollback ("如何将 Llama
+ * 变成 Mamba？...", «推测解码»).  For every (b, h), starting from state_in, the
+ * recurrence above runs over k = 1..K; y is written for all K positions.
+ *
+ * Arguments (all device pointers):
+ *   state_in   [b, H, P, N]     fp32   state before the first draft token
+ *   x          [b, K, H, P]     io
+ *   dt         [b, K, H]        fp32
+ *   A          [H]              fp32
+ *   B, C       [b, K, G, N]     io
+ *   D          [H]              fp32
+ *   accept_len [b]              int32  accepted draft tokens a_b in [0, K]
+ *   y          [b, K, H, P]     io     outputs for all K positions (written)
+ *   state_out  [b, H, P, N]     fp32   state after a_b tokens (written); a_b = 0
+ *                                      copies state_in bit for bit.  May equal
+ *                                      state_in exactly (in-place update).
+ *   states_all [b, K, H, P, N]  fp32   NULL, or the state after each of the K tokens
+ *   err_flag   int32            NULL, or a device word set to 1 when some
+ *                                      accept_len lies outside [0, K] (that value is
+ *                                      clamped into range); never cleared here
+ * Supported: K in [1, 16], N in {16, 32, 64, 128, 256}, any P >= 1.  state_in,
+ * state_out and states_all must be 16-byte aligned; state_out must not partially
+ * overlap state_in, and states_all must not overlap either.
+ */
+ssd_status_t ssd_verify_step(const float *state_in, const void *x, const float *dt,
+                             const float *A, const void *B, const void *C, const float *D,
+                             const int32_t *accept_len, void *y, float *state_out,
+                             float *states_all, int32_t *err_flag, int b, int K, int H, int P,
+                             int N, int G, ssd_dtype_t io, void *hip_stream);
+
+/* Static, human-readable name of a status code. */
+const char *ssd_status_string(ssd_status_t status);
+
+/* Static version string of the library, e.g. "ssd_mi355x 0.1.0 gfx950". */
+const char *ssd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_MI355X_H */

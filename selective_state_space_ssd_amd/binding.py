@@ -1,0 +1,192 @@
+"""Thin Python binding of libssd_mi355x.so (the C ABI in include/ssd_mi355x.h).
+
+The functions named like the C entry points (``ssd_chunk_scan_fwd``,
+``ssd_verify_step``, ...) only marshal torch tensors into pointers and sizes and
+raise on a non-OK status; all computation happens in the HIP kernels.  The
+convenience wrappers ``chunk_scan_fwd`` and ``verify_step`` additionally allocate
+the outputs and the workspace with torch.  There is no fallback: if the library is
+not built, or a tensor is not on the GPU, a call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssd_mi355x.so")
+
+SSD_DTYPE_F32 = 0
+SSD_DTYPE_BF16 = 1
+
+STATUS_NAMES = {
+    0: "SSD_OK", 1: "SSD_ERR_NULL_ARG", 2: "SSD_ERR_BAD_DIM", 3: "SSD_ERR_GROUPS",
+    4: "SSD_ERR_UNSUPPORTED", 5: "SSD_ERR_ALIGN", 6: "SSD_ERR_WORKSPACE", 7: "SSD_ERR_ALIAS",
+    8: "SSD_ERR_HIP",
+}
+
+# Every symbol declared in include/ssd_mi355x.h
+EXPORTED = ("ssd_chunk_scan_workspace_bytes", "ssd_chunk_scan_fwd", "ssd_verify_step",
+            "ssd_status_string", "ssd_version")
+
+_lib = None
+
+
+class SSDError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} "
+                         f"({lib().ssd_status_string(status).decode()})")
+
+
+def lib() -> ctypes.CDLL:
+    """Open libssd_mi355x.so (built in-tree by selective_state_space_ssd_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run "
+                               "`python -m selective_state_space_ssd_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.ssd_chunk_scan_workspace_bytes.argtypes = [i32] * 7 + [i32]
+        L.ssd_chunk_scan_workspace_bytes.restype = sz
+        L.ssd_chunk_scan_fwd.argtypes = [vp] * 9 + [i32] * 7 + [i32, vp, sz, vp]
+        L.ssd_chunk_scan_fwd.restype = i32
+        L.ssd_verify_step.argtypes = [vp] * 12 + [i32] * 6 + [i32, vp]
+        L.ssd_verify_step.restype = i32
+        L.ssd_status_string.argtypes = [i32]
+        L.ssd_status_string.restype = ctypes.c_char_p
+        L.ssd_version.argtypes = []
+        L.ssd_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def ssd_version() -> str:
+    return lib().ssd_version().decode()
+
+
+def ssd_status_string(status: int) -> str:
+    return lib().ssd_status_string(status).decode()
+
+
+def _io_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SSD_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return SSD_DTYPE_BF16
+    raise TypeError(f"x/B/C/y must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def ssd_chunk_scan_workspace_bytes(b, L, H, P, N, G, Q, io: int) -> int:
+    n = lib().ssd_chunk_scan_workspace_bytes(b, L, H, P, N, G, Q, io)
+    if n == ctypes.c_size_t(-1).value:
+        raise SSDError(2, "ssd_chunk_scan_workspace_bytes")
+    return n
+
+
+def ssd_chunk_scan_fwd(x, dt, A, B, C, D, init_state, y, final_state, Q, workspace,
+                       stream=None) -> None:
+    """Enqueue the chunked scan on ``stream`` (default: torch's current stream).
+
+    x[b,L,H,P], B/C[b,L,G,N], y[b,L,H,P] share one dtype (float32 or bfloat16);
+    dt[b,L,H], A[H], D[H], init_state/final_state[b,H,P,N] are float32
+    (init_state and final_state may be None); workspace is a uint8 tensor of at
+    least ssd_chunk_scan_workspace_bytes(...) bytes.
+    """
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    io = _io_code(x)
+    f32 = torch.float32
+    st = lib().ssd_chunk_scan_fwd(
+        _ptr(x, "x", x.dtype), _ptr(dt, "dt", f32), _ptr(A, "A", f32), _ptr(B, "B", x.dtype),
+        _ptr(C, "C", x.dtype), _ptr(D, "D", f32), _ptr(init_state, "init_state", f32),
+        _ptr(y, "y", x.dtype), _ptr(final_state, "final_state", f32), b, L, H, P, N, G, Q, io,
+        _ptr(workspace, "workspace"), 0 if workspace is None else workspace.numel() *
+        workspace.element_size(), _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_chunk_scan_fwd")
+
+
+def ssd_verify_step(state_in, x, dt, A, B, C, D, accept_len, y, state_out, states_all=None,
+                    err_flag=None, stream=None) -> None:
+    """Enqueue the verify step on ``stream`` (default: torch's current stream)."""
+    b, K, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    io = _io_code(x)
+    f32 = torch.float32
+    st = lib().ssd_verify_step(
+        _ptr(state_in, "state_in", f32), _ptr(x, "x", x.dtype), _ptr(dt, "dt", f32),
+        _ptr(A, "A", f32), _ptr(B, "B", x.dtype), _ptr(C, "C", x.dtype), _ptr(D, "D", f32),
+        _ptr(accept_len, "accept_len", torch.int32), _ptr(y, "y", x.dtype),
+        _ptr(state_out, "state_out", f32), _ptr(states_all, "states_all", f32),
+        _ptr(err_flag, "err_flag", torch.int32), b, K, H, P, N, G, io, _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_verify_step")
+
+
+# ------------------------------------------------------------ allocating wrappers
+def chunk_scan_workspace(x, B, Q) -> torch.Tensor:
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    n = ssd_chunk_scan_workspace_bytes(b, L, H, P, N, G, Q, _io_code(x))
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=x.device)
+
+
+def chunk_scan_fwd(x, dt, A, B, C, D, Q, init_state=None, workspace=None, stream=None):
+    """Allocate y, final_state (and the workspace if not given); returns (y, final_state)."""
+    b, L, H, P = x.shape
+    N = B.shape[3]
+    y = torch.empty_like(x)
+    final_state = torch.empty((b, H, P, N), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = chunk_scan_workspace(x, B, Q)
+    ssd_chunk_scan_fwd(x, dt, A, B, C, D, init_state, y, final_state, Q, workspace, stream)
+    return y, final_state
+
+
+def verify_step(state, x, dt, A, B, C, D, accept_len, return_all_states=False, stream=None):
+    """Allocate outputs; returns (y, state_out) or (y, state_out, states_all)."""
+    b, K, H, P = x.shape
+    N = B.shape[3]
+    y = torch.empty_like(x)
+    state_out = torch.empty_like(state)
+    states_all = (torch.empty((b, K, H, P, N), dtype=torch.float32, device=x.device)
+                  if return_all_states else None)
+    ssd_verify_step(state, x, dt, A, B, C, D, accept_len, y, state_out, states_all, None, stream)
+    return (y, state_out, states_all) if return_all_states else (y, state_out)
+
+
+def to_device(arr, device="cuda"):
+    """Move one generator array (selective_state_space_ssd_amd.inputs.Tensor or an
+    ndarray) to the GPU in its storage type."""
+    import numpy as np
+
+    from .inputs import Tensor
+    if arr is None:
+        return None
+    if isinstance(arr, Tensor):
+        if arr.dtype == "bf16":
+            return torch.from_numpy(arr.data.view(np.int16)).view(torch.bfloat16).to(device)
+        return torch.from_numpy(arr.data).to(device)
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(device)

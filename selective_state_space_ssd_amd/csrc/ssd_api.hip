@@ -1,0 +1,161 @@
+// ssd_api.hip -- the C ABI declared in include/ssd_mi355x.h: host-side argument
+// checks, workspace planning and dispatch to the gfx950 kernels.  Every check runs
+// before anything is enqueued; a failed check enqueues nothing.
+#include <stdint.h>
+
+#include "ssd_kernels.h"
+#include "ssd_mi355x.h"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+    uintptr_t lo = 0, hi = 0;   // [lo, hi); empty when lo == hi
+    Range() = default;
+    Range(const void *p, size_t bytes)
+        : lo(reinterpret_cast<uintptr_t>(p)), hi(reinterpret_cast<uintptr_t>(p) + (p ? bytes : 0)) {}
+    bool overlaps(const Range &o) const { return lo < o.hi && o.lo < hi; }
+    bool same(const Range &o) const { return lo == o.lo && hi == o.hi; }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char *ssd_status_string(ssd_status_t s) {
+    switch (s) {
+        case SSD_OK: return "SSD_OK";
+        case SSD_ERR_NULL_ARG: return "SSD_ERR_NULL_ARG: a required pointer is NULL";
+        case SSD_ERR_BAD_DIM: return "SSD_ERR_BAD_DIM: invalid dimension";
+        case SSD_ERR_GROUPS: return "SSD_ERR_GROUPS: H is not a multiple of G";
+        case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED: shape, chunk size or dtype not supported";
+        case SSD_ERR_ALIGN: return "SSD_ERR_ALIGN: pointer not suitably aligned";
+        case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace missing or too small";
+        case SSD_ERR_ALIAS: return "SSD_ERR_ALIAS: output overlaps an input";
+        case SSD_ERR_HIP: return "SSD_ERR_HIP: HIP runtime error";
+    }
+    return "unknown ssd_status_t";
+}
+
+const char *ssd_version(void) { return "ssd_mi355x 0.1.0 gfx950"; }
+
+size_t ssd_chunk_scan_workspace_bytes(int b, int L, int H, int P, int N, int G, int Q,
+                                      ssd_dtype_t io) {
+    if (b < 0 || L < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || Q <= 0) return size_t(-1);
+    if (io != SSD_DTYPE_F32 && io != SSD_DTYPE_BF16) return size_t(-1);
+    if (b == 0 || L == 0) return 0;
+    return ssd::plan_chunk_scan(b, L, H, P, N, G, Q, io == SSD_DTYPE_BF16).total;
+}
+
+ssd_status_t ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, const void *B,
+                                const void *C, const float *D, const float *init_state, void *y,
+                                float *final_state, int b, int L, int H, int P, int N, int G,
+                                int Q, ssd_dtype_t io, void *workspace, size_t workspace_bytes,
+                                void *hip_stream) {
+    if (io != SSD_DTYPE_F32 && io != SSD_DTYPE_BF16) return SSD_ERR_UNSUPPORTED;
+    if (b < 0 || L < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || Q <= 0) return SSD_ERR_BAD_DIM;
+    if (H % G != 0) return SSD_ERR_GROUPS;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    const size_t state_bytes = size_t(b) * H * P * N * sizeof(float);
+
+    if (b == 0 || L == 0) {   // empty sequence: final state is the initial state
+        if (final_state && b > 0) {
+            if (!aligned(final_state, 16) || (init_state && !aligned(init_state, 16)))
+                return SSD_ERR_ALIGN;
+            if (init_state && Range(init_state, state_bytes).overlaps(Range(final_state, state_bytes)) &&
+                !Range(init_state, state_bytes).same(Range(final_state, state_bytes)))
+                return SSD_ERR_ALIAS;
+            if (ssd::launch_copy_state(init_state, final_state, state_bytes / 4, stream) != hipSuccess)
+                return SSD_ERR_HIP;
+        }
+        return SSD_OK;
+    }
+    if (!x || !dt || !A || !B || !C || !D || !y) return SSD_ERR_NULL_ARG;
+
+    const bool bf16 = io == SSD_DTYPE_BF16;
+    const ssd::ChunkScanPlan plan = ssd::plan_chunk_scan(b, L, H, P, N, G, Q, bf16);
+    if (!plan.supported) return SSD_ERR_UNSUPPORTED;
+
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) ||
+        !aligned(init_state, 16) || !aligned(final_state, 16) || !aligned(workspace, 16) ||
+        !aligned(dt, 4) || !aligned(A, 4) || !aligned(D, 4))
+        return SSD_ERR_ALIGN;
+    if (!workspace || workspace_bytes < plan.total) return SSD_ERR_WORKSPACE;
+
+    const size_t esz = bf16 ? 2 : 4;
+    const Range rx(x, size_t(b) * L * H * P * esz), ry(y, size_t(b) * L * H * P * esz);
+    const Range rB(B, size_t(b) * L * G * N * esz), rC(C, size_t(b) * L * G * N * esz);
+    const Range rdt(dt, size_t(b) * L * H * 4), rA(A, size_t(H) * 4), rD(D, size_t(H) * 4);
+    const Range rinit(init_state, state_bytes), rfin(final_state, state_bytes);
+    const Range rws(workspace, plan.total);
+    const Range inputs[] = {rx, rB, rC, rdt, rA, rD, rinit};
+    for (const Range &in : inputs) {
+        if (ry.overlaps(in) || rws.overlaps(in)) return SSD_ERR_ALIAS;
+        // final_state may replace init_state in place, but may not clobber other inputs
+        if (&in != &inputs[6] && rfin.overlaps(in)) return SSD_ERR_ALIAS;
+    }
+    if (rfin.overlaps(rinit) && !rfin.same(rinit)) return SSD_ERR_ALIAS;
+    if (ry.overlaps(rfin) || ry.overlaps(rws) || rws.overlaps(rfin)) return SSD_ERR_ALIAS;
+
+    ssd::ChunkScanArgs a;
+    a.x = x; a.dt = dt; a.A = A; a.B = B; a.C = C; a.D = D;
+    a.init_state = init_state; a.y = y; a.final_state = final_state;
+    a.b = b; a.L = L; a.H = H; a.P = P; a.N = N; a.G = G; a.Q = Q;
+    a.bf16 = bf16;
+    a.workspace = workspace;
+    if (ssd::launch_chunk_scan(a, plan, stream) != hipSuccess) return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
+ssd_status_t ssd_verify_step(const float *state_in, const void *x, const float *dt,
+                             const float *A, const void *B, const void *C, const float *D,
+                             const int32_t *accept_len, void *y, float *state_out,
+                             float *states_all, int32_t *err_flag, int b, int K, int H, int P,
+                             int N, int G, ssd_dtype_t io, void *hip_stream) {
+    if (io != SSD_DTYPE_F32 && io != SSD_DTYPE_BF16) return SSD_ERR_UNSUPPORTED;
+    if (b < 0 || K <= 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0) return SSD_ERR_BAD_DIM;
+    if (H % G != 0) return SSD_ERR_GROUPS;
+    if (K > 16 || !ssd::verify_supported_n(N) || H > 65535 || b > 65535)
+        return SSD_ERR_UNSUPPORTED;
+    if (b == 0) return SSD_OK;
+    if (!state_in || !x || !dt || !A || !B || !C || !D || !accept_len || !y || !state_out)
+        return SSD_ERR_NULL_ARG;
+    const bool bf16 = io == SSD_DTYPE_BF16;
+    const size_t esz = bf16 ? 2 : 4;
+    if (!aligned(state_in, 16) || !aligned(state_out, 16) || !aligned(states_all, 16) ||
+        !aligned(B, 16) || !aligned(C, 16) || !aligned(x, esz) || !aligned(y, esz) ||
+        !aligned(dt, 4) || !aligned(A, 4) || !aligned(D, 4) || !aligned(accept_len, 4) ||
+        !aligned(err_flag, 4))
+        return SSD_ERR_ALIGN;
+
+    const size_t state_bytes = size_t(b) * H * P * N * 4;
+    const Range rin(state_in, state_bytes), rout(state_out, state_bytes);
+    const Range rall(states_all, state_bytes * K);
+    const Range rx(x, size_t(b) * K * H * P * esz), ry(y, size_t(b) * K * H * P * esz);
+    const Range rB(B, size_t(b) * K * G * N * esz), rC(C, size_t(b) * K * G * N * esz);
+    const Range rdt(dt, size_t(b) * K * H * 4), rA(A, size_t(H) * 4), rD(D, size_t(H) * 4);
+    const Range racc(accept_len, size_t(b) * 4), rerr(err_flag, 4);
+    if (rout.overlaps(rin) && !rout.same(rin)) return SSD_ERR_ALIAS;
+    const Range others[] = {rx, rB, rC, rdt, rA, rD, racc};
+    const Range outs[] = {rout, rall, ry, rerr};
+    for (const Range &o : outs)
+        for (const Range &i : others)
+            if (o.overlaps(i)) return SSD_ERR_ALIAS;
+    if (rall.overlaps(rin) || rall.overlaps(rout) || ry.overlaps(rin) || ry.overlaps(rout) ||
+        ry.overlaps(rall) || rerr.overlaps(rin) || rerr.overlaps(rout) || rerr.overlaps(rall) ||
+        rerr.overlaps(ry))
+        return SSD_ERR_ALIAS;
+
+    ssd::VerifyArgs a;
+    a.state_in = state_in; a.x = x; a.dt = dt; a.A = A; a.B = B; a.C = C; a.D = D;
+    a.accept_len = accept_len; a.y = y; a.state_out = state_out; a.states_all = states_all;
+    a.err_flag = err_flag;
+    a.b = b; a.K = K; a.H = H; a.P = P; a.N = N; a.G = G;
+    a.bf16 = bf16;
+    if (ssd::launch_verify(a, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+        return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
+}  // extern "C"

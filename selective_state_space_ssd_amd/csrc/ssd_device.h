@@ -1,0 +1,89 @@
+// ssd_device.h -- device-side building blocks shared by the gfx950 kernels.
+//
+// Element types: I/O tensors are either float or bfloat16 stored as uint16 bit
+// patterns.  Matrix-core tiles use the 16x16 MFMA shapes of CDNA4 with wave64:
+//   lane l: column/row index r16 = l & 15, lane group g4 = l >> 4 (0..3)
+//   accumulator (4 floats): element i is D[row 4*g4 + i][col r16]
+//   bf16 16x16x32: each lane supplies 8 bf16 of A (row r16) and 8 of B (col r16);
+//                  the k index of element j in lane group g4 is the same
+//                  function for A and B, so any consistent k assignment works
+//   fp32 16x16x4:  each lane supplies A[r16][k = g4] and B[k = g4][r16]
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace ssd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef uint16_t bf16_bits;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_bits v) {
+    return __uint_as_float(uint32_t(v) << 16);
+}
+
+// float -> bfloat16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ bf16_bits f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_bits((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return bf16_bits(u >> 16);
+}
+
+template <typename IO>
+__device__ __forceinline__ float to_f32(IO v) {
+    if constexpr (std::is_same_v<IO, float>) return v;
+    else return bf16_to_f32(v);
+}
+
+template <typename IO>
+__device__ __forceinline__ IO from_f32(float v) {
+    if constexpr (std::is_same_v<IO, float>) return v;
+    else return f32_to_bf16(v);
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// 16 bytes of bf16 bit patterns as an MFMA operand.
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Two 8-byte halves (4 bf16 each) as one MFMA operand.
+__device__ __forceinline__ bf16x8 as_bf16x8(uint2 lo, uint2 hi) {
+    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// Pack two floats into a 32-bit pair of bf16 (first value in the low half).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+// Inclusive prefix sum over a 256-thread block (4 waves).  `tmp` is LDS scratch
+// of at least 4 floats; the call contains two block barriers.
+__device__ __forceinline__ float block_inclusive_scan_256(float v, float *tmp) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        float o = __shfl_up(v, off, 64);
+        if (lane >= off) v += o;
+    }
+    if (lane == 63) tmp[wave] = v;
+    __syncthreads();
+    float add = 0.f;
+    for (int w = 0; w < wave; ++w) add += tmp[w];
+    __syncthreads();
+    return v + add;
+}
+
+}  // namespace ssd

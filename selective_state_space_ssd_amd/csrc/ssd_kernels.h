@@ -1,0 +1,67 @@
+// ssd_kernels.h -- host-side launch interface between the C ABI (ssd_api.hip) and
+// the kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssd {
+
+constexpr size_t kMaxLds = 160 * 1024;   // LDS per CU on gfx950
+
+struct VerifyArgs {
+    const float *state_in;
+    const void *x;
+    const float *dt;
+    const float *A;
+    const void *B;
+    const void *C;
+    const float *D;
+    const int32_t *accept_len;
+    void *y;
+    float *state_out;
+    float *states_all;
+    int32_t *err_flag;
+    int b, K, H, P, N, G;
+    bool bf16;
+};
+
+bool verify_supported_n(int N);
+hipError_t launch_verify(const VerifyArgs &a, hipStream_t stream);
+
+struct ChunkScanArgs {
+    const void *x;
+    const float *dt;
+    const float *A;
+    const void *B;
+    const void *C;
+    const float *D;
+    const float *init_state;
+    void *y;
+    float *final_state;
+    int b, L, H, P, N, G, Q;
+    bool bf16;
+    void *workspace;
+};
+
+// Sizes and workspace layout of one chunked-scan call.
+struct ChunkScanPlan {
+    int nc = 0;                 // number of chunks, ceil(L / Q)
+    size_t off_states = 0;      // fp32 [b, H, nc, P, N]: chunk states, step 2 output
+    size_t off_alpha = 0;       // fp32 [b, H, nc]: total decay of each chunk
+    size_t off_hprev = 0;       // io   [b, H, nc, P, N]: state entering each chunk
+    size_t total = 0;           // workspace bytes
+    size_t lds_state = 0;       // dynamic LDS of the chunk-state kernel
+    size_t lds_out = 0;         // dynamic LDS of the chunk-output kernel
+    bool supported = false;     // this build runs the shape
+};
+
+ChunkScanPlan plan_chunk_scan(int b, int L, int H, int P, int N, int G, int Q, bool bf16);
+hipError_t launch_chunk_scan(const ChunkScanArgs &a, const ChunkScanPlan &plan,
+                             hipStream_t stream);
+// final_state = init_state (or zeros) for an empty sequence.
+hipError_t launch_copy_state(const float *init_state, float *final_state, size_t count,
+                             hipStream_t stream);
+
+}  // namespace ssd

@@ -1,0 +1,149 @@
+// ssd_verify.hip -- verify step of speculative decoding on gfx950.
+//
+// K draft tokens are applied to an existing state per (batch, head); outputs are
+// written for every position and the state after the accepted number of tokens is
+// kept ("如何将 Llama 变成 Mamba？研究人员推出新工作并提高推理速度", «推测解码»:
+// Mamba holds only its current state, so the verifier must keep the state at the
+// position where the draft stops matching).
+//
+// The work is a stream over the state: every element is read once from HBM, updated
+// K times in registers and written once (plus once per position when all states are
+// requested).  Layout of the work: a row p of the P x N state is spread over LR
+// consecutive lanes, each holding J float4 chunks whose columns interleave so that
+// one load instruction of the wave covers whole 128-byte row segments; the
+// reduction y = C . h over N is an in-lane sum followed by log2(LR) lane
+// butterflies.
+#include "ssd_device.h"
+#include "ssd_kernels.h"
+
+namespace ssd {
+
+template <int N>
+struct VerifyShape {
+    static constexpr int LR = (N >= 32) ? 8 : N / 4;   // lanes per state row
+    static constexpr int J = N / (4 * LR);             // float4 chunks per lane
+    static constexpr int RW = 64 / LR;                 // rows per wave
+    static constexpr int RB = 4 * RW;                  // rows per 256-thread block
+    static_assert(J >= 1 && LR >= 1 && (N % (4 * LR)) == 0, "unsupported N");
+};
+
+template <typename IO>
+__device__ __forceinline__ float4 load4(const IO *p) {
+    if constexpr (std::is_same_v<IO, float>) {
+        return *reinterpret_cast<const float4 *>(p);
+    } else {
+        const uint2 v = *reinterpret_cast<const uint2 *>(p);
+        return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                           __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+    }
+}
+
+template <typename IO, int N>
+__global__ __launch_bounds__(256) void k_verify(
+    const float *state_in, const IO *__restrict__ x, const float *__restrict__ dt,
+    const float *__restrict__ A, const IO *__restrict__ B, const IO *__restrict__ C,
+    const float *__restrict__ D, const int32_t *__restrict__ accept_len, IO *__restrict__ y,
+    float *state_out, float *__restrict__ states_all, int32_t *err_flag, int K, int H, int P,
+    int G) {
+    using S = VerifyShape<N>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lr = lane % S::LR, rw = lane / S::LR;
+    const int p = blockIdx.x * S::RB + wave * S::RW + rw;
+    const int h = blockIdx.y, bi = blockIdx.z;
+    const int g = h / (H / G);
+    const bool valid = p < P;
+    const size_t bh = size_t(bi) * H + h;
+    const size_t row = (bh * P + (valid ? p : 0)) * N;
+
+    float4 s[S::J];
+#pragma unroll
+    for (int j = 0; j < S::J; ++j) {
+        const int n = j * 4 * S::LR + lr * 4;
+        s[j] = valid ? *reinterpret_cast<const float4 *>(state_in + row + n)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+
+    int a = accept_len[bi];
+    if (a < 0 || a > K) {
+        if (err_flag && blockIdx.x == 0 && h == 0 && threadIdx.x == 0) *err_flag = 1;
+        a = a < 0 ? 0 : K;
+    }
+    if (a == 0 && valid) {
+#pragma unroll
+        for (int j = 0; j < S::J; ++j)
+            *reinterpret_cast<float4 *>(state_out + row + j * 4 * S::LR + lr * 4) = s[j];
+    }
+
+    const float Ah = A[h], Dh = D[h];
+    for (int k = 0; k < K; ++k) {
+        const size_t tk = size_t(bi) * K + k;
+        const float d = dt[tk * H + h];
+        const float decay = expf(d * Ah);
+        const float xk = valid ? to_f32<IO>(x[(tk * H + h) * P + p]) : 0.f;
+        const float u = d * xk;
+        const IO *Bk = B + (tk * G + g) * N;
+        const IO *Ck = C + (tk * G + g) * N;
+        float part = 0.f;
+#pragma unroll
+        for (int j = 0; j < S::J; ++j) {
+            const int n = j * 4 * S::LR + lr * 4;
+            const float4 bb = load4<IO>(Bk + n);
+            const float4 cc = load4<IO>(Ck + n);
+            s[j].x = decay * s[j].x + u * bb.x;
+            s[j].y = decay * s[j].y + u * bb.y;
+            s[j].z = decay * s[j].z + u * bb.z;
+            s[j].w = decay * s[j].w + u * bb.w;
+            part += cc.x * s[j].x + cc.y * s[j].y + cc.z * s[j].z + cc.w * s[j].w;
+        }
+#pragma unroll
+        for (int off = 1; off < S::LR; off <<= 1) part += __shfl_xor(part, off, 64);
+        if (valid && lr == 0) y[(tk * H + h) * P + p] = from_f32<IO>(part + Dh * xk);
+        if (valid) {
+            if (states_all) {
+                float *dst = states_all + ((tk * H + h) * P + p) * N;
+#pragma unroll
+                for (int j = 0; j < S::J; ++j)
+                    *reinterpret_cast<float4 *>(dst + j * 4 * S::LR + lr * 4) = s[j];
+            }
+            if (k + 1 == a) {
+#pragma unroll
+                for (int j = 0; j < S::J; ++j)
+                    *reinterpret_cast<float4 *>(state_out + row + j * 4 * S::LR + lr * 4) = s[j];
+            }
+        }
+    }
+}
+
+template <typename IO, int N>
+static hipError_t launch_verify_n(const VerifyArgs &a, hipStream_t stream) {
+    using S = VerifyShape<N>;
+    dim3 grid((a.P + S::RB - 1) / S::RB, a.H, a.b);
+    hipLaunchKernelGGL((k_verify<IO, N>), grid, dim3(256), 0, stream, a.state_in,
+                       static_cast<const IO *>(a.x), a.dt, a.A, static_cast<const IO *>(a.B),
+                       static_cast<const IO *>(a.C), a.D, a.accept_len, static_cast<IO *>(a.y),
+                       a.state_out, a.states_all, a.err_flag, a.K, a.H, a.P, a.G);
+    return hipGetLastError();
+}
+
+template <typename IO>
+static hipError_t launch_verify_io(const VerifyArgs &a, hipStream_t stream) {
+    switch (a.N) {
+        case 16: return launch_verify_n<IO, 16>(a, stream);
+        case 32: return launch_verify_n<IO, 32>(a, stream);
+        case 64: return launch_verify_n<IO, 64>(a, stream);
+        case 128: return launch_verify_n<IO, 128>(a, stream);
+        case 256: return launch_verify_n<IO, 256>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+bool verify_supported_n(int N) {
+    return N == 16 || N == 32 || N == 64 || N == 128 || N == 256;
+}
+
+hipError_t launch_verify(const VerifyArgs &a, hipStream_t stream) {
+    if (a.bf16) return launch_verify_io<bf16_bits>(a, stream);
+    return launch_verify_io<float>(a, stream);
+}
+
+}  // namespace ssd

@@ -1,0 +1,163 @@
+"""The C-ABI library: loads, exports every declared symbol, and rejects bad
+arguments on the host before anything is enqueued (CPU only: no compute call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from selective_state_space_ssd_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd_mi355x.h")
+
+OK, NULL, DIM, GROUPS, UNSUP, ALIGN, WS, ALIAS, HIP = range(9)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.LIB_PATH):
+        from selective_state_space_ssd_amd import build
+        build.build()
+    return bd.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(bd.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert bd.ssd_version().startswith("ssd_mi355x")
+    for code in range(9):
+        assert bd.ssd_status_string(code).startswith(bd.STATUS_NAMES[code])
+
+
+def test_workspace_bytes(lib):
+    # fp32 chunk states + per-chunk decay + io-typed entering states (256-byte aligned)
+    b, L, H, P, N, G, Q = 4, 2048, 80, 64, 128, 1, 256
+    n = bd.ssd_chunk_scan_workspace_bytes(b, L, H, P, N, G, Q, bd.SSD_DTYPE_BF16)
+    units = b * H * (L // Q)
+    assert n >= units * P * N * (4 + 2) + units * 4
+    assert n < units * P * N * (4 + 2) + units * 4 + 3 * 256
+    assert bd.ssd_chunk_scan_workspace_bytes(0, L, H, P, N, G, Q, 1) == 0
+    assert bd.ssd_chunk_scan_workspace_bytes(b, 0, H, P, N, G, Q, 1) == 0
+    with pytest.raises(bd.SSDError):
+        bd.ssd_chunk_scan_workspace_bytes(b, L, 0, P, N, G, Q, 1)
+
+
+# Fake device addresses: never dereferenced, because every case below fails a
+# host-side check before any launch.
+BASE = 0x7F0000000000
+
+
+def addr(i, misalign=0):
+    return BASE + i * 0x100000000 + misalign
+
+
+def scan_call(lib, over=None, dims=None, io=1, ws_bytes=1 << 40):
+    ptrs = dict(x=addr(1), dt=addr(2), A=addr(3), B=addr(4), C=addr(5), D=addr(6),
+                init=None, y=addr(7), final=addr(8), ws=addr(9))
+    ptrs.update(over or {})
+    d = dict(b=1, L=256, H=4, P=16, N=16, G=1, Q=64)
+    d.update(dims or {})
+    return lib.ssd_chunk_scan_fwd(ptrs["x"], ptrs["dt"], ptrs["A"], ptrs["B"], ptrs["C"],
+                                  ptrs["D"], ptrs["init"], ptrs["y"], ptrs["final"], d["b"],
+                                  d["L"], d["H"], d["P"], d["N"], d["G"], d["Q"], io,
+                                  ptrs["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("name", ["x", "dt", "A", "B", "C", "D", "y"])
+def test_scan_null_required_pointer(lib, name):
+    assert scan_call(lib, {name: None}) == NULL
+
+
+@pytest.mark.parametrize("dims,code", [
+    (dict(b=-1), DIM), (dict(L=-5), DIM), (dict(H=0), DIM), (dict(P=0), DIM), (dict(N=0), DIM),
+    (dict(G=0), DIM), (dict(Q=0), DIM), (dict(G=3), GROUPS),
+    (dict(Q=32), UNSUP), (dict(Q=100), UNSUP), (dict(P=24), UNSUP), (dict(N=24), UNSUP),
+    (dict(N=512), UNSUP), (dict(P=128, N=256, Q=256), UNSUP),
+])
+def test_scan_bad_dims(lib, dims, code):
+    assert scan_call(lib, dims=dims) == code
+
+
+def test_scan_bad_dtype(lib):
+    assert scan_call(lib, io=7) == UNSUP
+
+
+@pytest.mark.parametrize("name,mis", [("x", 8), ("B", 2), ("C", 4), ("y", 8), ("final", 4),
+                                      ("init", 8), ("ws", 8), ("dt", 2), ("A", 1), ("D", 2)])
+def test_scan_misaligned(lib, name, mis):
+    idx = {"x": 1, "dt": 2, "A": 3, "B": 4, "C": 5, "D": 6, "y": 7, "final": 8, "ws": 9,
+           "init": 10}[name]
+    assert scan_call(lib, {name: addr(idx, mis)}) == ALIGN
+
+
+def test_scan_workspace_checks(lib):
+    need = bd.ssd_chunk_scan_workspace_bytes(1, 256, 4, 16, 16, 1, 64, 1)
+    assert scan_call(lib, ws_bytes=need - 1) == WS
+    assert scan_call(lib, {"ws": None}) == WS
+
+
+def test_scan_alias_checks(lib):
+    assert scan_call(lib, {"y": addr(1)}) == ALIAS                   # y == x
+    assert scan_call(lib, {"ws": addr(4)}) == ALIAS                  # workspace on B
+    assert scan_call(lib, {"final": addr(5)}) == ALIAS               # final_state on C
+    assert scan_call(lib, {"init": addr(10), "final": addr(10, 16)}) == ALIAS   # partial
+
+
+def test_scan_empty_problem_needs_no_pointers(lib):
+    # b == 0: nothing to do, returns OK without touching anything
+    assert scan_call(lib, {k: None for k in ("x", "dt", "A", "B", "C", "D", "y", "final",
+                                             "ws")}, dims=dict(b=0)) == OK
+
+
+def verify_call(lib, over=None, dims=None, io=1):
+    p = dict(state_in=addr(1), x=addr(2), dt=addr(3), A=addr(4), B=addr(5), C=addr(6),
+             D=addr(7), acc=addr(8), y=addr(9), state_out=addr(10), all=None, err=None)
+    p.update(over or {})
+    d = dict(b=2, K=4, H=4, P=16, N=32, G=2)
+    d.update(dims or {})
+    return lib.ssd_verify_step(p["state_in"], p["x"], p["dt"], p["A"], p["B"], p["C"], p["D"],
+                               p["acc"], p["y"], p["state_out"], p["all"], p["err"], d["b"],
+                               d["K"], d["H"], d["P"], d["N"], d["G"], io, None)
+
+
+@pytest.mark.parametrize("name", ["state_in", "x", "dt", "A", "B", "C", "D", "acc", "y",
+                                  "state_out"])
+def test_verify_null_required_pointer(lib, name):
+    assert verify_call(lib, {name: None}) == NULL
+
+
+@pytest.mark.parametrize("dims,code", [
+    (dict(b=-1), DIM), (dict(K=0), DIM), (dict(H=0), DIM), (dict(P=0), DIM), (dict(N=0), DIM),
+    (dict(G=0), DIM), (dict(G=3), GROUPS), (dict(K=17), UNSUP), (dict(N=48), UNSUP),
+    (dict(N=512), UNSUP),
+])
+def test_verify_bad_dims(lib, dims, code):
+    assert verify_call(lib, dims=dims) == code
+
+
+def test_verify_alignment_and_alias(lib):
+    assert verify_call(lib, {"state_in": addr(1, 4)}) == ALIGN
+    assert verify_call(lib, {"state_out": addr(10, 8)}) == ALIGN
+    assert verify_call(lib, {"all": addr(11, 4)}) == ALIGN
+    assert verify_call(lib, {"B": addr(5, 2)}) == ALIGN
+    assert verify_call(lib, {"state_out": addr(1, 16)}) == ALIAS     # partial overlap
+    assert verify_call(lib, {"all": addr(1)}) == ALIAS               # states_all on state_in
+    assert verify_call(lib, {"y": addr(2)}) == ALIAS                 # y on x
+    assert verify_call(lib, {"err": addr(8)}) == ALIAS               # flag on accept_len
+
+
+def test_verify_empty_batch_is_ok(lib):
+    assert verify_call(lib, {k: None for k in ("state_in", "x", "y", "state_out")},
+                       dims=dict(b=0)) == OK

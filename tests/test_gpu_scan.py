@@ -1,0 +1,111 @@
+"""GPU parity of ssd_chunk_scan_fwd against the fp64 oracle (MI355X only)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import TOL, run_scan, scan_errors, to_f64
+from selective_state_space_ssd_amd import binding as bd
+from selective_state_space_ssd_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(inp, units=None, tol=None):
+    y, fs = run_scan(inp)
+    ey, ef = scan_errors(inp, y, fs, units)
+    tol = tol or TOL[inp.io]
+    print(f"  y err {ey:.3e}  final_state err {ef:.3e}  (tol {tol})", flush=True)
+    assert np.isfinite(ey) and np.isfinite(ef)
+    assert ey <= tol and ef <= tol
+    return y, fs
+
+
+def test_tiny_fp32_workload_full_oracle():
+    _check(inputs.make_workload("tiny_fp32"))
+
+
+# Small cases the oracle finishes in seconds: several chunks and MFMA tiles, ragged
+# last chunks, nonzero initial states, every supported P, several N and Q, both dtypes.
+SMALL = [
+    # b,  L,  H,   P,   N, G,   Q,  io,   init
+    (2, 300, 4, 64, 128, 2, 256, "bf16", True),
+    (1, 200, 4, 16, 16, 1, 64, "bf16", False),
+    (2, 517, 2, 32, 64, 1, 128, "bf16", True),
+    (1, 384, 4, 64, 256, 4, 128, "bf16", True),
+    (1, 129, 2, 128, 32, 1, 64, "bf16", False),
+    (1, 150, 2, 32, 32, 2, 64, "f32", True),
+    (2, 333, 4, 64, 48, 2, 128, "f32", True),
+    (1, 64, 1, 16, 16, 1, 64, "f32", False),
+    (1, 1, 2, 16, 16, 1, 64, "bf16", True),          # one token
+    (1, 63, 2, 16, 16, 1, 64, "f32", True),          # shorter than one chunk
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "b{}L{}H{}P{}N{}G{}Q{}{}{}".format(
+    *c[:8], "init" if c[8] else ""))
+def test_small_cases_full_oracle(case):
+    b, L, H, P, N, G, Q, io, init = case
+    _check(inputs.make_scan_inputs(b, L, H, P, N, G, Q, io=io, init=init, seed=L + N + P))
+
+
+FULL = ["mamba2_2p7b_L2k", "mamba2_2p7b_L16k", "dstate_sweep_N16", "dstate_sweep_N64",
+        "dstate_sweep_N128", "dstate_sweep_N256"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workloads_sampled_heads(name):
+    inp = inputs.make_workload(name)
+    d = inp.dims
+    nu = d["b"] * d["H"]
+    units = sorted({0, nu // 2 + 1, nu - 1})
+    _check(inp, units=units)
+
+
+def test_run_to_run_bitwise_determinism():
+    inp = inputs.make_scan_inputs(2, 700, 8, 64, 128, 2, 256, io="bf16", init=True, seed=3)
+    y1, f1 = run_scan(inp)
+    y2, f2 = run_scan(inp)
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+def test_null_init_equals_zero_init():
+    inp = inputs.make_scan_inputs(1, 300, 4, 64, 64, 1, 128, io="bf16", init=False, seed=8)
+    y1, f1 = run_scan(inp)
+    inp.init_state = inputs.Tensor(np.zeros((1, 4, 64, 64), np.float32), "f32")
+    y2, f2 = run_scan(inp)
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+def test_split_sequence_state_handoff_on_gpu():
+    """Two calls chained through final_state match one call (context-parallel semantics)."""
+    inp = inputs.make_scan_inputs(1, 512, 4, 64, 128, 1, 256, io="bf16", init=True, seed=9)
+    y, fs = run_scan(inp)
+    dev = lambda a: bd.to_device(a)
+    x, dt, A, B, C, D = (dev(getattr(inp, n)) for n in ("x", "dt", "A", "B", "C", "D"))
+    init = dev(inp.init_state)
+    ya, fa = bd.chunk_scan_fwd(x[:, :256].contiguous(), dt[:, :256].contiguous(), A,
+                               B[:, :256].contiguous(), C[:, :256].contiguous(), D, 256, init)
+    yb, fb = bd.chunk_scan_fwd(x[:, 256:].contiguous(), dt[:, 256:].contiguous(), A,
+                               B[:, 256:].contiguous(), C[:, 256:].contiguous(), D, 256, fa)
+    torch.cuda.synchronize()
+    # the split lands on a chunk boundary, so the arithmetic is the same up to the
+    # rounding of the handed-over state
+    ycat = torch.cat([ya, yb], dim=1)
+    err = (to_f64(ycat) - to_f64(y))
+    assert np.max(np.abs(err)) <= 2e-2 * np.max(np.abs(to_f64(y)))
+    assert np.max(np.abs(to_f64(fb) - to_f64(fs))) <= 1e-3 * np.max(np.abs(to_f64(fs)))
+
+
+def test_empty_sequence_copies_initial_state():
+    init = torch.randn(2, 4, 16, 16, device="cuda")
+    x = torch.empty(2, 0, 4, 16, device="cuda", dtype=torch.bfloat16)
+    dt = torch.empty(2, 0, 4, device="cuda")
+    B = torch.empty(2, 0, 1, 16, device="cuda", dtype=torch.bfloat16)
+    A = torch.full((4,), -1.0, device="cuda")
+    D = torch.ones(4, device="cuda")
+    y, fs = bd.chunk_scan_fwd(x, dt, A, B, B, D, 64, init_state=init)
+    torch.cuda.synchronize()
+    assert torch.equal(fs, init)
+    y, fs = bd.chunk_scan_fwd(x, dt, A, B, B, D, 64, init_state=None)
+    torch.cuda.synchronize()
+    assert torch.equal(fs, torch.zeros_like(fs))

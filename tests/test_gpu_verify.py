@@ -1,0 +1,126 @@
+"""GPU parity of ssd_verify_step against the fp64 oracle (MI355X only)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import TOL, TOL_VERIFY_STATE, slice_err, to_f64
+from selective_state_space_ssd_amd import binding as bd
+from selective_state_space_ssd_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(v):
+    return dict(state=bd.to_device(v.state), x=bd.to_device(v.x), dt=bd.to_device(v.dt),
+                A=bd.to_device(v.A), B=bd.to_device(v.B), C=bd.to_device(v.C),
+                D=bd.to_device(v.D), acc=bd.to_device(v.accept_len))
+
+
+def _oracle(v, accept=None):
+    acc = v.accept_len if accept is None else accept
+    return oracle.verify_f64(v.state.f64(), v.x.f64(), v.dt.f64(), v.A.f64(), v.B.f64(),
+                             v.C.f64(), v.D.f64(), acc)
+
+
+def _run(v, with_all=True, in_place=False, err_flag=None):
+    t = _dev(v)
+    y = torch.empty_like(t["x"])
+    state_out = t["state"] if in_place else torch.empty_like(t["state"])
+    b, K, H, P = t["x"].shape
+    N = t["B"].shape[3]
+    states_all = (torch.empty((b, K, H, P, N), device="cuda", dtype=torch.float32)
+                  if with_all else None)
+    state_in = t["state"]
+    bd.ssd_verify_step(state_in, t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["acc"], y,
+                       state_out, states_all, err_flag)
+    torch.cuda.synchronize()
+    return y, state_out, states_all
+
+
+def _check(v, tol_y):
+    y, so, sa = _run(v)
+    yo, soo, sao = _oracle(v)
+    ey = slice_err(to_f64(y), yo, (1, 3))
+    es = slice_err(to_f64(so), soo, (2, 3))
+    ea = slice_err(to_f64(sa), sao, (3, 4))
+    print(f"  y {ey:.3e}  state_out {es:.3e}  states_all {ea:.3e}", flush=True)
+    assert ey <= tol_y and es <= TOL_VERIFY_STATE and ea <= TOL_VERIFY_STATE
+    # selection is exact: state_out is bit-identical to the stored state at a-1,
+    # or to state_in for a = 0
+    st_in = bd.to_device(v.state)
+    for bi, a in enumerate(v.accept_len):
+        if a == 0:
+            assert torch.equal(so[bi], st_in[bi])
+        else:
+            assert torch.equal(so[bi], sa[bi, a - 1])
+    return y, so, sa, soo, sao
+
+
+def test_verify_workload_full_size():
+    """b=32, K=4, H=32, P=128, N=128, G=8, bf16 I/O, fp32 state, random accept lengths."""
+    v = inputs.make_workload("verify_b32_K4")
+    y, so, sa, soo, sao = _check(v, TOL["bf16"])
+    # the tolerance separates neighbouring positions: the kept state is much closer
+    # to the oracle state at a than to the one at a-1 or a+1
+    sog = to_f64(so)
+    K = v.x.shape[1]
+    st0 = v.state.f64()
+    for bi, a in enumerate(v.accept_len):
+        seq = [st0[bi]] + [sao[bi, k] for k in range(K)]
+        d_here = np.max(np.abs(sog[bi] - seq[a]))
+        for nb in (a - 1, a + 1):
+            if 0 <= nb <= K:
+                gap = np.max(np.abs(seq[nb] - seq[a]))
+                assert d_here < 1e-3 * gap, (bi, a, nb)
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("N", [16, 32, 64, 256])
+def test_verify_small_shapes(io, N):
+    v = inputs.make_verify_inputs(b=5, K=6, H=4, P=20, N=N, G=2, io=io, seed=N)
+    v.accept_len = np.array([0, 1, 3, 5, 6], np.int32)
+    _check(v, TOL[io])
+
+
+@pytest.mark.parametrize("K", [1, 16])
+def test_verify_K_extremes(K):
+    v = inputs.make_verify_inputs(b=3, K=K, H=2, P=33, N=128, G=1, io="bf16", seed=K)
+    v.accept_len = np.array([0, K, K // 2], np.int32)
+    _check(v, TOL["bf16"])
+
+
+def test_verify_in_place_and_no_states_all():
+    v = inputs.make_verify_inputs(b=4, K=4, H=4, P=64, N=128, G=2, io="bf16", seed=77)
+    y, so, _ = _run(v, with_all=False, in_place=True)
+    yo, soo, _ = _oracle(v)
+    assert slice_err(to_f64(so), soo, (2, 3)) <= TOL_VERIFY_STATE
+    assert slice_err(to_f64(y), yo, (1, 3)) <= TOL["bf16"]
+
+
+def test_verify_out_of_range_accept_len_is_clamped_and_flagged():
+    v = inputs.make_verify_inputs(b=3, K=4, H=2, P=16, N=32, G=1, io="f32", seed=5)
+    v.accept_len = np.array([-2, 2, 9], np.int32)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y, so, sa = _run(v, err_flag=flag)
+    assert int(flag.item()) == 1
+    yo, soo, _ = _oracle(v, accept=np.array([0, 2, 4], np.int32))
+    assert slice_err(to_f64(so), soo, (2, 3)) <= TOL_VERIFY_STATE
+    flag.zero_()
+    v.accept_len = np.array([0, 2, 4], np.int32)
+    _run(v, err_flag=flag)
+    assert int(flag.item()) == 0
+
+
+def test_verify_matches_chunk_scan_over_K_tokens():
+    """The verify outputs equal the chunked scan of the same K tokens from the same
+    state (both against the oracle; here also GPU against GPU)."""
+    v = inputs.make_verify_inputs(b=2, K=4, H=4, P=64, N=64, G=2, io="bf16", seed=12)
+    v.accept_len = np.array([4, 4], np.int32)
+    y, so, _ = _run(v)
+    t = _dev(v)
+    ys, fs = bd.chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], 64,
+                               init_state=t["state"])
+    torch.cuda.synchronize()
+    assert slice_err(to_f64(ys), to_f64(y), (1, 3)) <= TOL["bf16"]
+    assert slice_err(to_f64(fs), to_f64(so), (2, 3)) <= TOL["bf16"]
