@@ -45,7 +45,10 @@ size_t ssd_chunk_scan_workspace_bytes(int b, int L, int H, int P, int N, int G, 
     if (b < 0 || L < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || Q <= 0) return size_t(-1);
     if (io != SSD_DTYPE_F32 && io != SSD_DTYPE_BF16) return size_t(-1);
     if (b == 0 || L == 0) return 0;
-    return ssd::plan_chunk_scan(b, L, H, P, N, G, Q, io == SSD_DTYPE_BF16).total;
+    const bool bf16 = io == SSD_DTYPE_BF16;
+    const ssd::FusedPlan fp = ssd::plan_fused(b, L, H, P, N, G, Q, bf16);
+    if (fp.supported) return fp.total;
+    return ssd::plan_chunk_scan(b, L, H, P, N, G, Q, bf16).total;
 }
 
 ssd_status_t ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, const void *B,
@@ -74,21 +77,23 @@ ssd_status_t ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, 
     if (!x || !dt || !A || !B || !C || !D || !y) return SSD_ERR_NULL_ARG;
 
     const bool bf16 = io == SSD_DTYPE_BF16;
+    const ssd::FusedPlan fplan = ssd::plan_fused(b, L, H, P, N, G, Q, bf16);
     const ssd::ChunkScanPlan plan = ssd::plan_chunk_scan(b, L, H, P, N, G, Q, bf16);
-    if (!plan.supported) return SSD_ERR_UNSUPPORTED;
+    if (!fplan.supported && !plan.supported) return SSD_ERR_UNSUPPORTED;
+    const size_t ws_need = fplan.supported ? fplan.total : plan.total;
 
     if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) ||
         !aligned(init_state, 16) || !aligned(final_state, 16) || !aligned(workspace, 16) ||
         !aligned(dt, 4) || !aligned(A, 4) || !aligned(D, 4))
         return SSD_ERR_ALIGN;
-    if (!workspace || workspace_bytes < plan.total) return SSD_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < ws_need) return SSD_ERR_WORKSPACE;
 
     const size_t esz = bf16 ? 2 : 4;
     const Range rx(x, size_t(b) * L * H * P * esz), ry(y, size_t(b) * L * H * P * esz);
     const Range rB(B, size_t(b) * L * G * N * esz), rC(C, size_t(b) * L * G * N * esz);
     const Range rdt(dt, size_t(b) * L * H * 4), rA(A, size_t(H) * 4), rD(D, size_t(H) * 4);
     const Range rinit(init_state, state_bytes), rfin(final_state, state_bytes);
-    const Range rws(workspace, plan.total);
+    const Range rws(workspace, ws_need);
     const Range inputs[] = {rx, rB, rC, rdt, rA, rD, rinit};
     for (const Range &in : inputs) {
         if (ry.overlaps(in) || rws.overlaps(in)) return SSD_ERR_ALIAS;
@@ -104,7 +109,9 @@ ssd_status_t ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, 
     a.b = b; a.L = L; a.H = H; a.P = P; a.N = N; a.G = G; a.Q = Q;
     a.bf16 = bf16;
     a.workspace = workspace;
-    if (ssd::launch_chunk_scan(a, plan, stream) != hipSuccess) return SSD_ERR_HIP;
+    const hipError_t e = fplan.supported ? ssd::launch_fused(a, fplan, stream)
+                                         : ssd::launch_chunk_scan(a, plan, stream);
+    if (e != hipSuccess) return SSD_ERR_HIP;
     return SSD_OK;
 }
 

@@ -1,0 +1,564 @@
+// ssd_chunk_fused.hip -- single-pass SSD chunked scan for gfx950 (bf16 I/O, P = 64).
+//
+// Same four steps as the chunked algorithm of the Mamba-2 article (msbhsh.com),
+// «SSD 算法：分块矩阵分解» / «SSD 算法：分块和形态传递», fused into one kernel so that
+// x is read once, y is written once and no per-chunk state makes a round trip
+// through HBM:
+//
+//   * one workgroup (8 waves, two per SIMD) per (batch, chunk, block of HB heads of
+//     one group);
+//   * C B^T of the chunk is computed once per workgroup and kept in registers as
+//     MFMA operands (it is shared by every head of the group);
+//   * decay factors only ever exponentiate non-positive numbers: tokens are
+//     grouped in 32-token blocks, each block's x is pre-scaled by the decay to the
+//     block end, and the chunk-level sums over blocks are taken in Horner form
+//     (accumulator *= decay across one block, then add the block's MFMA);
+//     the diagonal block uses the exact pairwise decay;
+//   * step 3 (state passing) is a chain between workgroups: the workgroup of
+//     chunk c waits until chunk c-1 of the same head has published its state,
+//     publishes H_c = exp(Acum_end) H_{c-1} + S_c, and only then needs H_{c-1} for
+//     its own outputs.  The hand-off uses device-coherent (agent-scope, relaxed)
+//     loads and stores for both the state and its ready flag, and the writer waits
+//     for its state stores to complete before it raises the flag; no cache-wide
+//     fence is needed.  Work items are taken from an atomic ticket in chunk-major
+//     order, so every item a workgroup waits for is held by a workgroup that is
+//     already running: the chain cannot deadlock whatever the dispatch order.  The
+//     wait is bounded; on time-out the state is poisoned with NaN and an error word
+//     in the workspace is set, so a failure is loud and never a hang.
+//
+// Step 1, 2 and 4 contractions use v_mfma_f32_16x16x32_bf16 with fp32 accumulation;
+// the in-chunk decay cumsum is a wavefront scan.
+#include "ssd_device.h"
+#include "ssd_kernels.h"
+#include "ssd_stage.h"
+
+namespace ssd {
+
+namespace {
+
+constexpr int kFT = 512;                    // threads per workgroup
+constexpr int kFW = kFT / 64;               // waves per workgroup
+constexpr uint32_t kSpinLimit = 1u << 20;   // about a second of polling before giving up
+
+template <int Q, int N>
+struct Fz {
+    static constexpr int P = 64;
+    static constexpr int PT = P / 16;              // 16-row channel tiles
+    static constexpr int NT = Q / 16;              // 16-token output tiles
+    static constexpr int NSB = Q / 32;             // 32-token blocks
+    static constexpr int TPW = (NT + kFW - 1) / kFW;   // output tiles per wave
+    static constexpr int NK = (N + 31) / 32;       // 32-wide k-steps over N
+    static constexpr int NPAD = NK * 32;
+    static constexpr int QS = Q + 8;               // LDS row stride, token-contiguous tiles
+    static constexpr int HS = NPAD + 8;            // LDS row stride of the state tile
+    static constexpr int NTN = N / 16;             // state column tiles
+    // state tiles of a wave: with >= 8 column tiles each wave owns whole columns,
+    // otherwise the waves of one column split its channel tiles
+    static constexpr int NTW = NTN >= kFW ? NTN / kFW : 1;
+    static constexpr int WPN = NTN >= kFW ? 1 : kFW / NTN;     // waves per column tile
+    static constexpr int PTW = NTN >= kFW ? PT : (PT >= WPN ? PT / WPN : 1);
+    static constexpr size_t kScalars = 3328;       // acum, dts, wtok [256 each], fac, misc
+    static constexpr size_t kLds =
+        kScalars + size_t(N) * QS * 2 + 2 * size_t(P) * QS * 2 + size_t(P) * HS * 2;
+    // B in natural layout is staged, before the head loop, over the x / state regions
+    static constexpr bool kBnatFits = size_t(Q) * HS <= 2 * size_t(P) * QS + size_t(P) * HS;
+    static_assert(Q % 64 == 0 && Q <= 256, "Q must be 64, 128 or 256");
+    static_assert(N % 16 == 0, "N must be a multiple of 16");
+};
+
+// t-tile handled by wave w in its m-th slot: a snake order so that the waves get
+// similar amounts of causal work.
+__device__ __forceinline__ int tile_of(int m, int w) {
+    return kFW * m + ((m & 1) ? kFW - 1 - w : w);
+}
+
+__device__ __forceinline__ uint4 ld_bf16x8_global(const bf16_bits *p, bool ok) {
+    return ok ? *reinterpret_cast<const uint4 *>(p) : make_uint4(0, 0, 0, 0);
+}
+
+// 2^x for x <= 0 with the hardware transcendental (results below the normal range
+// flush to zero, which is what a decay factor that small means anyway).
+__device__ __forceinline__ float exp2_dec(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Stage a [Q tokens][W channels] bf16 slice (token t at src + t * tok_stride) into
+// LDS transposed, dst[w * stride + t], in blocks of 8 tokens x 8 channels: eight
+// 16-byte row loads, a register transpose, eight 16-byte LDS stores.  Consecutive
+// lanes take consecutive token blocks, so the stores of a wave hit distinct banks.
+// With kScaled, row t is multiplied by wt[t] first (and rounded to bf16) and written
+// to dst_scaled as well as unscaled to dst (when dst is non-null).
+template <bool kScaled>
+__device__ __forceinline__ void stage_tok8(const bf16_bits *__restrict__ src, size_t tok_stride,
+                                           int W, int Q, int qlen, bf16_bits *dst,
+                                           bf16_bits *dst_scaled, int stride, const float *wt) {
+    const int TG = Q / 8, items = TG * (W / 8);
+    for (int it = threadIdx.x; it < items; it += kFT) {
+        const int t8 = 8 * (it % TG), w0 = 8 * (it / TG);
+        uint4 rows[8], cols[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            rows[i] = t8 + i < qlen
+                          ? *reinterpret_cast<const uint4 *>(src + size_t(t8 + i) * tok_stride + w0)
+                          : make_uint4(0, 0, 0, 0);
+        if (dst) {
+            transpose8x8_b16(rows, cols);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                *reinterpret_cast<uint4 *>(dst + (w0 + j) * stride + t8) = cols[j];
+        }
+        if constexpr (kScaled) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float f = wt[t8 + i];
+                uint4 &r = rows[i];
+                r = make_uint4(pack_bf16x2(bf16_lo(r.x) * f, bf16_hi(r.x) * f),
+                               pack_bf16x2(bf16_lo(r.y) * f, bf16_hi(r.y) * f),
+                               pack_bf16x2(bf16_lo(r.z) * f, bf16_hi(r.z) * f),
+                               pack_bf16x2(bf16_lo(r.w) * f, bf16_hi(r.w) * f));
+            }
+            transpose8x8_b16(rows, cols);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                *reinterpret_cast<uint4 *>(dst_scaled + (w0 + j) * stride + t8) = cols[j];
+        }
+    }
+}
+
+// Device-coherent accesses for the chunk-to-chunk state hand-off (another
+// workgroup, possibly on another XCD, reads what this one writes).
+__device__ __forceinline__ float ld_coherent(const float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's outstanding memory operations have completed.
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int Q, int N>
+__global__ __launch_bounds__(kFT, 1) void k_ssd_fused(
+    const bf16_bits *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
+    const bf16_bits *__restrict__ B, const bf16_bits *__restrict__ C,
+    const float *__restrict__ D, const float *__restrict__ init_state,
+    bf16_bits *__restrict__ y, float *__restrict__ final_state, float *hbuf, uint32_t *flags,
+    uint32_t *hdr, int L, int H, int G, int HB, int nchains, int nc) {
+    using F = Fz<Q, N>;
+    constexpr int P = F::P;
+    extern __shared__ __align__(16) unsigned char smem[];
+    float *acum = reinterpret_cast<float *>(smem);     // [256] log2-domain decay cumsum
+    float *dts = acum + 256;                            // [256] dt
+    float *wtok = dts + 256;                            // [256] weight of x_t in XwT
+    float *fac = wtok + 256;                            // [32]  decay across each block
+    int *misc = reinterpret_cast<int *>(fac + 32);      // [8]
+    float *scan_tmp = reinterpret_cast<float *>(misc + 8);   // [8]
+    bf16_bits *BT = reinterpret_cast<bf16_bits *>(smem + F::kScalars);   // [N][QS]
+    bf16_bits *XwT = BT + N * F::QS;                    // [P][QS] block-decayed dt x
+    bf16_bits *XT = XwT + P * F::QS;                    // [P][QS] x as given
+    bf16_bits *Hs = XT + P * F::QS;                     // [P][HS] entering state, bf16
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r16 = lane & 15, g4 = lane >> 4;
+
+    if (tid == 0) misc[0] = int(atomicAdd(&hdr[0], 1u));
+    __syncthreads();
+    const int item = misc[0];
+    const int c = item / nchains, chain = item % nchains;
+    const int hblocks = H / HB;
+    const int bi = chain / hblocks, h0 = (chain % hblocks) * HB;
+    const int g = h0 / (H / G);
+    const int t0 = c * Q, qlen = min(Q, L - t0);
+    const size_t tok0 = size_t(bi) * L + t0;
+    const bool last = (c == nc - 1);
+
+    // ---- B of the chunk, transposed, for the chunk-state contraction (step 2), and
+    // in natural layout (over the x / state regions, free until the head loop) for
+    // the score tiles
+    stage_tok8<false>(B + (tok0 * G + g) * N, size_t(G) * N, N, Q, qlen, BT, nullptr, F::QS,
+                      nullptr);
+    bf16_bits *Bnat = XwT;   // [Q][HS]
+    {
+        constexpr int VPR = F::NPAD / 8;
+        for (int it = tid; it < Q * VPR; it += kFT) {
+            const int r = it / VPR, w0 = (it % VPR) * 8;
+            *reinterpret_cast<uint4 *>(Bnat + r * F::HS + w0) =
+                ld_bf16x8_global(B + ((tok0 + r) * G + g) * N + w0, r < qlen && w0 < N);
+        }
+    }
+
+    // C rows of this wave's output tiles (B-operand layout: column t, k = n), kept for
+    // the whole workgroup
+    uint4 cf[F::TPW][F::NK];
+#pragma unroll
+    for (int m = 0; m < F::TPW; ++m) {
+        const int T = tile_of(m, w);
+        const int t = 16 * T + r16;
+#pragma unroll
+        for (int kk = 0; kk < F::NK; ++kk) {
+            const int n0 = kk * 32 + 8 * g4;
+            cf[m][kk] = ld_bf16x8_global(C + ((tok0 + t) * G + g) * N + n0,
+                                         T < F::NT && t < qlen && n0 < N);
+        }
+    }
+    __syncthreads();
+
+    // ---- G^T = B C^T tiles of this wave's output tiles, kept as MFMA B operands
+    // gfrag[m][S]: off-diagonal 32-token block S of tile slot m, bf16
+    // gdiag[m][.]: the diagonal block in fp32 (masked per head later)
+    constexpr int kSlots = (kFW / 2) * F::TPW;     // max off-diagonal blocks of a slot
+    uint4 gfrag[F::TPW][kSlots];
+    float gdiag[F::TPW][8];
+#pragma unroll
+    for (int m = 0; m < F::TPW; ++m) {
+        const int T = tile_of(m, w);
+        if (T >= F::NT) continue;
+        const int nsb = T / 2;   // off-diagonal blocks of this tile
+#pragma unroll
+        for (int S = 0; S <= (kFW / 2) * (m + 1) - 1; ++S) {
+            if (S > nsb) break;
+            f32x4 gt[2];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                gt[half] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const bf16_bits *brow = Bnat + (32 * S + 16 * half + r16) * F::HS + 8 * g4;
+#pragma unroll
+                for (int kk = 0; kk < F::NK; ++kk)
+                    gt[half] = mfma_bf16(as_bf16x8(*reinterpret_cast<const uint4 *>(brow + 32 * kk)),
+                                         as_bf16x8(cf[m][kk]), gt[half]);
+            }
+            if (S < nsb) {
+                gfrag[m][S] = make_uint4(pack_bf16x2(gt[0][0], gt[0][1]),
+                                         pack_bf16x2(gt[0][2], gt[0][3]),
+                                         pack_bf16x2(gt[1][0], gt[1][1]),
+                                         pack_bf16x2(gt[1][2], gt[1][3]));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    gdiag[m][i] = gt[0][i];
+                    gdiag[m][4 + i] = gt[1][i];
+                }
+            }
+        }
+    }
+    __syncthreads();   // Bnat is overwritten by the first head's x
+
+    // state tiles of this wave (step 2 accumulators and the hand-off)
+    const int nt_base = F::NTN >= kFW ? w : (w % F::NTN);
+    const int pt_base = F::NTN >= kFW ? 0 : (w / F::NTN);
+    constexpr int NT_STEP = kFW, PT_STEP = F::NTN >= kFW ? 1 : F::WPN;
+    const bool s_active = pt_base < F::PT;
+
+    for (int hh = 0; hh < HB; ++hh) {
+        const int h = h0 + hh;
+        const size_t bh = size_t(bi) * H + h;
+        // ---- discretisation and in-chunk decay scan
+        float d = 0.f;
+        if (tid < qlen) d = dt[(tok0 + tid) * H + h];
+        const float cs = block_inclusive_scan<4>(d * A[h] * kLog2e, scan_tmp);
+        if (tid < 256) {
+            acum[tid] = cs;   // constant past qlen (a = 0 there)
+            dts[tid] = d;
+        }
+        __syncthreads();
+        if (tid < F::NSB) fac[tid] = exp2_dec(acum[32 * tid + 31] - (tid > 0 ? acum[32 * tid - 1] : 0.f));
+        // weight of token t in the block-decayed copy of x: decay to its block end, dt
+        if (tid < 256) wtok[tid] = tid < Q ? exp2_dec(acum[tid | 31] - cs) * d : 0.f;
+        __syncthreads();
+        // ---- x of this head: block-decayed copy and plain copy, both transposed
+        stage_tok8<true>(x + (tok0 * H + h) * P, size_t(H) * P, P, Q, qlen, XT, XwT, F::QS, wtok);
+        __syncthreads();
+
+        // ---- step 2: S_c = sum over blocks (Horner) of XwT_S^T B_S
+        f32x4 accS[F::PTW][F::NTW];
+#pragma unroll
+        for (int k = 0; k < F::PTW; ++k)
+#pragma unroll
+            for (int j = 0; j < F::NTW; ++j) accS[k][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (s_active) {
+#pragma unroll
+            for (int S = 0; S < F::NSB; ++S) {
+                const float f = fac[S];
+                uint4 af[F::PTW], bfr[F::NTW];
+#pragma unroll
+                for (int k = 0; k < F::PTW; ++k)
+                    af[k] = *reinterpret_cast<const uint4 *>(
+                        XwT + ((pt_base + PT_STEP * k) * 16 + r16) * F::QS + 32 * S + 8 * g4);
+#pragma unroll
+                for (int j = 0; j < F::NTW; ++j)
+                    bfr[j] = *reinterpret_cast<const uint4 *>(
+                        BT + ((nt_base + NT_STEP * j) * 16 + r16) * F::QS + 32 * S + 8 * g4);
+#pragma unroll
+                for (int k = 0; k < F::PTW; ++k)
+#pragma unroll
+                    for (int j = 0; j < F::NTW; ++j)
+                        accS[k][j] =
+                            mfma_bf16(as_bf16x8(af[k]), as_bf16x8(bfr[j]), accS[k][j] * f);
+            }
+        }
+
+        // ---- step 3: chain with the previous chunk of this head
+        const float alpha = exp2_dec(acum[Q - 1]);
+        const float *hsrc = nullptr;   // state entering this chunk, fp32 [P][N]; null = zeros
+        bool coherent = false, poisoned = false;
+        if (c > 0) {
+            const uint32_t *flag = flags + bh * nc + (c - 1);
+            if (tid == 0) {
+                uint32_t it = 0;
+                int ok = 1;
+                while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+                    __builtin_amdgcn_s_sleep(2);
+                    if (++it > kSpinLimit) {
+                        ok = 0;
+                        __hip_atomic_store(&hdr[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                }
+                misc[1] = ok;
+            }
+            __syncthreads();
+            poisoned = misc[1] == 0;
+            coherent = true;
+            hsrc = hbuf + (bh * 2 + ((c - 1) & 1)) * size_t(P) * N;
+        } else if (init_state) {
+            hsrc = init_state + bh * size_t(P) * N;
+        }
+        const float nanv = __int_as_float(0x7fc00000);
+        if (s_active) {
+            // all loads first, then the update, then all stores
+            float hp[F::PTW][F::NTW][4];
+#pragma unroll
+            for (int k = 0; k < F::PTW; ++k)
+#pragma unroll
+                for (int j = 0; j < F::NTW; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int p = (pt_base + PT_STEP * k) * 16 + 4 * g4 + i;
+                        const int n = (nt_base + NT_STEP * j) * 16 + r16;
+                        hp[k][j][i] = !hsrc ? 0.f
+                                      : coherent ? ld_coherent(hsrc + p * N + n)
+                                                 : hsrc[p * N + n];
+                    }
+            float *hdst = last ? (final_state ? final_state + bh * size_t(P) * N : nullptr)
+                               : hbuf + (bh * 2 + (c & 1)) * size_t(P) * N;
+            if (hdst) {
+#pragma unroll
+                for (int k = 0; k < F::PTW; ++k)
+#pragma unroll
+                    for (int j = 0; j < F::NTW; ++j)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int p = (pt_base + PT_STEP * k) * 16 + 4 * g4 + i;
+                            const int n = (nt_base + NT_STEP * j) * 16 + r16;
+                            const float hn =
+                                alpha * (poisoned ? nanv : hp[k][j][i]) + accS[k][j][i];
+                            if (last) hdst[p * N + n] = hn;
+                            else st_coherent(hdst + p * N + n, hn);
+                        }
+            }
+        }
+        if (!last) wait_vm();   // this wave's state stores are complete and visible
+        // entering state as bf16 [p][n] in LDS (columns past N zero)
+        {
+            constexpr int V4 = F::NPAD / 4;
+            for (int it = tid; it < P * V4; it += kFT) {
+                const int p = it / V4, n0 = (it % V4) * 4;
+                float v[4] = {0.f, 0.f, 0.f, 0.f};
+                if (n0 < N && hsrc) {
+                    const float *q = hsrc + p * N + n0;
+                    if (coherent) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = ld_coherent(q + e);
+                    } else {
+                        const float4 t4 = *reinterpret_cast<const float4 *>(q);
+                        v[0] = t4.x; v[1] = t4.y; v[2] = t4.z; v[3] = t4.w;
+                    }
+                }
+                if (poisoned) v[0] = v[1] = v[2] = v[3] = nanv;
+                *reinterpret_cast<uint2 *>(Hs + p * F::HS + n0) =
+                    make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+            }
+        }
+        __syncthreads();
+        if (!last && tid == 0)
+            __hip_atomic_store(flags + bh * nc + c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+        // ---- steps 1 and 4 for this wave's output tiles
+        const float Dh = D[h];
+#pragma unroll
+        for (int m = 0; m < F::TPW; ++m) {
+            const int T = tile_of(m, w);
+            const int tl0 = 16 * T;
+            if (T >= F::NT || tl0 >= qlen) continue;
+            const int t = tl0 + r16;
+            const bool tv = t < qlen;
+            f32x4 acc[F::PT];
+#pragma unroll
+            for (int pt = 0; pt < F::PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // step 4 (entering state through C), referenced to the chunk start
+#pragma unroll
+            for (int kk = 0; kk < F::NK; ++kk)
+#pragma unroll
+                for (int pt = 0; pt < F::PT; ++pt)
+                    acc[pt] = mfma_bf16(
+                        as_bf16x8(*reinterpret_cast<const uint4 *>(
+                            Hs + (pt * 16 + r16) * F::HS + kk * 32 + 8 * g4)),
+                        as_bf16x8(cf[m][kk]), acc[pt]);
+            // step 1, off-diagonal blocks, Horner over block ends
+            const int nsb = T / 2;
+#pragma unroll
+            for (int S = 0; S < kSlots; ++S) {
+                if (S >= nsb) break;
+                const float f = fac[S];
+#pragma unroll
+                for (int pt = 0; pt < F::PT; ++pt) {
+                    const bf16_bits *xr = XwT + (pt * 16 + r16) * F::QS + 32 * S + 4 * g4;
+                    acc[pt] = mfma_bf16(as_bf16x8(*reinterpret_cast<const uint2 *>(xr),
+                                                  *reinterpret_cast<const uint2 *>(xr + 16)),
+                                        as_bf16x8(gfrag[m][S]), acc[pt] * f);
+                }
+            }
+            const float ref = nsb > 0 ? acum[32 * nsb - 1] : 0.f;
+            const float at = acum[t];
+            const float u = tv ? exp2_dec(at - ref) : 0.f;
+            // step 1, diagonal block with the pairwise decay
+            float mv[8];
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int s = 32 * nsb + 16 * half + 4 * g4 + i;
+                    const bool ok = tv && s <= t;
+                    mv[4 * half + i] =
+                        ok ? gdiag[m][4 * half + i] * exp2_dec(at - acum[s]) * dts[s] : 0.f;
+                }
+            const bf16x8 mop = as_bf16x8(make_uint4(pack_bf16x2(mv[0], mv[1]),
+                                                    pack_bf16x2(mv[2], mv[3]),
+                                                    pack_bf16x2(mv[4], mv[5]),
+                                                    pack_bf16x2(mv[6], mv[7])));
+#pragma unroll
+            for (int pt = 0; pt < F::PT; ++pt) {
+                const bf16_bits *xr = XT + (pt * 16 + r16) * F::QS + 32 * nsb + 4 * g4;
+                acc[pt] = mfma_bf16(as_bf16x8(*reinterpret_cast<const uint2 *>(xr),
+                                              *reinterpret_cast<const uint2 *>(xr + 16)),
+                                    mop, acc[pt] * u);
+            }
+            // epilogue: + D x, round to bf16, store y[t][p..p+3]
+            if (tv) {
+                bf16_bits *yrow = y + (tok0 + t) * size_t(H) * P + size_t(h) * P;
+#pragma unroll
+                for (int pt = 0; pt < F::PT; ++pt) {
+                    const int p0 = pt * 16 + 4 * g4;
+                    float o[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        o[i] = acc[pt][i] + Dh * bf16_to_f32(XT[(p0 + i) * F::QS + t]);
+                    *reinterpret_cast<uint2 *>(yrow + p0) =
+                        make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+__global__ void k_fused_reset(uint32_t *hdr, uint32_t *flags, size_t nflags) {
+    const size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < 64) hdr[i] = 0u;
+    if (i < nflags) flags[i] = 0u;
+}
+
+template <int Q, int N>
+hipError_t launch_fused_qn(const ChunkScanArgs &a, const FusedPlan &fp, hipStream_t stream) {
+    using F = Fz<Q, N>;
+    char *ws = static_cast<char *>(a.workspace);
+    uint32_t *hdr = reinterpret_cast<uint32_t *>(ws + fp.off_hdr);
+    uint32_t *flags = reinterpret_cast<uint32_t *>(ws + fp.off_flags);
+    float *hbuf = reinterpret_cast<float *>(ws + fp.off_hbuf);
+    const size_t nflags = size_t(a.b) * a.H * fp.nc;
+    hipLaunchKernelGGL(k_fused_reset, dim3(unsigned((nflags + 64 + 255) / 256)), dim3(256), 0,
+                       stream, hdr, flags, nflags);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_ssd_fused<Q, N>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(F::kLds));
+    if (e != hipSuccess) return e;
+    const int nchains = a.b * (a.H / fp.HB);
+    const unsigned items = unsigned(nchains) * unsigned(fp.nc);
+    hipLaunchKernelGGL((k_ssd_fused<Q, N>), dim3(items), dim3(kFT), F::kLds, stream,
+                       static_cast<const bf16_bits *>(a.x), a.dt, a.A,
+                       static_cast<const bf16_bits *>(a.B), static_cast<const bf16_bits *>(a.C),
+                       a.D, a.init_state, static_cast<bf16_bits *>(a.y), a.final_state, hbuf,
+                       flags, hdr, a.L, a.H, a.G, fp.HB, nchains, fp.nc);
+    return hipGetLastError();
+}
+
+template <int Q>
+hipError_t launch_fused_q(const ChunkScanArgs &a, const FusedPlan &fp, hipStream_t stream) {
+    switch (a.N) {
+        case 16: return launch_fused_qn<Q, 16>(a, fp, stream);
+        case 32: return launch_fused_qn<Q, 32>(a, fp, stream);
+        case 64: return launch_fused_qn<Q, 64>(a, fp, stream);
+        case 128: return launch_fused_qn<Q, 128>(a, fp, stream);
+        case 256:
+            if constexpr (Fz<Q, 256>::kLds <= kMaxLds && Fz<Q, 256>::kBnatFits)
+                return launch_fused_qn<Q, 256>(a, fp, stream);
+            return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int Q, int N>
+size_t fused_lds() { return Fz<Q, N>::kBnatFits ? Fz<Q, N>::kLds : size_t(-1); }
+
+size_t fused_lds_bytes(int Q, int N) {
+#define SSD_LDS_CASE(q)                                  \
+    if (Q == q) {                                        \
+        switch (N) {                                     \
+            case 16: return fused_lds<q, 16>();          \
+            case 32: return fused_lds<q, 32>();          \
+            case 64: return fused_lds<q, 64>();          \
+            case 128: return fused_lds<q, 128>();        \
+            case 256: return fused_lds<q, 256>();        \
+        }                                                \
+    }
+    SSD_LDS_CASE(64)
+    SSD_LDS_CASE(128)
+    SSD_LDS_CASE(256)
+#undef SSD_LDS_CASE
+    return size_t(-1);
+}
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+}  // namespace
+
+FusedPlan plan_fused(int b, int L, int H, int P, int N, int G, int Q, bool bf16) {
+    FusedPlan fp;
+    if (!bf16 || P != 64 || b <= 0 || L <= 0) return fp;
+    if (Q != 64 && Q != 128 && Q != 256) return fp;
+    if (N != 16 && N != 32 && N != 64 && N != 128 && N != 256) return fp;
+    if (G <= 0 || H % G != 0) return fp;
+    const size_t lds = fused_lds_bytes(Q, N);
+    if (lds > kMaxLds) return fp;
+    const int hpg = H / G;
+    fp.HB = hpg % 4 == 0 ? 4 : (hpg % 2 == 0 ? 2 : 1);
+    fp.nc = (L + Q - 1) / Q;
+    const size_t items = size_t(b) * (H / fp.HB) * fp.nc;
+    if (items > 0x7fffffffu) return fp;
+    fp.off_hdr = 0;
+    fp.off_flags = 256;
+    fp.off_hbuf = fp.off_flags + align256(size_t(b) * H * fp.nc * 4);
+    fp.total = fp.off_hbuf + align256(size_t(b) * H * 2 * size_t(P) * N * 4);
+    fp.lds = lds;
+    fp.supported = true;
+    return fp;
+}
+
+hipError_t launch_fused(const ChunkScanArgs &a, const FusedPlan &fp, hipStream_t stream) {
+    switch (a.Q) {
+        case 64: return launch_fused_q<64>(a, fp, stream);
+        case 128: return launch_fused_q<128>(a, fp, stream);
+        case 256: return launch_fused_q<256>(a, fp, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace ssd

@@ -18,6 +18,8 @@
 namespace ssd {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -28,12 +30,10 @@ __device__ __forceinline__ float bf16_to_f32(bf16_bits v) {
     return __uint_as_float(uint32_t(v) << 16);
 }
 
-// float -> bfloat16, round to nearest even; NaN stays NaN.
+// float -> bfloat16 with the hardware conversion (v_cvt_pk_bf16_f32: round to
+// nearest even in the default rounding mode; NaN stays NaN).
 __device__ __forceinline__ bf16_bits f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_bits((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return bf16_bits(u >> 16);
+    return __builtin_bit_cast(bf16_bits, static_cast<__bf16>(f));
 }
 
 template <typename IO>
@@ -64,9 +64,50 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint2 lo, uint2 hi) {
     return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
-// Pack two floats into a 32-bit pair of bf16 (first value in the low half).
+// Pack two floats into a 32-bit pair of bf16 (first value in the low half), one
+// v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// The low / high bf16 of a packed pair, widened exactly to float.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Transpose an 8 x 8 block of 16-bit values: in[r] holds row r (8 values, element j
+// in half (j & 1) of word j / 2); out[j] receives column j.  32 byte permutes.
+__device__ __forceinline__ void transpose8x8_b16(const uint4 (&in)[8], uint4 (&out)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t a = (&in[2 * k].x)[j >> 1], b = (&in[2 * k + 1].x)[j >> 1];
+            w[k] = __builtin_amdgcn_perm(b, a, sel);
+        }
+        out[j] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+// Inclusive prefix sum over the first 64 * kWaves threads of the block (the other
+// waves only take part in the barriers).  `tmp` is LDS scratch of at least kWaves
+// floats; the call contains two block barriers.
+template <int kWaves>
+__device__ __forceinline__ float block_inclusive_scan(float v, float *tmp) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        float o = __shfl_up(v, off, 64);
+        if (lane >= off) v += o;
+    }
+    if (lane == 63 && wave < kWaves) tmp[wave] = v;
+    __syncthreads();
+    float add = 0.f;
+    for (int w = 0; w < wave && w < kWaves; ++w) add += tmp[w];
+    __syncthreads();
+    return v + add;
 }
 
 // Inclusive prefix sum over a 256-thread block (4 waves).  `tmp` is LDS scratch

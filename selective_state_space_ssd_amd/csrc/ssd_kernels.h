@@ -58,6 +58,23 @@ struct ChunkScanPlan {
 };
 
 ChunkScanPlan plan_chunk_scan(int b, int L, int H, int P, int N, int G, int Q, bool bf16);
+
+// Single-pass kernel (bf16 I/O, P = 64, N in {16, 32, 64, 128, 256}): workspace holds
+// a ticket/error header, one ready flag per (batch, head, chunk) and a two-slot fp32
+// state ring per (batch, head) for the chunk-to-chunk hand-off.
+struct FusedPlan {
+    int nc = 0;
+    int HB = 1;                 // heads per workgroup (all of one group)
+    size_t off_hdr = 0;         // uint32 [64]: ticket, time-out error word
+    size_t off_flags = 0;       // uint32 [b, H, nc]
+    size_t off_hbuf = 0;        // fp32   [b, H, 2, P, N]
+    size_t total = 0;
+    size_t lds = 0;
+    bool supported = false;
+};
+
+FusedPlan plan_fused(int b, int L, int H, int P, int N, int G, int Q, bool bf16);
+hipError_t launch_fused(const ChunkScanArgs &a, const FusedPlan &plan, hipStream_t stream);
 hipError_t launch_chunk_scan(const ChunkScanArgs &a, const ChunkScanPlan &plan,
                              hipStream_t stream);
 // final_state = init_state (or zeros) for an empty sequence.

@@ -42,12 +42,17 @@ def test_version_and_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    # fp32 chunk states + per-chunk decay + io-typed entering states (256-byte aligned)
+    # bf16, P = 64: single-pass kernel, workspace = header + one flag per (b, h, chunk)
+    # + a two-slot fp32 state ring per (b, h)
     b, L, H, P, N, G, Q = 4, 2048, 80, 64, 128, 1, 256
     n = bd.ssd_chunk_scan_workspace_bytes(b, L, H, P, N, G, Q, bd.SSD_DTYPE_BF16)
+    ring = b * H * 2 * P * N * 4
+    flags = b * H * (L // Q) * 4
+    assert ring + flags + 256 <= n < ring + flags + 256 + 2 * 256
+    # fp32 I/O: three-kernel path, fp32 chunk states + per-chunk decay + entering states
+    n32 = bd.ssd_chunk_scan_workspace_bytes(b, L, H, P, N, G, Q, bd.SSD_DTYPE_F32)
     units = b * H * (L // Q)
-    assert n >= units * P * N * (4 + 2) + units * 4
-    assert n < units * P * N * (4 + 2) + units * 4 + 3 * 256
+    assert units * P * N * 8 + units * 4 <= n32 < units * P * N * 8 + units * 4 + 3 * 256
     assert bd.ssd_chunk_scan_workspace_bytes(0, L, H, P, N, G, Q, 1) == 0
     assert bd.ssd_chunk_scan_workspace_bytes(b, 0, H, P, N, G, Q, 1) == 0
     with pytest.raises(bd.SSDError):
