@@ -9,11 +9,15 @@
 //     one group);
 //   * C B^T of the chunk is computed once per workgroup and kept in registers as
 //     MFMA operands (it is shared by every head of the group);
-//   * decay factors only ever exponentiate non-positive numbers: tokens are
-//     grouped in 32-token blocks, each block's x is pre-scaled by the decay to the
-//     block end, and the chunk-level sums over blocks are taken in Horner form
-//     (accumulator *= decay across one block, then add the block's MFMA);
-//     the diagonal block uses the exact pairwise decay;
+//   * decay: every token of x is pre-scaled by dt times its decay to the chunk end
+//     (a factor <= 1), which makes step 2 a plain contraction.  When the total
+//     decay of a head over the chunk is moderate (-log2 decay <= kFastSpan, always
+//     true for step sizes and decay rates in the usual ranges) step 1 uses the same
+//     scaled x, causally masked, and rescales each output column once by the decay
+//     from its token to the chunk end (a factor >= 1, at most 2^kFastSpan).
+//     Otherwise the head takes an exact fallback for step 1 that only exponentiates
+//     non-positive numbers: each score is multiplied by its pairwise decay and dt
+//     and contracted with x as given;
 //   * step 3 (state passing) is a chain between workgroups: the workgroup of
 //     chunk c waits until chunk c-1 of the same head has published its state,
 //     publishes H_c = exp(Acum_end) H_{c-1} + S_c, and only then needs H_{c-1} for
@@ -39,6 +43,10 @@ namespace {
 constexpr int kFT = 512;                    // threads per workgroup
 constexpr int kFW = kFT / 64;               // waves per workgroup
 constexpr uint32_t kSpinLimit = 1u << 20;   // about a second of polling before giving up
+// Largest -log2(decay over one chunk) handled by the single-reference form: scaled
+// x stays >= 2^-100 * |dt x| (normal fp32 / bf16 range) and the output rescale stays
+// <= 2^100.
+constexpr float kFastSpan = 100.f;
 
 template <int Q, int N>
 struct Fz {
@@ -57,7 +65,7 @@ struct Fz {
     static constexpr int NTW = NTN >= kFW ? NTN / kFW : 1;
     static constexpr int WPN = NTN >= kFW ? 1 : kFW / NTN;     // waves per column tile
     static constexpr int PTW = NTN >= kFW ? PT : (PT >= WPN ? PT / WPN : 1);
-    static constexpr size_t kScalars = 3328;       // acum, dts, wtok [256 each], fac, misc
+    static constexpr size_t kScalars = 6208;       // acum, dts [256], dt of 4 heads [4][256], misc
     static constexpr size_t kLds =
         kScalars + size_t(N) * QS * 2 + 2 * size_t(P) * QS * 2 + size_t(P) * HS * 2;
     // B in natural layout is staged, before the head loop, over the x / state regions
@@ -76,9 +84,11 @@ __device__ __forceinline__ uint4 ld_bf16x8_global(const bf16_bits *p, bool ok) {
     return ok ? *reinterpret_cast<const uint4 *>(p) : make_uint4(0, 0, 0, 0);
 }
 
-// 2^x for x <= 0 with the hardware transcendental (results below the normal range
-// flush to zero, which is what a decay factor that small means anyway).
-__device__ __forceinline__ float exp2_dec(float x) { return __builtin_amdgcn_exp2f(x); }
+// A decay factor 2^x, x <= 0, with the hardware transcendental (results below the
+// normal range flush to zero, which is what a decay factor that small means).  The
+// argument is clamped at 0 so that a value computed for a masked-out (s > t) pair can
+// never be inf and turn a discarded 0 * inf into NaN.
+__device__ __forceinline__ float exp2_dec(float x) { return __builtin_amdgcn_exp2f(fminf(x, 0.f)); }
 
 // Stage a [Q tokens][W channels] bf16 slice (token t at src + t * tok_stride) into
 // LDS transposed, dst[w * stride + t], in blocks of 8 tokens x 8 channels: eight
@@ -145,11 +155,9 @@ __global__ __launch_bounds__(kFT, 1) void k_ssd_fused(
     constexpr int P = F::P;
     extern __shared__ __align__(16) unsigned char smem[];
     float *acum = reinterpret_cast<float *>(smem);     // [256] log2-domain decay cumsum
-    float *dts = acum + 256;                            // [256] dt
-    float *wtok = dts + 256;                            // [256] weight of x_t in XwT
-    float *fac = wtok + 256;                            // [32]  decay across each block
-    int *misc = reinterpret_cast<int *>(fac + 32);      // [8]
-    float *scan_tmp = reinterpret_cast<float *>(misc + 8);   // [8]
+    float *dts = acum + 256;                            // [256] dt of the current head
+    float *dtl = dts + 256;                             // [4][256] dt of the block's heads
+    int *misc = reinterpret_cast<int *>(dtl + 4 * 256); // [8]
     bf16_bits *BT = reinterpret_cast<bf16_bits *>(smem + F::kScalars);   // [N][QS]
     bf16_bits *XwT = BT + N * F::QS;                    // [P][QS] block-decayed dt x
     bf16_bits *XT = XwT + P * F::QS;                    // [P][QS] x as given
@@ -184,6 +192,11 @@ __global__ __launch_bounds__(kFT, 1) void k_ssd_fused(
         }
     }
 
+    // dt of the block's heads for the whole chunk, [head][token] (0 past the end)
+    for (int it = tid; it < 4 * 256; it += kFT) {
+        const int j = it >> 8, t = it & 255;
+        dtl[it] = (j < HB && t < qlen) ? dt[(tok0 + t) * H + h0 + j] : 0.f;
+    }
     // C rows of this wave's output tiles (B-operand layout: column t, k = n), kept for
     // the whole workgroup
     uint4 cf[F::TPW][F::NK];
@@ -240,33 +253,106 @@ __global__ __launch_bounds__(kFT, 1) void k_ssd_fused(
     }
     __syncthreads();   // Bnat is overwritten by the first head's x
 
+    // causally masked diagonal score tile (head independent), bf16 B operand
+    uint4 gdmask[F::TPW];
+#pragma unroll
+    for (int m = 0; m < F::TPW; ++m) {
+        const int T = tile_of(m, w);
+        const int t = 16 * T + r16, nsb = T / 2;
+        float mv[8];
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s = 32 * nsb + 16 * half + 4 * g4 + i;
+                mv[4 * half + i] = (T < F::NT && s <= t) ? gdiag[m][4 * half + i] : 0.f;
+            }
+        gdmask[m] = make_uint4(pack_bf16x2(mv[0], mv[1]), pack_bf16x2(mv[2], mv[3]),
+                               pack_bf16x2(mv[4], mv[5]), pack_bf16x2(mv[6], mv[7]));
+    }
+
     // state tiles of this wave (step 2 accumulators and the hand-off)
     const int nt_base = F::NTN >= kFW ? w : (w % F::NTN);
     const int pt_base = F::NTN >= kFW ? 0 : (w / F::NTN);
     constexpr int NT_STEP = kFW, PT_STEP = F::NTN >= kFW ? 1 : F::WPN;
     const bool s_active = pt_base < F::PT;
 
+    // ---- per-head inputs are loaded one head ahead.  Lane l of every wave owns the
+    // four tokens 4l .. 4l+3 (for the decay cumsum, which each wave computes for the
+    // whole chunk on its own, and for staging x); wave w stages channels 8w .. 8w+7.
+    const int tq0 = 4 * lane;
+    uint4 xq[4];       // x rows of the lane's 4 tokens, channels 8w .. 8w+7, next head
+    {
+        const bf16_bits *src = x + (tok0 * H + h0) * P + 8 * w;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            xq[k] = ld_bf16x8_global(src + size_t(tq0 + k) * H * P, tq0 + k < qlen);
+    }
+    // zero the padding columns of the entering-state tile once
+    for (int it = tid; it < P * (F::NPAD - N); it += kFT)
+        Hs[(it / (F::NPAD - N)) * F::HS + N + it % (F::NPAD - N)] = 0;
+
     for (int hh = 0; hh < HB; ++hh) {
         const int h = h0 + hh;
         const size_t bh = size_t(bi) * H + h;
-        // ---- discretisation and in-chunk decay scan
-        float d = 0.f;
-        if (tid < qlen) d = dt[(tok0 + tid) * H + h];
-        const float cs = block_inclusive_scan<4>(d * A[h] * kLog2e, scan_tmp);
-        if (tid < 256) {
-            acum[tid] = cs;   // constant past qlen (a = 0 there)
-            dts[tid] = d;
+        // ---- discretisation and in-chunk decay cumsum (inclusive, log2 domain),
+        // computed by every wave for all tokens: 4 tokens per lane + a wave scan
+        const float Al2 = A[h] * kLog2e;
+        float dq[4], aq[4];
+        {
+            const float4 d4 = *reinterpret_cast<const float4 *>(dtl + hh * 256 + tq0);
+            dq[0] = d4.x; dq[1] = d4.y; dq[2] = d4.z; dq[3] = d4.w;
+        }
+        aq[0] = dq[0] * Al2;
+        aq[1] = aq[0] + dq[1] * Al2;
+        aq[2] = aq[1] + dq[2] * Al2;
+        aq[3] = aq[2] + dq[3] * Al2;
+        float run = aq[3];
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float o = __shfl_up(run, off, 64);
+            if (lane >= off) run += o;
+        }
+        const float excl = run - aq[3];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) aq[k] += excl;   // constant past qlen (dt = 0 there)
+        const float aend = __shfl(aq[(Q - 1) & 3], (Q - 1) >> 2, 64);
+        const bool fast = -aend <= kFastSpan;   // uniform over the workgroup
+        if (w == 0) {
+            *reinterpret_cast<float4 *>(acum + tq0) = make_float4(aq[0], aq[1], aq[2], aq[3]);
+            *reinterpret_cast<float4 *>(dts + tq0) = make_float4(dq[0], dq[1], dq[2], dq[3]);
+        }
+        // ---- x of this head: x decayed to the chunk end (times dt), and x as given,
+        // both transposed to [channel][token]; 4 tokens x 8 channels per lane
+        if (tq0 < Q) {
+            uint2 cols[8];
+            transpose4x8_b16(xq, cols);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                *reinterpret_cast<uint2 *>(XT + (8 * w + j) * F::QS + tq0) = cols[j];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float f = exp2_dec(aend - aq[k]) * dq[k];
+                uint4 &r = xq[k];
+                r = make_uint4(pack_bf16x2(bf16_lo(r.x) * f, bf16_hi(r.x) * f),
+                               pack_bf16x2(bf16_lo(r.y) * f, bf16_hi(r.y) * f),
+                               pack_bf16x2(bf16_lo(r.z) * f, bf16_hi(r.z) * f),
+                               pack_bf16x2(bf16_lo(r.w) * f, bf16_hi(r.w) * f));
+            }
+            transpose4x8_b16(xq, cols);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                *reinterpret_cast<uint2 *>(XwT + (8 * w + j) * F::QS + tq0) = cols[j];
+        }
+        if (hh + 1 < HB) {   // next head's x, in flight during the rest of this head
+            const bf16_bits *src = x + (tok0 * H + h + 1) * P + 8 * w;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                xq[k] = ld_bf16x8_global(src + size_t(tq0 + k) * H * P, tq0 + k < qlen);
         }
         __syncthreads();
-        if (tid < F::NSB) fac[tid] = exp2_dec(acum[32 * tid + 31] - (tid > 0 ? acum[32 * tid - 1] : 0.f));
-        // weight of token t in the block-decayed copy of x: decay to its block end, dt
-        if (tid < 256) wtok[tid] = tid < Q ? exp2_dec(acum[tid | 31] - cs) * d : 0.f;
-        __syncthreads();
-        // ---- x of this head: block-decayed copy and plain copy, both transposed
-        stage_tok8<true>(x + (tok0 * H + h) * P, size_t(H) * P, P, Q, qlen, XT, XwT, F::QS, wtok);
-        __syncthreads();
 
-        // ---- step 2: S_c = sum over blocks (Horner) of XwT_S^T B_S
+        // ---- step 2: S_c = XwT^T B (x already carries dt and the decay to the chunk end)
         f32x4 accS[F::PTW][F::NTW];
 #pragma unroll
         for (int k = 0; k < F::PTW; ++k)
@@ -275,7 +361,6 @@ __global__ __launch_bounds__(kFT, 1) void k_ssd_fused(
         if (s_active) {
 #pragma unroll
             for (int S = 0; S < F::NSB; ++S) {
-                const float f = fac[S];
                 uint4 af[F::PTW], bfr[F::NTW];
 #pragma unroll
                 for (int k = 0; k < F::PTW; ++k)
@@ -289,13 +374,12 @@ __global__ __launch_bounds__(kFT, 1) void k_ssd_fused(
                 for (int k = 0; k < F::PTW; ++k)
 #pragma unroll
                     for (int j = 0; j < F::NTW; ++j)
-                        accS[k][j] =
-                            mfma_bf16(as_bf16x8(af[k]), as_bf16x8(bfr[j]), accS[k][j] * f);
+                        accS[k][j] = mfma_bf16(as_bf16x8(af[k]), as_bf16x8(bfr[j]), accS[k][j]);
             }
         }
 
         // ---- step 3: chain with the previous chunk of this head
-        const float alpha = exp2_dec(acum[Q - 1]);
+        const float alpha = exp2_dec(aend);
         const float *hsrc = nullptr;   // state entering this chunk, fp32 [P][N]; null = zeros
         bool coherent = false, poisoned = false;
         if (c > 0) {
@@ -322,8 +406,46 @@ __global__ __launch_bounds__(kFT, 1) void k_ssd_fused(
         }
         const float nanv = __int_as_float(0x7fc00000);
         if (s_active) {
-            // all loads first, then the update, then all stores
+            // one read of the entering state, in the accumulator layout: it feeds the
+            // update and the bf16 copy in LDS; then the update and all stores
             float hp[F::PTW][F::NTW][4];
+            int off[F::PTW][F::NTW][4];
+#pragma unroll
+            for (int k = 0; k < F::PTW; ++k)
+#pragma unroll
+                for (int j = 0; j < F::NTW; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        off[k][j][i] = ((pt_base + PT_STEP * k) * 16 + 4 * g4 + i) * N +
+                                       (nt_base + NT_STEP * j) * 16 + r16;
+                        hp[k][j][i] = 0.f;
+                    }
+            if (coherent) {
+#pragma unroll
+                for (int k = 0; k < F::PTW; ++k)
+#pragma unroll
+                    for (int j = 0; j < F::NTW; ++j)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) hp[k][j][i] = ld_coherent(hsrc + off[k][j][i]);
+            } else if (hsrc) {
+#pragma unroll
+                for (int k = 0; k < F::PTW; ++k)
+#pragma unroll
+                    for (int j = 0; j < F::NTW; ++j)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) hp[k][j][i] = hsrc[off[k][j][i]];
+            }
+            if (poisoned) {
+#pragma unroll
+                for (int k = 0; k < F::PTW; ++k)
+#pragma unroll
+                    for (int j = 0; j < F::NTW; ++j)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) hp[k][j][i] = nanv;
+            }
+            // fast form: the entering state reaches token t with decay
+            // 2^(acum_t - aend) * 2^aend; the second factor is folded into the copy
+            const float sc = fast ? alpha : 1.f;
 #pragma unroll
             for (int k = 0; k < F::PTW; ++k)
 #pragma unroll
@@ -332,50 +454,28 @@ __global__ __launch_bounds__(kFT, 1) void k_ssd_fused(
                     for (int i = 0; i < 4; ++i) {
                         const int p = (pt_base + PT_STEP * k) * 16 + 4 * g4 + i;
                         const int n = (nt_base + NT_STEP * j) * 16 + r16;
-                        hp[k][j][i] = !hsrc ? 0.f
-                                      : coherent ? ld_coherent(hsrc + p * N + n)
-                                                 : hsrc[p * N + n];
+                        Hs[p * F::HS + n] = f32_to_bf16(hp[k][j][i] * sc);
+                        hp[k][j][i] = alpha * hp[k][j][i] + accS[k][j][i];
                     }
-            float *hdst = last ? (final_state ? final_state + bh * size_t(P) * N : nullptr)
-                               : hbuf + (bh * 2 + (c & 1)) * size_t(P) * N;
-            if (hdst) {
+            if (!last) {
+                float *hdst = hbuf + (bh * 2 + (c & 1)) * size_t(P) * N;
 #pragma unroll
                 for (int k = 0; k < F::PTW; ++k)
 #pragma unroll
                     for (int j = 0; j < F::NTW; ++j)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int p = (pt_base + PT_STEP * k) * 16 + 4 * g4 + i;
-                            const int n = (nt_base + NT_STEP * j) * 16 + r16;
-                            const float hn =
-                                alpha * (poisoned ? nanv : hp[k][j][i]) + accS[k][j][i];
-                            if (last) hdst[p * N + n] = hn;
-                            else st_coherent(hdst + p * N + n, hn);
-                        }
+                        for (int i = 0; i < 4; ++i) st_coherent(hdst + off[k][j][i], hp[k][j][i]);
+            } else if (final_state) {
+                float *fdst = final_state + bh * size_t(P) * N;
+#pragma unroll
+                for (int k = 0; k < F::PTW; ++k)
+#pragma unroll
+                    for (int j = 0; j < F::NTW; ++j)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) fdst[off[k][j][i]] = hp[k][j][i];
             }
         }
         if (!last) wait_vm();   // this wave's state stores are complete and visible
-        // entering state as bf16 [p][n] in LDS (columns past N zero)
-        {
-            constexpr int V4 = F::NPAD / 4;
-            for (int it = tid; it < P * V4; it += kFT) {
-                const int p = it / V4, n0 = (it % V4) * 4;
-                float v[4] = {0.f, 0.f, 0.f, 0.f};
-                if (n0 < N && hsrc) {
-                    const float *q = hsrc + p * N + n0;
-                    if (coherent) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = ld_coherent(q + e);
-                    } else {
-                        const float4 t4 = *reinterpret_cast<const float4 *>(q);
-                        v[0] = t4.x; v[1] = t4.y; v[2] = t4.z; v[3] = t4.w;
-                    }
-                }
-                if (poisoned) v[0] = v[1] = v[2] = v[3] = nanv;
-                *reinterpret_cast<uint2 *>(Hs + p * F::HS + n0) =
-                    make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-            }
-        }
         __syncthreads();
         if (!last && tid == 0)
             __hip_atomic_store(flags + bh * nc + c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -401,44 +501,67 @@ __global__ __launch_bounds__(kFT, 1) void k_ssd_fused(
                         as_bf16x8(*reinterpret_cast<const uint4 *>(
                             Hs + (pt * 16 + r16) * F::HS + kk * 32 + 8 * g4)),
                         as_bf16x8(cf[m][kk]), acc[pt]);
-            // step 1, off-diagonal blocks, Horner over block ends
             const int nsb = T / 2;
+            const float at = acum[t];
+            if (fast) {
+                // step 1, all blocks up to and including the diagonal one, against x
+                // decayed to the chunk end; then rescale column t to its own token
 #pragma unroll
-            for (int S = 0; S < kSlots; ++S) {
-                if (S >= nsb) break;
-                const float f = fac[S];
+                for (int S = 0; S < kSlots; ++S) {
+                    if (S >= nsb) break;
+#pragma unroll
+                    for (int pt = 0; pt < F::PT; ++pt) {
+                        const bf16_bits *xr = XwT + (pt * 16 + r16) * F::QS + 32 * S + 4 * g4;
+                        acc[pt] = mfma_bf16(as_bf16x8(*reinterpret_cast<const uint2 *>(xr),
+                                                      *reinterpret_cast<const uint2 *>(xr + 16)),
+                                            as_bf16x8(gfrag[m][S]), acc[pt]);
+                    }
+                }
 #pragma unroll
                 for (int pt = 0; pt < F::PT; ++pt) {
-                    const bf16_bits *xr = XwT + (pt * 16 + r16) * F::QS + 32 * S + 4 * g4;
+                    const bf16_bits *xr = XwT + (pt * 16 + r16) * F::QS + 32 * nsb + 4 * g4;
                     acc[pt] = mfma_bf16(as_bf16x8(*reinterpret_cast<const uint2 *>(xr),
                                                   *reinterpret_cast<const uint2 *>(xr + 16)),
-                                        as_bf16x8(gfrag[m][S]), acc[pt] * f);
+                                        as_bf16x8(gdmask[m]), acc[pt]);
                 }
-            }
-            const float ref = nsb > 0 ? acum[32 * nsb - 1] : 0.f;
-            const float at = acum[t];
-            const float u = tv ? exp2_dec(at - ref) : 0.f;
-            // step 1, diagonal block with the pairwise decay
-            float mv[8];
+                const float u = tv ? __builtin_amdgcn_exp2f(at - aend) : 0.f;
 #pragma unroll
-            for (int half = 0; half < 2; ++half)
+                for (int pt = 0; pt < F::PT; ++pt) acc[pt] *= u;
+            } else {
+                // exact fallback: entering state decays by 2^acum_t; every score tile
+                // (off-diagonal and the masked diagonal one) is multiplied element by
+                // element by dt_s 2^(acum_t - acum_s) and contracted with x as given
+                const float e0 = tv ? exp2_dec(at) : 0.f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int s = 32 * nsb + 16 * half + 4 * g4 + i;
-                    const bool ok = tv && s <= t;
-                    mv[4 * half + i] =
-                        ok ? gdiag[m][4 * half + i] * exp2_dec(at - acum[s]) * dts[s] : 0.f;
+                for (int pt = 0; pt < F::PT; ++pt) acc[pt] *= e0;
+                // a rolled loop (rare path, kept small): the score fragment of block S
+                // is picked from the register array with a static select chain
+#pragma unroll 1
+                for (int S = 0; S <= nsb; ++S) {
+                    uint4 gsrc = gdmask[m];   // block nsb is the diagonal one
+#pragma unroll
+                    for (int k = 0; k < kSlots; ++k)
+                        if (k == S && S < nsb) gsrc = gfrag[m][k];
+                    float mv[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int s = 32 * S + (j < 4 ? 4 * g4 + j : 16 + 4 * g4 + j - 4);
+                        const uint32_t wd = (&gsrc.x)[j >> 1];
+                        const float gv = (j & 1) ? bf16_hi(wd) : bf16_lo(wd);
+                        mv[j] = (tv && s <= t) ? gv * exp2_dec(at - acum[s]) * dts[s] : 0.f;
+                    }
+                    const bf16x8 mop = as_bf16x8(make_uint4(pack_bf16x2(mv[0], mv[1]),
+                                                            pack_bf16x2(mv[2], mv[3]),
+                                                            pack_bf16x2(mv[4], mv[5]),
+                                                            pack_bf16x2(mv[6], mv[7])));
+#pragma unroll
+                    for (int pt = 0; pt < F::PT; ++pt) {
+                        const bf16_bits *xr = XT + (pt * 16 + r16) * F::QS + 32 * S + 4 * g4;
+                        acc[pt] = mfma_bf16(as_bf16x8(*reinterpret_cast<const uint2 *>(xr),
+                                                      *reinterpret_cast<const uint2 *>(xr + 16)),
+                                            mop, acc[pt]);
+                    }
                 }
-            const bf16x8 mop = as_bf16x8(make_uint4(pack_bf16x2(mv[0], mv[1]),
-                                                    pack_bf16x2(mv[2], mv[3]),
-                                                    pack_bf16x2(mv[4], mv[5]),
-                                                    pack_bf16x2(mv[6], mv[7])));
-#pragma unroll
-            for (int pt = 0; pt < F::PT; ++pt) {
-                const bf16_bits *xr = XT + (pt * 16 + r16) * F::QS + 32 * nsb + 4 * g4;
-                acc[pt] = mfma_bf16(as_bf16x8(*reinterpret_cast<const uint2 *>(xr),
-                                              *reinterpret_cast<const uint2 *>(xr + 16)),
-                                    mop, acc[pt] * u);
             }
             // epilogue: + D x, round to bf16, store y[t][p..p+3]
             if (tv) {

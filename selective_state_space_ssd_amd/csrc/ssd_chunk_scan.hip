@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_out(
                     for (int i = 0; i < 4; ++i) {
                         const int s = sb + 4 * g4 + i;
                         const bool ok = tv && s <= t && s < qlen;
-                        gv[half][i] = ok ? gt[i] * exp2f(acum_t - acum[s]) * dts[s] : 0.f;
+                        gv[half][i] = ok ? gt[i] * exp2f(fminf(acum_t - acum[s], 0.f)) * dts[s] : 0.f;
                     }
                 }
                 const bf16x8 bop = as_bf16x8(make_uint4(
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_out(
                 for (int i = 0; i < 4; ++i) {
                     const int s = sb + 4 * g4 + i;
                     const bool ok = tv && s <= t && s < qlen;
-                    const float gvi = ok ? gt[i] * exp2f(acum_t - acum[s]) * dts[s] : 0.f;
+                    const float gvi = ok ? gt[i] * exp2f(fminf(acum_t - acum[s], 0.f)) * dts[s] : 0.f;
 #pragma unroll
                     for (int pt = 0; pt < NPT; ++pt)
                         acc[pt] = mfma_f32(XT[(pt * 16 + r16) * QS + sb + 4 * g4 + i], gvi,

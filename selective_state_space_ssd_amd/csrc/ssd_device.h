@@ -91,6 +91,18 @@ __device__ __forceinline__ void transpose8x8_b16(const uint4 (&in)[8], uint4 (&o
     }
 }
 
+// Transpose a 4 x 8 block of 16-bit values: in[r] holds row r (8 values); out[j]
+// receives column j (4 values, row r in half (r & 1) of word r / 2).  16 permutes.
+__device__ __forceinline__ void transpose4x8_b16(const uint4 (&in)[4], uint2 (&out)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t a0 = (&in[0].x)[j >> 1], a1 = (&in[1].x)[j >> 1];
+        const uint32_t a2 = (&in[2].x)[j >> 1], a3 = (&in[3].x)[j >> 1];
+        out[j] = make_uint2(__builtin_amdgcn_perm(a1, a0, sel), __builtin_amdgcn_perm(a3, a2, sel));
+    }
+}
+
 // Inclusive prefix sum over the first 64 * kWaves threads of the block (the other
 // waves only take part in the barriers).  `tmp` is LDS scratch of at least kWaves
 // floats; the call contains two block barriers.

@@ -109,3 +109,24 @@ def test_empty_sequence_copies_initial_state():
     y, fs = bd.chunk_scan_fwd(x, dt, A, B, B, D, 64, init_state=None)
     torch.cuda.synchronize()
     assert torch.equal(fs, torch.zeros_like(fs))
+
+
+def _extreme_decay_inputs(seed, heads_slow):
+    """Heads in `heads_slow` get dt ~ U(0.5, 1) and A = -16 (a decay far beyond the
+    single-reference range over one chunk); the others keep the usual recipe."""
+    inp = inputs.make_scan_inputs(2, 600, 8, 64, 128, 2, 256, io="bf16", init=True, seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    dt = inp.dt.data.copy()
+    A = inp.A.data.copy()
+    for h in heads_slow:
+        dt[:, :, h] = rng.uniform(0.5, 1.0, dt[:, :, h].shape).astype(np.float32)
+        A[h] = -16.0
+    inp.dt = inputs.Tensor(dt, "f32")
+    inp.A = inputs.Tensor(A, "f32")
+    return inp
+
+
+@pytest.mark.parametrize("heads_slow", [(1, 2, 5, 6), tuple(range(8))],
+                         ids=["mixed", "all_extreme"])
+def test_extreme_decay_takes_exact_path(heads_slow):
+    _check(_extreme_decay_inputs(17, heads_slow))
