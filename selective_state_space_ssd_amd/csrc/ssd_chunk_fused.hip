@@ -59,6 +59,7 @@ struct Fz {
     static constexpr int NPAD = NK * 32;
     static constexpr int QS = Q + 8;               // LDS row stride, token-contiguous tiles
     static constexpr int HS = NPAD + 8;            // LDS row stride of the state tile
+    static constexpr int XS = P + 8;               // LDS row stride of x in token-major order
     static constexpr int NTN = N / 16;             // state column tiles
     // state tiles of a wave: with >= 8 column tiles each wave owns whole columns,
     // otherwise the waves of one column split its channel tiles
@@ -66,12 +67,19 @@ struct Fz {
     static constexpr int WPN = NTN >= kFW ? 1 : kFW / NTN;     // waves per column tile
     static constexpr int PTW = NTN >= kFW ? PT : (PT >= WPN ? PT / WPN : 1);
     static constexpr size_t kScalars = 6208;       // acum, dts [256], dt of 4 heads [4][256], misc
-    static constexpr size_t kLds =
-        kScalars + size_t(N) * QS * 2 + 2 * size_t(P) * QS * 2 + size_t(P) * HS * 2;
+    static constexpr size_t kLds = kScalars + size_t(N) * QS * 2 + size_t(P) * QS * 2 +
+                                   size_t(Q) * XS * 2 + size_t(P) * HS * 2;
     // B in natural layout is staged, before the head loop, over the x / state regions
-    static constexpr bool kBnatFits = size_t(Q) * HS <= 2 * size_t(P) * QS + size_t(P) * HS;
+    static constexpr bool kBnatFits =
+        size_t(Q) * HS <= size_t(P) * QS + size_t(Q) * XS + size_t(P) * HS;
     static_assert(Q % 64 == 0 && Q <= 256, "Q must be 64, 128 or 256");
     static_assert(N % 16 == 0, "N must be a multiple of 16");
+    // workgroups per CU the LDS allows (at most two); with two, every wave must fit
+    // in a quarter of the register file
+    static constexpr int kWgPerCu = kLds <= 80 * 1024 ? 2 : 1;
+    // LDS operand reads run this many k-steps ahead of the matrix products (deeper
+    // pipelining needs registers that two workgroups per CU do not have)
+    static constexpr int kDepth = kWgPerCu == 1 ? 2 : 1;
 };
 
 // t-tile handled by wave w in its m-th slot: a snake order so that the waves get
@@ -82,6 +90,13 @@ __device__ __forceinline__ int tile_of(int m, int w) {
 
 __device__ __forceinline__ uint4 ld_bf16x8_global(const bf16_bits *p, bool ok) {
     return ok ? *reinterpret_cast<const uint4 *>(p) : make_uint4(0, 0, 0, 0);
+}
+
+// 16 bytes at a 32-bit byte offset from a workgroup-uniform base (scalar base
+// register + one offset register per lane)
+__device__ __forceinline__ uint4 ld_b128_off(const void *base, uint32_t byte_off, bool ok) {
+    return ok ? *reinterpret_cast<const uint4 *>(static_cast<const char *>(base) + byte_off)
+              : make_uint4(0, 0, 0, 0);
 }
 
 // A decay factor 2^x, x <= 0, with the hardware transcendental (results below the
@@ -145,7 +160,8 @@ __device__ __forceinline__ void st_coherent(float *p, float v) {
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <int Q, int N>
-__global__ __launch_bounds__(kFT, 1) void k_ssd_fused(
+__global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(2 * Fz<Q, N>::kWgPerCu)))
+void k_ssd_fused(
     const bf16_bits *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
     const bf16_bits *__restrict__ B, const bf16_bits *__restrict__ C,
     const float *__restrict__ D, const float *__restrict__ init_state,
@@ -160,15 +176,18 @@ __global__ __launch_bounds__(kFT, 1) void k_ssd_fused(
     int *misc = reinterpret_cast<int *>(dtl + 4 * 256); // [8]
     bf16_bits *BT = reinterpret_cast<bf16_bits *>(smem + F::kScalars);   // [N][QS]
     bf16_bits *XwT = BT + N * F::QS;                    // [P][QS] block-decayed dt x
-    bf16_bits *XT = XwT + P * F::QS;                    // [P][QS] x as given
-    bf16_bits *Hs = XT + P * F::QS;                     // [P][HS] entering state, bf16
+    bf16_bits *XN = XwT + P * F::QS;                    // [Q][XS] x as given, token-major
+    bf16_bits *Hs = XN + Q * F::XS;                     // [P][HS] entering state, bf16
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave index; held in a scalar register except in the Q = 256 kernels, whose
+    // register assignment only stays spill-free with it in a vector register
+    const int w = Q == 256 ? tid >> 6 : __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, g4 = lane >> 4;
 
     if (tid == 0) misc[0] = int(atomicAdd(&hdr[0], 1u));
     __syncthreads();
-    const int item = misc[0];
+    const int item = __builtin_amdgcn_readfirstlane(misc[0]);   // uniform: keep it scalar
     const int c = item / nchains, chain = item % nchains;
     const int hblocks = H / HB;
     const int bi = chain / hblocks, h0 = (chain % hblocks) * HB;
@@ -277,26 +296,39 @@ __global__ __launch_bounds__(kFT, 1) void k_ssd_fused(
     constexpr int NT_STEP = kFW, PT_STEP = F::NTN >= kFW ? 1 : F::WPN;
     const bool s_active = pt_base < F::PT;
 
-    // ---- per-head inputs are loaded one head ahead.  Lane l of every wave owns the
-    // four tokens 4l .. 4l+3 (for the decay cumsum, which each wave computes for the
-    // whole chunk on its own, and for staging x); wave w stages channels 8w .. 8w+7.
+    // ---- per-head x.  Lane l of every wave owns the four tokens 4l .. 4l+3 (for the
+    // decay cumsum, which each wave computes for the whole chunk on its own, and for
+    // staging x); wave w stages channels 8w .. 8w+7.  x is loaded one head ahead,
+    // except where two workgroups share a CU and the registers are too few for it
+    // (N > 32): there the other workgroup covers the load latency and x is loaded at
+    // the start of its head.
+    constexpr bool kPrefetchX = F::kWgPerCu == 1 || N <= 32;
     const int tq0 = 4 * lane;
-    uint4 xq[4];       // x rows of the lane's 4 tokens, channels 8w .. 8w+7, next head
-    {
-        const bf16_bits *src = x + (tok0 * H + h0) * P + 8 * w;
+    uint4 xq[4];       // x rows of the lane's 4 tokens, channels 8w .. 8w+7
+    if constexpr (kPrefetchX) {
+        const bf16_bits *src = x + (tok0 * H + h0) * P;   // uniform base
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            xq[k] = ld_bf16x8_global(src + size_t(tq0 + k) * H * P, tq0 + k < qlen);
+            xq[k] = ld_b128_off(src, uint32_t(((tq0 + k) * H * P + 8 * w) * 2), tq0 + k < qlen);
     }
     // zero the padding columns of the entering-state tile once
-    for (int it = tid; it < P * (F::NPAD - N); it += kFT)
-        Hs[(it / (F::NPAD - N)) * F::HS + N + it % (F::NPAD - N)] = 0;
+    if constexpr (F::NPAD > N) {
+        for (int it = tid; it < P * (F::NPAD - N); it += kFT)
+            Hs[(it / (F::NPAD - N)) * F::HS + N + it % (F::NPAD - N)] = 0;
+    }
 
     for (int hh = 0; hh < HB; ++hh) {
         const int h = h0 + hh;
         const size_t bh = size_t(bi) * H + h;
         // ---- discretisation and in-chunk decay cumsum (inclusive, log2 domain),
         // computed by every wave for all tokens: 4 tokens per lane + a wave scan
+        if constexpr (!kPrefetchX) {
+            const bf16_bits *src = x + (tok0 * H + h) * P;   // uniform base
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                xq[k] = ld_b128_off(src, uint32_t(((tq0 + k) * H * P + 8 * w) * 2),
+                                    tq0 + k < qlen);
+        }
         const float Al2 = A[h] * kLog2e;
         float dq[4], aq[4];
         {
@@ -322,14 +354,13 @@ __global__ __launch_bounds__(kFT, 1) void k_ssd_fused(
             *reinterpret_cast<float4 *>(acum + tq0) = make_float4(aq[0], aq[1], aq[2], aq[3]);
             *reinterpret_cast<float4 *>(dts + tq0) = make_float4(dq[0], dq[1], dq[2], dq[3]);
         }
-        // ---- x of this head: x decayed to the chunk end (times dt), and x as given,
-        // both transposed to [channel][token]; 4 tokens x 8 channels per lane
+        // ---- x of this head: x as given, token-major (for the D x term), and x
+        // decayed to the chunk end (times dt), transposed to [channel][token]; 4 tokens
+        // x 8 channels per lane
         if (tq0 < Q) {
-            uint2 cols[8];
-            transpose4x8_b16(xq, cols);
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                *reinterpret_cast<uint2 *>(XT + (8 * w + j) * F::QS + tq0) = cols[j];
+            for (int k = 0; k < 4; ++k)
+                *reinterpret_cast<uint4 *>(XN + (tq0 + k) * F::XS + 8 * w) = xq[k];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const float f = exp2_dec(aend - aq[k]) * dq[k];
@@ -339,16 +370,18 @@ __global__ __launch_bounds__(kFT, 1) void k_ssd_fused(
                                pack_bf16x2(bf16_lo(r.z) * f, bf16_hi(r.z) * f),
                                pack_bf16x2(bf16_lo(r.w) * f, bf16_hi(r.w) * f));
             }
+            uint2 cols[8];
             transpose4x8_b16(xq, cols);
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 *reinterpret_cast<uint2 *>(XwT + (8 * w + j) * F::QS + tq0) = cols[j];
         }
-        if (hh + 1 < HB) {   // next head's x, in flight during the rest of this head
-            const bf16_bits *src = x + (tok0 * H + h + 1) * P + 8 * w;
+        if (kPrefetchX && hh + 1 < HB) {   // next head's x, in flight during this head
+            const bf16_bits *src = x + (tok0 * H + h + 1) * P;   // uniform base
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                xq[k] = ld_bf16x8_global(src + size_t(tq0 + k) * H * P, tq0 + k < qlen);
+                xq[k] = ld_b128_off(src, uint32_t(((tq0 + k) * H * P + 8 * w) * 2),
+                                    tq0 + k < qlen);
         }
         __syncthreads();
 
@@ -359,22 +392,41 @@ __global__ __launch_bounds__(kFT, 1) void k_ssd_fused(
 #pragma unroll
             for (int j = 0; j < F::NTW; ++j) accS[k][j] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (s_active) {
+            // software pipelined: the LDS operands of block S + kDepth - 1 are read
+            // while block S is multiplied
+            constexpr int DP = F::kDepth;
+            uint4 af[DP][F::PTW], bfr[DP][F::NTW];
 #pragma unroll
-            for (int S = 0; S < F::NSB; ++S) {
-                uint4 af[F::PTW], bfr[F::NTW];
+            for (int L = 0; L < DP - 1; ++L) {
 #pragma unroll
                 for (int k = 0; k < F::PTW; ++k)
-                    af[k] = *reinterpret_cast<const uint4 *>(
-                        XwT + ((pt_base + PT_STEP * k) * 16 + r16) * F::QS + 32 * S + 8 * g4);
+                    af[L][k] = *reinterpret_cast<const uint4 *>(
+                        XwT + ((pt_base + PT_STEP * k) * 16 + r16) * F::QS + 32 * L + 8 * g4);
 #pragma unroll
                 for (int j = 0; j < F::NTW; ++j)
-                    bfr[j] = *reinterpret_cast<const uint4 *>(
-                        BT + ((nt_base + NT_STEP * j) * 16 + r16) * F::QS + 32 * S + 8 * g4);
+                    bfr[L][j] = *reinterpret_cast<const uint4 *>(
+                        BT + ((nt_base + NT_STEP * j) * 16 + r16) * F::QS + 32 * L + 8 * g4);
+            }
+#pragma unroll
+            for (int S = 0; S < F::NSB; ++S) {
+                const int L = S + DP - 1;   // block whose operands are read now
+                if (L < F::NSB) {
+#pragma unroll
+                    for (int k = 0; k < F::PTW; ++k)
+                        af[L % DP][k] = *reinterpret_cast<const uint4 *>(
+                            XwT + ((pt_base + PT_STEP * k) * 16 + r16) * F::QS + 32 * L + 8 * g4);
+#pragma unroll
+                    for (int j = 0; j < F::NTW; ++j)
+                        bfr[L % DP][j] = *reinterpret_cast<const uint4 *>(
+                            BT + ((nt_base + NT_STEP * j) * 16 + r16) * F::QS + 32 * L + 8 * g4);
+                }
+                if (DP > 1) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int k = 0; k < F::PTW; ++k)
 #pragma unroll
                     for (int j = 0; j < F::NTW; ++j)
-                        accS[k][j] = mfma_bf16(as_bf16x8(af[k]), as_bf16x8(bfr[j]), accS[k][j]);
+                        accS[k][j] = mfma_bf16(as_bf16x8(af[S % DP][k]),
+                                               as_bf16x8(bfr[S % DP][j]), accS[k][j]);
             }
         }
 
@@ -398,7 +450,7 @@ __global__ __launch_bounds__(kFT, 1) void k_ssd_fused(
                 misc[1] = ok;
             }
             __syncthreads();
-            poisoned = misc[1] == 0;
+            poisoned = __builtin_amdgcn_readfirstlane(misc[1]) == 0;
             coherent = true;
             hsrc = hbuf + (bh * 2 + ((c - 1) & 1)) * size_t(P) * N;
         } else if (init_state) {
@@ -482,58 +534,101 @@ __global__ __launch_bounds__(kFT, 1) void k_ssd_fused(
 
         // ---- steps 1 and 4 for this wave's output tiles
         const float Dh = D[h];
+        // step 4 (entering state through C, referenced to the chunk start) for all
+        // of the wave's tile slots at once: each state fragment read from LDS feeds
+        // every slot; the reads of k-step kk are in flight during the products of
+        // k-step kk - 1
+        f32x4 acc[F::TPW][F::PT];
+        bool slot_ok[F::TPW];
 #pragma unroll
         for (int m = 0; m < F::TPW; ++m) {
             const int T = tile_of(m, w);
-            const int tl0 = 16 * T;
-            if (T >= F::NT || tl0 >= qlen) continue;
-            const int t = tl0 + r16;
-            const bool tv = t < qlen;
-            f32x4 acc[F::PT];
+            slot_ok[m] = T < F::NT && 16 * T < qlen;   // uniform over the wave
 #pragma unroll
-            for (int pt = 0; pt < F::PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            // step 4 (entering state through C), referenced to the chunk start
+            for (int pt = 0; pt < F::PT; ++pt) acc[m][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        {
+            constexpr int DP = F::kDepth;
+            uint4 hf[DP][F::PT];
 #pragma unroll
-            for (int kk = 0; kk < F::NK; ++kk)
+            for (int L = 0; L < DP - 1; ++L)
 #pragma unroll
                 for (int pt = 0; pt < F::PT; ++pt)
-                    acc[pt] = mfma_bf16(
-                        as_bf16x8(*reinterpret_cast<const uint4 *>(
-                            Hs + (pt * 16 + r16) * F::HS + kk * 32 + 8 * g4)),
-                        as_bf16x8(cf[m][kk]), acc[pt]);
+                    hf[L][pt] = *reinterpret_cast<const uint4 *>(
+                        Hs + (pt * 16 + r16) * F::HS + L * 32 + 8 * g4);
+#pragma unroll
+            for (int kk = 0; kk < F::NK; ++kk) {
+                const int L = kk + DP - 1;
+                if (L < F::NK) {
+#pragma unroll
+                    for (int pt = 0; pt < F::PT; ++pt)
+                        hf[L % DP][pt] = *reinterpret_cast<const uint4 *>(
+                            Hs + (pt * 16 + r16) * F::HS + L * 32 + 8 * g4);
+                }
+                if (DP > 1) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int m = 0; m < F::TPW; ++m)
+                    if (slot_ok[m]) {
+#pragma unroll
+                        for (int pt = 0; pt < F::PT; ++pt)
+                            acc[m][pt] = mfma_bf16(as_bf16x8(hf[kk % DP][pt]),
+                                                   as_bf16x8(cf[m][kk]), acc[m][pt]);
+                    }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < F::TPW; ++m) {
+            if (!slot_ok[m]) continue;
+            const int T = tile_of(m, w);
+            const int tl0 = 16 * T;
+            const int t = tl0 + r16;
+            const bool tv = t < qlen;
             const int nsb = T / 2;
             const float at = acum[t];
             if (fast) {
                 // step 1, all blocks up to and including the diagonal one, against x
-                // decayed to the chunk end; then rescale column t to its own token
+                // decayed to the chunk end; then rescale column t to its own token.
+                // The x fragments of block S + kDepth - 1 are read while block S is
+                // multiplied.
+                constexpr int DP = F::kDepth;
+                uint2 xlo[DP][F::PT], xhi[DP][F::PT];
 #pragma unroll
-                for (int S = 0; S < kSlots; ++S) {
-                    if (S >= nsb) break;
+                for (int L = 0; L < DP - 1; ++L)
 #pragma unroll
                     for (int pt = 0; pt < F::PT; ++pt) {
-                        const bf16_bits *xr = XwT + (pt * 16 + r16) * F::QS + 32 * S + 4 * g4;
-                        acc[pt] = mfma_bf16(as_bf16x8(*reinterpret_cast<const uint2 *>(xr),
-                                                      *reinterpret_cast<const uint2 *>(xr + 16)),
-                                            as_bf16x8(gfrag[m][S]), acc[pt]);
+                        const bf16_bits *xr = XwT + (pt * 16 + r16) * F::QS + 32 * L + 4 * g4;
+                        xlo[L][pt] = *reinterpret_cast<const uint2 *>(xr);
+                        xhi[L][pt] = *reinterpret_cast<const uint2 *>(xr + 16);
                     }
-                }
 #pragma unroll
-                for (int pt = 0; pt < F::PT; ++pt) {
-                    const bf16_bits *xr = XwT + (pt * 16 + r16) * F::QS + 32 * nsb + 4 * g4;
-                    acc[pt] = mfma_bf16(as_bf16x8(*reinterpret_cast<const uint2 *>(xr),
-                                                  *reinterpret_cast<const uint2 *>(xr + 16)),
-                                        as_bf16x8(gdmask[m]), acc[pt]);
+                for (int S = 0; S <= (kFW / 2) * (m + 1) - 1; ++S) {   // nsb's bound
+                    if (S > nsb) break;
+                    const int L = S + DP - 1;
+                    if (L <= nsb) {
+#pragma unroll
+                        for (int pt = 0; pt < F::PT; ++pt) {
+                            const bf16_bits *xr = XwT + (pt * 16 + r16) * F::QS + 32 * L + 4 * g4;
+                            xlo[L % DP][pt] = *reinterpret_cast<const uint2 *>(xr);
+                            xhi[L % DP][pt] = *reinterpret_cast<const uint2 *>(xr + 16);
+                        }
+                    }
+                    if (DP > 1) __builtin_amdgcn_sched_barrier(0);
+                    const uint4 gop = S < nsb ? gfrag[m][S] : gdmask[m];
+#pragma unroll
+                    for (int pt = 0; pt < F::PT; ++pt)
+                        acc[m][pt] = mfma_bf16(as_bf16x8(xlo[S % DP][pt], xhi[S % DP][pt]),
+                                               as_bf16x8(gop), acc[m][pt]);
                 }
                 const float u = tv ? __builtin_amdgcn_exp2f(at - aend) : 0.f;
 #pragma unroll
-                for (int pt = 0; pt < F::PT; ++pt) acc[pt] *= u;
+                for (int pt = 0; pt < F::PT; ++pt) acc[m][pt] *= u;
             } else {
                 // exact fallback: entering state decays by 2^acum_t; every score tile
                 // (off-diagonal and the masked diagonal one) is multiplied element by
                 // element by dt_s 2^(acum_t - acum_s) and contracted with x as given
                 const float e0 = tv ? exp2_dec(at) : 0.f;
 #pragma unroll
-                for (int pt = 0; pt < F::PT; ++pt) acc[pt] *= e0;
+                for (int pt = 0; pt < F::PT; ++pt) acc[m][pt] *= e0;
                 // a rolled loop (rare path, kept small): the score fragment of block S
                 // is picked from the register array with a static select chain
 #pragma unroll 1
@@ -556,23 +651,34 @@ __global__ __launch_bounds__(kFT, 1) void k_ssd_fused(
                                                             pack_bf16x2(mv[6], mv[7])));
 #pragma unroll
                     for (int pt = 0; pt < F::PT; ++pt) {
-                        const bf16_bits *xr = XT + (pt * 16 + r16) * F::QS + 32 * S + 4 * g4;
-                        acc[pt] = mfma_bf16(as_bf16x8(*reinterpret_cast<const uint2 *>(xr),
-                                                      *reinterpret_cast<const uint2 *>(xr + 16)),
-                                            mop, acc[pt]);
+                        // x as given, channel pt * 16 + r16, the fragment's eight tokens
+                        const bf16_bits *xc = XN + (32 * S + 4 * g4) * F::XS + pt * 16 + r16;
+                        uint32_t xw[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int s0 = (q < 2 ? 2 * q : 16 + 2 * (q - 2)) * F::XS;
+                            xw[q] = uint32_t(xc[s0]) | (uint32_t(xc[s0 + F::XS]) << 16);
+                        }
+                        acc[m][pt] = mfma_bf16(as_bf16x8(make_uint4(xw[0], xw[1], xw[2], xw[3])),
+                                               mop, acc[m][pt]);
                     }
                 }
             }
             // epilogue: + D x, round to bf16, store y[t][p..p+3]
             if (tv) {
-                bf16_bits *yrow = y + (tok0 + t) * size_t(H) * P + size_t(h) * P;
+                uint2 xd[F::PT];   // x[t][p0 .. p0+3]
+#pragma unroll
+                for (int pt = 0; pt < F::PT; ++pt)
+                    xd[pt] = *reinterpret_cast<const uint2 *>(XN + t * F::XS + pt * 16 + 4 * g4);
+                bf16_bits *yrow = y + (tok0 * H + h) * P + uint32_t(t * H * P);
 #pragma unroll
                 for (int pt = 0; pt < F::PT; ++pt) {
                     const int p0 = pt * 16 + 4 * g4;
                     float o[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        o[i] = acc[pt][i] + Dh * bf16_to_f32(XT[(p0 + i) * F::QS + t]);
+                    o[0] = acc[m][pt][0] + Dh * bf16_lo(xd[pt].x);
+                    o[1] = acc[m][pt][1] + Dh * bf16_hi(xd[pt].x);
+                    o[2] = acc[m][pt][2] + Dh * bf16_lo(xd[pt].y);
+                    o[3] = acc[m][pt][3] + Dh * bf16_hi(xd[pt].y);
                     *reinterpret_cast<uint2 *>(yrow + p0) =
                         make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
                 }
