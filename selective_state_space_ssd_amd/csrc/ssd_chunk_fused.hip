@@ -105,45 +105,37 @@ __device__ __forceinline__ uint4 ld_b128_off(const void *base, uint32_t byte_off
 // never be inf and turn a discarded 0 * inf into NaN.
 __device__ __forceinline__ float exp2_dec(float x) { return __builtin_amdgcn_exp2f(fminf(x, 0.f)); }
 
-// Stage a [Q tokens][W channels] bf16 slice (token t at src + t * tok_stride) into
-// LDS transposed, dst[w * stride + t], in blocks of 8 tokens x 8 channels: eight
-// 16-byte row loads, a register transpose, eight 16-byte LDS stores.  Consecutive
-// lanes take consecutive token blocks, so the stores of a wave hit distinct banks.
-// With kScaled, row t is multiplied by wt[t] first (and rounded to bf16) and written
-// to dst_scaled as well as unscaled to dst (when dst is non-null).
-template <bool kScaled>
-__device__ __forceinline__ void stage_tok8(const bf16_bits *__restrict__ src, size_t tok_stride,
-                                           int W, int Q, int qlen, bf16_bits *dst,
-                                           bf16_bits *dst_scaled, int stride, const float *wt) {
-    const int TG = Q / 8, items = TG * (W / 8);
-    for (int it = threadIdx.x; it < items; it += kFT) {
+// Stage the chunk's B rows ([Q tokens][N channels] bf16, token t at
+// src + t * tok_stride) into LDS twice from one read: transposed, bt[n * bt_stride + t]
+// (k = token contiguous, for the chunk-state contraction), and in natural order,
+// bn[t * bn_stride + n] for n < NPAD (zero padded; for the score tiles).  Work items
+// are blocks of 8 tokens x 8 channels: eight 16-byte row loads, all issued before
+// any LDS store, a register transpose, 16-byte LDS stores.  Consecutive lanes take
+// consecutive token blocks.
+template <int kThreads, int Q, int N, int NPAD>
+__device__ __forceinline__ void stage_B(const bf16_bits *__restrict__ src, size_t tok_stride,
+                                        int qlen, bf16_bits *bt, int bt_stride, bf16_bits *bn,
+                                        int bn_stride) {
+    constexpr int TG = Q / 8, items = TG * (NPAD / 8);
+#pragma unroll
+    for (int it0 = 0; it0 < items; it0 += kThreads) {
+        const int it = it0 + int(threadIdx.x);
+        if (items % kThreads != 0 && it >= items) break;
         const int t8 = 8 * (it % TG), w0 = 8 * (it / TG);
         uint4 rows[8], cols[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            rows[i] = t8 + i < qlen
+            rows[i] = (t8 + i < qlen && w0 < N)
                           ? *reinterpret_cast<const uint4 *>(src + size_t(t8 + i) * tok_stride + w0)
                           : make_uint4(0, 0, 0, 0);
-        if (dst) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            *reinterpret_cast<uint4 *>(bn + (t8 + i) * bn_stride + w0) = rows[i];
+        if (w0 < N) {
             transpose8x8_b16(rows, cols);
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                *reinterpret_cast<uint4 *>(dst + (w0 + j) * stride + t8) = cols[j];
-        }
-        if constexpr (kScaled) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float f = wt[t8 + i];
-                uint4 &r = rows[i];
-                r = make_uint4(pack_bf16x2(bf16_lo(r.x) * f, bf16_hi(r.x) * f),
-                               pack_bf16x2(bf16_lo(r.y) * f, bf16_hi(r.y) * f),
-                               pack_bf16x2(bf16_lo(r.z) * f, bf16_hi(r.z) * f),
-                               pack_bf16x2(bf16_lo(r.w) * f, bf16_hi(r.w) * f));
-            }
-            transpose8x8_b16(rows, cols);
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                *reinterpret_cast<uint4 *>(dst_scaled + (w0 + j) * stride + t8) = cols[j];
+                *reinterpret_cast<uint4 *>(bt + (w0 + j) * bt_stride + t8) = cols[j];
         }
     }
 }
@@ -196,28 +188,9 @@ void k_ssd_fused(
     const size_t tok0 = size_t(bi) * L + t0;
     const bool last = (c == nc - 1);
 
-    // ---- B of the chunk, transposed, for the chunk-state contraction (step 2), and
-    // in natural layout (over the x / state regions, free until the head loop) for
-    // the score tiles
-    stage_tok8<false>(B + (tok0 * G + g) * N, size_t(G) * N, N, Q, qlen, BT, nullptr, F::QS,
-                      nullptr);
-    bf16_bits *Bnat = XwT;   // [Q][HS]
-    {
-        constexpr int VPR = F::NPAD / 8;
-        for (int it = tid; it < Q * VPR; it += kFT) {
-            const int r = it / VPR, w0 = (it % VPR) * 8;
-            *reinterpret_cast<uint4 *>(Bnat + r * F::HS + w0) =
-                ld_bf16x8_global(B + ((tok0 + r) * G + g) * N + w0, r < qlen && w0 < N);
-        }
-    }
-
-    // dt of the block's heads for the whole chunk, [head][token] (0 past the end)
-    for (int it = tid; it < 4 * 256; it += kFT) {
-        const int j = it >> 8, t = it & 255;
-        dtl[it] = (j < HB && t < qlen) ? dt[(tok0 + t) * H + h0 + j] : 0.f;
-    }
+    // ---- global loads of the prologue, all issued before the first LDS store:
     // C rows of this wave's output tiles (B-operand layout: column t, k = n), kept for
-    // the whole workgroup
+    // the whole workgroup; dt of the block's heads for the whole chunk; B of the chunk
     uint4 cf[F::TPW][F::NK];
 #pragma unroll
     for (int m = 0; m < F::TPW; ++m) {
@@ -230,6 +203,21 @@ void k_ssd_fused(
                                          T < F::NT && t < qlen && n0 < N);
         }
     }
+    static_assert((4 * 256) % kFT == 0, "dt staging assumes whole rounds");
+    float dtv[4 * 256 / kFT];   // dt[head][token], 0 past the end
+#pragma unroll
+    for (int r = 0; r < 4 * 256 / kFT; ++r) {
+        const int it = r * kFT + tid, j = it >> 8, t = it & 255;
+        dtv[r] = (j < HB && t < qlen) ? dt[(tok0 + t) * H + h0 + j] : 0.f;
+    }
+    // B of the chunk: transposed for the chunk-state contraction (step 2), and in
+    // natural layout (over the x / state regions, free until the head loop) for the
+    // score tiles
+    bf16_bits *Bnat = XwT;   // [Q][HS]
+    stage_B<kFT, Q, N, F::NPAD>(B + (tok0 * G + g) * N, size_t(G) * N, qlen, BT, F::QS, Bnat,
+                                F::HS);
+#pragma unroll
+    for (int r = 0; r < 4 * 256 / kFT; ++r) dtl[r * kFT + tid] = dtv[r];
     __syncthreads();
 
     // ---- G^T = B C^T tiles of this wave's output tiles, kept as MFMA B operands
