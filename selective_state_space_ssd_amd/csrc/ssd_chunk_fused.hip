@@ -32,6 +32,9 @@
 //
 // Step 1, 2 and 4 contractions use v_mfma_f32_16x16x32_bf16 with fp32 accumulation;
 // the in-chunk decay cumsum is a wavefront scan.
+#include <algorithm>
+#include <cmath>
+
 #include "ssd_device.h"
 #include "ssd_kernels.h"
 #include "ssd_stage.h"
@@ -66,7 +69,7 @@ struct Fz {
     static constexpr int NTW = NTN >= kFW ? NTN / kFW : 1;
     static constexpr int WPN = NTN >= kFW ? 1 : kFW / NTN;     // waves per column tile
     static constexpr int PTW = NTN >= kFW ? PT : (PT >= WPN ? PT / WPN : 1);
-    static constexpr size_t kScalars = 6208;       // acum, dts [256], dt of 4 heads [4][256], misc
+    static constexpr size_t kScalars = 3104;       // acum, dts, dtn [256], misc
     static constexpr size_t kLds = kScalars + size_t(N) * QS * 2 + size_t(P) * QS * 2 +
                                    size_t(Q) * XS * 2 + size_t(P) * HS * 2;
     // B in natural layout is staged, before the head loop, over the x / state regions
@@ -164,8 +167,8 @@ void k_ssd_fused(
     extern __shared__ __align__(16) unsigned char smem[];
     float *acum = reinterpret_cast<float *>(smem);     // [256] log2-domain decay cumsum
     float *dts = acum + 256;                            // [256] dt of the current head
-    float *dtl = dts + 256;                             // [4][256] dt of the block's heads
-    int *misc = reinterpret_cast<int *>(dtl + 4 * 256); // [8]
+    float *dtn = dts + 256;                             // [256] dt of the next head
+    int *misc = reinterpret_cast<int *>(dtn + 256);     // [8]
     bf16_bits *BT = reinterpret_cast<bf16_bits *>(smem + F::kScalars);   // [N][QS]
     bf16_bits *XwT = BT + N * F::QS;                    // [P][QS] block-decayed dt x
     bf16_bits *XN = XwT + P * F::QS;                    // [Q][XS] x as given, token-major
@@ -190,7 +193,7 @@ void k_ssd_fused(
 
     // ---- global loads of the prologue, all issued before the first LDS store:
     // C rows of this wave's output tiles (B-operand layout: column t, k = n), kept for
-    // the whole workgroup; dt of the block's heads for the whole chunk; B of the chunk
+    // the whole workgroup; B of the chunk
     uint4 cf[F::TPW][F::NK];
 #pragma unroll
     for (int m = 0; m < F::TPW; ++m) {
@@ -203,21 +206,14 @@ void k_ssd_fused(
                                          T < F::NT && t < qlen && n0 < N);
         }
     }
-    static_assert((4 * 256) % kFT == 0, "dt staging assumes whole rounds");
-    float dtv[4 * 256 / kFT];   // dt[head][token], 0 past the end
-#pragma unroll
-    for (int r = 0; r < 4 * 256 / kFT; ++r) {
-        const int it = r * kFT + tid, j = it >> 8, t = it & 255;
-        dtv[r] = (j < HB && t < qlen) ? dt[(tok0 + t) * H + h0 + j] : 0.f;
-    }
+    // dt of the first head, thread tid < Q holding token tid (0 past the end)
+    if (tid < Q) dtn[tid] = tid < qlen ? dt[(tok0 + tid) * H + h0] : 0.f;
     // B of the chunk: transposed for the chunk-state contraction (step 2), and in
     // natural layout (over the x / state regions, free until the head loop) for the
     // score tiles
     bf16_bits *Bnat = XwT;   // [Q][HS]
     stage_B<kFT, Q, N, F::NPAD>(B + (tok0 * G + g) * N, size_t(G) * N, qlen, BT, F::QS, Bnat,
                                 F::HS);
-#pragma unroll
-    for (int r = 0; r < 4 * 256 / kFT; ++r) dtl[r * kFT + tid] = dtv[r];
     __syncthreads();
 
     // ---- G^T = B C^T tiles of this wave's output tiles, kept as MFMA B operands
@@ -286,11 +282,10 @@ void k_ssd_fused(
 
     // ---- per-head x.  Lane l of every wave owns the four tokens 4l .. 4l+3 (for the
     // decay cumsum, which each wave computes for the whole chunk on its own, and for
-    // staging x); wave w stages channels 8w .. 8w+7.  x is loaded one head ahead,
-    // except where two workgroups share a CU and the registers are too few for it
-    // (N > 32): there the other workgroup covers the load latency and x is loaded at
-    // the start of its head.
-    constexpr bool kPrefetchX = F::kWgPerCu == 1 || N <= 32;
+    // staging x); wave w stages channels 8w .. 8w+7.  With one workgroup per CU, x is
+    // loaded one head ahead; with two, the other workgroup covers the load latency
+    // and the registers are worth more, so x is loaded at the start of its head.
+    constexpr bool kPrefetchX = F::kWgPerCu == 1;
     const int tq0 = 4 * lane;
     uint4 xq[4];       // x rows of the lane's 4 tokens, channels 8w .. 8w+7
     if constexpr (kPrefetchX) {
@@ -320,9 +315,12 @@ void k_ssd_fused(
         const float Al2 = A[h] * kLog2e;
         float dq[4], aq[4];
         {
-            const float4 d4 = *reinterpret_cast<const float4 *>(dtl + hh * 256 + tq0);
+            const float4 d4 = *reinterpret_cast<const float4 *>(dtn + tq0);
             dq[0] = d4.x; dq[1] = d4.y; dq[2] = d4.z; dq[3] = d4.w;
         }
+        // dt of the next head (thread tid < Q holds token tid), stored to dtn once
+        // every wave has read this head's values (after the staging barrier)
+        const float dt_next = (hh + 1 < HB && tid < qlen) ? dt[(tok0 + tid) * H + h + 1] : 0.f;
         aq[0] = dq[0] * Al2;
         aq[1] = aq[0] + dq[1] * Al2;
         aq[2] = aq[1] + dq[2] * Al2;
@@ -373,6 +371,7 @@ void k_ssd_fused(
         }
         __syncthreads();
 
+        if (tid < Q) dtn[tid] = dt_next;
         // ---- step 2: S_c = XwT^T B (x already carries dt and the decay to the chunk end)
         f32x4 accS[F::PTW][F::NTW];
 #pragma unroll
@@ -682,6 +681,33 @@ __global__ void k_fused_reset(uint32_t *hdr, uint32_t *flags, size_t nflags) {
     if (i < nflags) flags[i] = 0u;
 }
 
+// Heads per workgroup.  A workgroup computes the chunk's score tiles once (cost
+// about one head) and then runs its HB heads one after another, so a larger HB
+// amortises the score tiles but makes fewer, longer work items.  With `slots`
+// workgroups resident at a time, the estimate in head-times is
+//   ceil(items / slots) * (1 + HB)  +  (chunks of one head in flight - 1) * link,
+// the second term being the fill of the chunk-to-chunk hand-off chain (one link
+// costs about 0.3 of a head).  HB ranges over the divisors of H / G up to 16
+// (a block never straddles two groups); ties go to the smaller HB.
+int heads_per_workgroup(int b, int H, int G, int nc, int slots) {
+    const int hpg = H / G;
+    int best = 1;
+    double best_t = 0.0;
+    for (int hb = 1; hb <= 16 && hb <= hpg; ++hb) {
+        if (hpg % hb) continue;
+        const double chains = double(b) * (H / hb);
+        const double items = chains * nc;
+        const double rounds = std::ceil(items / slots);
+        const double inflight = std::min(double(nc), std::ceil(slots / chains));
+        const double t = rounds * (1.0 + hb) + (inflight - 1.0) * 0.3;
+        if (hb == 1 || t < best_t - 1e-9) {
+            best = hb;
+            best_t = t;
+        }
+    }
+    return best;
+}
+
 template <int Q, int N>
 hipError_t launch_fused_qn(const ChunkScanArgs &a, const FusedPlan &fp, hipStream_t stream) {
     using F = Fz<Q, N>;
@@ -697,13 +723,19 @@ hipError_t launch_fused_qn(const ChunkScanArgs &a, const FusedPlan &fp, hipStrea
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_ssd_fused<Q, N>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(F::kLds));
     if (e != hipSuccess) return e;
-    const int nchains = a.b * (a.H / fp.HB);
+    int dev = 0, cus = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int HB = heads_per_workgroup(a.b, a.H, a.G, fp.nc, std::max(1, cus) * F::kWgPerCu);
+    const int nchains = a.b * (a.H / HB);
     const unsigned items = unsigned(nchains) * unsigned(fp.nc);
     hipLaunchKernelGGL((k_ssd_fused<Q, N>), dim3(items), dim3(kFT), F::kLds, stream,
                        static_cast<const bf16_bits *>(a.x), a.dt, a.A,
                        static_cast<const bf16_bits *>(a.B), static_cast<const bf16_bits *>(a.C),
                        a.D, a.init_state, static_cast<bf16_bits *>(a.y), a.final_state, hbuf,
-                       flags, hdr, a.L, a.H, a.G, fp.HB, nchains, fp.nc);
+                       flags, hdr, a.L, a.H, a.G, HB, nchains, fp.nc);
     return hipGetLastError();
 }
 
@@ -755,10 +787,9 @@ FusedPlan plan_fused(int b, int L, int H, int P, int N, int G, int Q, bool bf16)
     if (G <= 0 || H % G != 0) return fp;
     const size_t lds = fused_lds_bytes(Q, N);
     if (lds > kMaxLds) return fp;
-    const int hpg = H / G;
-    fp.HB = hpg % 4 == 0 ? 4 : (hpg % 2 == 0 ? 2 : 1);
+    fp.HB = 1;   // the launch picks the heads per workgroup for the device it runs on
     fp.nc = (L + Q - 1) / Q;
-    const size_t items = size_t(b) * (H / fp.HB) * fp.nc;
+    const size_t items = size_t(b) * H * fp.nc;   // upper bound (one head per workgroup)
     if (items > 0x7fffffffu) return fp;
     fp.off_hdr = 0;
     fp.off_flags = 256;

@@ -64,7 +64,7 @@ ChunkScanPlan plan_chunk_scan(int b, int L, int H, int P, int N, int G, int Q, b
 // state ring per (batch, head) for the chunk-to-chunk hand-off.
 struct FusedPlan {
     int nc = 0;
-    int HB = 1;                 // heads per workgroup (all of one group)
+    int HB = 1;                 // heads per workgroup (the launch picks it per device)
     size_t off_hdr = 0;         // uint32 [64]: ticket, time-out error word
     size_t off_flags = 0;       // uint32 [b, H, nc]
     size_t off_hbuf = 0;        // fp32   [b, H, 2, P, N]
