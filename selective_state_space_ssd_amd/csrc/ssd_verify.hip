@@ -11,8 +11,8 @@
 // requested).  Layout of the work: a row p of the P x N state is spread over LR
 // consecutive lanes, each holding J float4 chunks whose columns interleave so that
 // one load instruction of the wave covers whole 128-byte row segments; the
-// reduction y = C . h over N is an in-lane sum followed by log2(LR) lane
-// butterflies.
+// reduction y = C . h over N is an in-lane sum followed by DPP lane moves.  B and C
+// of the K tokens are shared by every row of a block and are staged once into LDS.
 #include "ssd_device.h"
 #include "ssd_kernels.h"
 
@@ -27,6 +27,23 @@ struct VerifyShape {
     static_assert(J >= 1 && LR >= 1 && (N % (4 * LR)) == 0, "unsupported N");
 };
 
+// Sum over the LR consecutive lanes of a state row (LR in {4, 8}) with DPP lane
+// moves inside the VALU: swap neighbours, swap pairs, then (LR = 8) fold the two
+// quads of the 8-lane row half onto each other.
+template <int LR>
+__device__ __forceinline__ float row_sum(float v) {
+    static_assert(LR == 4 || LR == 8, "row_sum covers 4 or 8 lanes");
+    constexpr int kQuadSwap1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+    constexpr int kQuadSwap2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+    constexpr int kRowHalfMirror = 0x141;   // lane i <-> lane 7 - i within 8 lanes
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kQuadSwap1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kQuadSwap2, 0xF, 0xF, false));
+    if constexpr (LR == 8)
+        v += __int_as_float(
+            __builtin_amdgcn_update_dpp(0, __float_as_int(v), kRowHalfMirror, 0xF, 0xF, false));
+    return v;
+}
+
 template <typename IO>
 __device__ __forceinline__ float4 load4(const IO *p) {
     if constexpr (std::is_same_v<IO, float>) {
@@ -38,6 +55,9 @@ __device__ __forceinline__ float4 load4(const IO *p) {
     }
 }
 
+// B and C of the K tokens (group g) are staged once per block into LDS as fp32
+// ([K][N] each); the state loads are issued before the staging so their latency
+// overlaps it.
 template <typename IO, int N>
 __global__ __launch_bounds__(256) void k_verify(
     const float *state_in, const IO *__restrict__ x, const float *__restrict__ dt,
@@ -46,6 +66,8 @@ __global__ __launch_bounds__(256) void k_verify(
     float *state_out, float *__restrict__ states_all, int32_t *err_flag, int K, int H, int P,
     int G) {
     using S = VerifyShape<N>;
+    extern __shared__ __align__(16) float sbc[];   // [K][N] B, then [K][N] C
+    float *sB = sbc, *sC = sbc + K * N;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane % S::LR, rw = lane / S::LR;
     const int p = blockIdx.x * S::RB + wave * S::RW + rw;
@@ -62,6 +84,22 @@ __global__ __launch_bounds__(256) void k_verify(
         s[j] = valid ? *reinterpret_cast<const float4 *>(state_in + row + n)
                      : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    // per-token inputs of this row, loaded before the staging barrier
+    constexpr int kMaxK = 16;
+    // x and y of this (b, h): token k, row p at [k * H * P + p] from these bases
+    const size_t xy0 = (size_t(bi) * K * H + h) * P;
+    const uint32_t tok_stride = uint32_t(H) * uint32_t(P);
+    float xr[kMaxK];
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k)
+        xr[k] = (k < K && valid) ? to_f32<IO>(x[xy0 + (uint32_t(k) * tok_stride + uint32_t(p))])
+                                 : 0.f;
+    for (int i = 4 * int(threadIdx.x); i < K * N; i += 4 * 256) {
+        const int k = i / N, n = i % N;
+        const size_t src = ((size_t(bi) * K + k) * G + g) * N + n;
+        *reinterpret_cast<float4 *>(sB + i) = load4<IO>(B + src);
+        *reinterpret_cast<float4 *>(sC + i) = load4<IO>(C + src);
+    }
 
     int a = accept_len[bi];
     if (a < 0 || a > K) {
@@ -73,31 +111,32 @@ __global__ __launch_bounds__(256) void k_verify(
         for (int j = 0; j < S::J; ++j)
             *reinterpret_cast<float4 *>(state_out + row + j * 4 * S::LR + lr * 4) = s[j];
     }
+    __syncthreads();
 
     const float Ah = A[h], Dh = D[h];
-    for (int k = 0; k < K; ++k) {
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+        if (k >= K) break;
         const size_t tk = size_t(bi) * K + k;
         const float d = dt[tk * H + h];
         const float decay = expf(d * Ah);
-        const float xk = valid ? to_f32<IO>(x[(tk * H + h) * P + p]) : 0.f;
+        const float xk = xr[k];
         const float u = d * xk;
-        const IO *Bk = B + (tk * G + g) * N;
-        const IO *Ck = C + (tk * G + g) * N;
         float part = 0.f;
 #pragma unroll
         for (int j = 0; j < S::J; ++j) {
             const int n = j * 4 * S::LR + lr * 4;
-            const float4 bb = load4<IO>(Bk + n);
-            const float4 cc = load4<IO>(Ck + n);
+            const float4 bb = *reinterpret_cast<const float4 *>(sB + k * N + n);
+            const float4 cc = *reinterpret_cast<const float4 *>(sC + k * N + n);
             s[j].x = decay * s[j].x + u * bb.x;
             s[j].y = decay * s[j].y + u * bb.y;
             s[j].z = decay * s[j].z + u * bb.z;
             s[j].w = decay * s[j].w + u * bb.w;
             part += cc.x * s[j].x + cc.y * s[j].y + cc.z * s[j].z + cc.w * s[j].w;
         }
-#pragma unroll
-        for (int off = 1; off < S::LR; off <<= 1) part += __shfl_xor(part, off, 64);
-        if (valid && lr == 0) y[(tk * H + h) * P + p] = from_f32<IO>(part + Dh * xk);
+        part = row_sum<S::LR>(part);
+        if (valid && lr == 0)
+            y[xy0 + (uint32_t(k) * tok_stride + uint32_t(p))] = from_f32<IO>(part + Dh * xk);
         if (valid) {
             if (states_all) {
                 float *dst = states_all + ((tk * H + h) * P + p) * N;
@@ -118,7 +157,8 @@ template <typename IO, int N>
 static hipError_t launch_verify_n(const VerifyArgs &a, hipStream_t stream) {
     using S = VerifyShape<N>;
     dim3 grid((a.P + S::RB - 1) / S::RB, a.H, a.b);
-    hipLaunchKernelGGL((k_verify<IO, N>), grid, dim3(256), 0, stream, a.state_in,
+    const size_t lds = size_t(2) * a.K * N * sizeof(float);
+    hipLaunchKernelGGL((k_verify<IO, N>), grid, dim3(256), lds, stream, a.state_in,
                        static_cast<const IO *>(a.x), a.dt, a.A, static_cast<const IO *>(a.B),
                        static_cast<const IO *>(a.C), a.D, a.accept_len, static_cast<IO *>(a.y),
                        a.state_out, a.states_all, a.err_flag, a.K, a.H, a.P, a.G);
