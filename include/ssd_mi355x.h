@@ -73,6 +73,26 @@ size_t ssd_chunk_scan_workspace_bytes(int b, int L, int H, int P, int N, int G, 
                                       ssd_dtype_t io);
 
 /*
+ * ssd_chunk_scan_workspace_init -- prepare a workspace once, before its first use
+ * by ssd_chunk_scan_fwd (enqueued on hip_stream; workspace_bytes as allocated, at
+ * least what the calls need, 16-byte aligned).
+ *
+ * The bf16 chunk scan hands each chunk's state to the next chunk through the
+ * workspace: a work-item ticket and one ready flag per (batch, head, chunk).  This
+ * call zeroes them (and writes a marker); every ssd_chunk_scan_fwd call that
+ * completes leaves them zero again, so a prepared workspace serves any number of
+ * later calls, of any shape that fits, one at a time (calls that overlap on one
+ * workspace race).  A call that finds the workspace not prepared does not wait:
+ * the outputs of every chunk after the first then hold NaN.  After a call that
+ * timed out waiting for a neighbouring chunk (the device broke its forward-progress
+ * guarantee; the affected outputs are NaN), or that was aborted, prepare the
+ * workspace again.  Returns SSD_ERR_NULL_ARG for a NULL workspace with
+ * workspace_bytes > 0, SSD_ERR_ALIGN, or SSD_ERR_HIP.
+ */
+ssd_status_t ssd_chunk_scan_workspace_init(void *workspace, size_t workspace_bytes,
+                                           void *hip_stream);
+
+/*
  * ssd_chunk_scan_fwd -- SSD chunked scan over a whole sequence.
  *
  * Method (Mamba-2 article, «SSD 算法：分块和形态传递»): the sequence is cut into
@@ -96,10 +116,10 @@ size_t ssd_chunk_scan_workspace_bytes(int b, int L, int H, int P, int N, int G, 
  *   final_state[b, H, P, N]  fp32     state after token L-1 (written); NULL = skip
  *   Q                                 chunk length: 64, 128 or 256 (the last chunk
  *                                     may be shorter: L need not be a multiple of Q)
- *   workspace, workspace_bytes        scratch of at least
- *                                     ssd_chunk_scan_workspace_bytes(...) bytes,
- *                                     16-byte aligned; its contents on entry are
- *                                     ignored and on exit undefined
+ *   workspace, workspace_bytes        at least ssd_chunk_scan_workspace_bytes(...)
+ *                                     bytes, 16-byte aligned, prepared once by
+ *                                     ssd_chunk_scan_workspace_init and left to the
+ *                                     library between calls
  * Supported on this build: P in {16, 32, 64, 128}, N a multiple of 16 in [16, 256],
  * and the chunk tiles must fit the 160 KiB LDS of one CU (else
  * SSD_ERR_UNSUPPORTED).  b == 0 or L == 0 is a valid empty problem (final_state

@@ -28,8 +28,8 @@ STATUS_NAMES = {
 }
 
 # Every symbol declared in include/ssd_mi355x.h
-EXPORTED = ("ssd_chunk_scan_workspace_bytes", "ssd_chunk_scan_fwd", "ssd_verify_step",
-            "ssd_status_string", "ssd_version")
+EXPORTED = ("ssd_chunk_scan_workspace_bytes", "ssd_chunk_scan_workspace_init",
+            "ssd_chunk_scan_fwd", "ssd_verify_step", "ssd_status_string", "ssd_version")
 
 _lib = None
 
@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
         vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
         L.ssd_chunk_scan_workspace_bytes.argtypes = [i32] * 7 + [i32]
         L.ssd_chunk_scan_workspace_bytes.restype = sz
+        L.ssd_chunk_scan_workspace_init.argtypes = [vp, sz, vp]
+        L.ssd_chunk_scan_workspace_init.restype = i32
         L.ssd_chunk_scan_fwd.argtypes = [vp] * 9 + [i32] * 7 + [i32, vp, sz, vp]
         L.ssd_chunk_scan_fwd.restype = i32
         L.ssd_verify_step.argtypes = [vp] * 12 + [i32] * 6 + [i32, vp]
@@ -105,6 +107,15 @@ def ssd_chunk_scan_workspace_bytes(b, L, H, P, N, G, Q, io: int) -> int:
     return n
 
 
+def ssd_chunk_scan_workspace_init(workspace: torch.Tensor, stream=None) -> None:
+    """Prepare a workspace (uint8 GPU tensor) once before its first chunk-scan call."""
+    st = lib().ssd_chunk_scan_workspace_init(_ptr(workspace, "workspace"),
+                                             workspace.numel() * workspace.element_size(),
+                                             _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_chunk_scan_workspace_init")
+
+
 def ssd_chunk_scan_fwd(x, dt, A, B, C, D, init_state, y, final_state, Q, workspace,
                        stream=None) -> None:
     """Enqueue the chunked scan on ``stream`` (default: torch's current stream).
@@ -146,11 +157,14 @@ def ssd_verify_step(state_in, x, dt, A, B, C, D, accept_len, y, state_out, state
 
 
 # ------------------------------------------------------------ allocating wrappers
-def chunk_scan_workspace(x, B, Q) -> torch.Tensor:
+def chunk_scan_workspace(x, B, Q, stream=None) -> torch.Tensor:
+    """Allocate and prepare a workspace for chunk scans of x's and B's shapes."""
     b, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     n = ssd_chunk_scan_workspace_bytes(b, L, H, P, N, G, Q, _io_code(x))
-    return torch.empty(max(n, 1), dtype=torch.uint8, device=x.device)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
+    ssd_chunk_scan_workspace_init(ws, stream)
+    return ws
 
 
 def chunk_scan_fwd(x, dt, A, B, C, D, Q, init_state=None, workspace=None, stream=None):

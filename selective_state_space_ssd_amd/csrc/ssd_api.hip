@@ -51,6 +51,16 @@ size_t ssd_chunk_scan_workspace_bytes(int b, int L, int H, int P, int N, int G, 
     return ssd::plan_chunk_scan(b, L, H, P, N, G, Q, bf16).total;
 }
 
+ssd_status_t ssd_chunk_scan_workspace_init(void *workspace, size_t workspace_bytes,
+                                           void *hip_stream) {
+    if (workspace_bytes == 0) return SSD_OK;
+    if (!workspace) return SSD_ERR_NULL_ARG;
+    if (!aligned(workspace, 16)) return SSD_ERR_ALIGN;
+    const hipError_t e = ssd::launch_workspace_init(workspace, workspace_bytes,
+                                                    static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
 ssd_status_t ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, const void *B,
                                 const void *C, const float *D, const float *init_state, void *y,
                                 float *final_state, int b, int L, int H, int P, int N, int G,

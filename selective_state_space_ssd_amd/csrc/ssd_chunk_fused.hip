@@ -180,9 +180,31 @@ void k_ssd_fused(
     const int w = Q == 256 ? tid >> 6 : __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, g4 = lane >> 4;
 
-    if (tid == 0) misc[0] = int(atomicAdd(&hdr[0], 1u));
+    if (tid == 0) {
+        // A prepared workspace carries the magic word.  The first 8 bytes of the
+        // header hold the work-item count (low half) and the call number ("epoch",
+        // high half); one 64-bit atomic add gives a workgroup both its ticket and
+        // the epoch, and the workgroup that takes the last ticket wraps the count
+        // back to 0 and advances the epoch for the next call.  Ready flags carry
+        // epoch + 1, so flags left by earlier calls (or other shapes' data in the
+        // flag region) never read as ready.  Without a prepared workspace every item
+        // runs at its own index and never waits (its handed-over states are NaN).
+        const uint32_t magic =
+            __hip_atomic_load(&hdr[kWsMagicWord], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t old = atomicAdd(reinterpret_cast<unsigned long long *>(hdr), 1ull);
+        const uint32_t count = uint32_t(old), epoch = uint32_t(old >> 32);
+        const bool prepared = magic == kWsMagic && count < gridDim.x;
+        if (prepared && count == gridDim.x - 1u)
+            atomicAdd(reinterpret_cast<unsigned long long *>(hdr), (1ull << 32) - gridDim.x);
+        const int ticket = prepared ? int(count) : int(blockIdx.x);
+        misc[0] = ticket;
+        misc[2] = prepared;
+        misc[3] = int(epoch + 1u);
+    }
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(misc[0]);   // uniform: keep it scalar
+    const bool ws_ok = __builtin_amdgcn_readfirstlane(misc[2]) != 0;
+    const uint32_t ready = uint32_t(__builtin_amdgcn_readfirstlane(misc[3]));   // flag value
     const int c = item / nchains, chain = item % nchains;
     const int hblocks = H / HB;
     const int bi = chain / hblocks, h0 = (chain % hblocks) * HB;
@@ -422,15 +444,16 @@ void k_ssd_fused(
         const float *hsrc = nullptr;   // state entering this chunk, fp32 [P][N]; null = zeros
         bool coherent = false, poisoned = false;
         if (c > 0) {
-            const uint32_t *flag = flags + bh * nc + (c - 1);
+            uint32_t *flag = flags + bh * nc + (c - 1);
             if (tid == 0) {
                 uint32_t it = 0;
-                int ok = 1;
-                while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+                int ok = ws_ok;
+                while (ok && __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != ready) {
                     __builtin_amdgcn_s_sleep(2);
                     if (++it > kSpinLimit) {
                         ok = 0;
-                        __hip_atomic_store(&hdr[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(&hdr[kWsErrorWord], 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
                         break;
                     }
                 }
@@ -517,7 +540,7 @@ void k_ssd_fused(
         if (!last) wait_vm();   // this wave's state stores are complete and visible
         __syncthreads();
         if (!last && tid == 0)
-            __hip_atomic_store(flags + bh * nc + c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(flags + bh * nc + c, ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
         // ---- steps 1 and 4 for this wave's output tiles
         const float Dh = D[h];
@@ -675,11 +698,6 @@ void k_ssd_fused(
     }
 }
 
-__global__ void k_fused_reset(uint32_t *hdr, uint32_t *flags, size_t nflags) {
-    const size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i < 64) hdr[i] = 0u;
-    if (i < nflags) flags[i] = 0u;
-}
 
 // Heads per workgroup.  A workgroup computes the chunk's score tiles once (cost
 // about one head) and then runs its HB heads one after another, so a larger HB
@@ -715,12 +733,7 @@ hipError_t launch_fused_qn(const ChunkScanArgs &a, const FusedPlan &fp, hipStrea
     uint32_t *hdr = reinterpret_cast<uint32_t *>(ws + fp.off_hdr);
     uint32_t *flags = reinterpret_cast<uint32_t *>(ws + fp.off_flags);
     float *hbuf = reinterpret_cast<float *>(ws + fp.off_hbuf);
-    const size_t nflags = size_t(a.b) * a.H * fp.nc;
-    hipLaunchKernelGGL(k_fused_reset, dim3(unsigned((nflags + 64 + 255) / 256)), dim3(256), 0,
-                       stream, hdr, flags, nflags);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_ssd_fused<Q, N>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_ssd_fused<Q, N>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(F::kLds));
     if (e != hipSuccess) return e;
     int dev = 0, cus = 0;
@@ -778,6 +791,23 @@ size_t fused_lds_bytes(int Q, int N) {
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 }  // namespace
+
+namespace {
+__global__ void k_workspace_init(uint32_t *ws, size_t words) {
+    const size_t stride = size_t(gridDim.x) * blockDim.x;
+    for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < words; i += stride)
+        ws[i] = i == size_t(kWsMagicWord) ? kWsMagic : 0u;
+}
+}  // namespace
+
+hipError_t launch_workspace_init(void *workspace, size_t bytes, hipStream_t stream) {
+    const size_t words = bytes / 4;
+    if (words == 0) return hipSuccess;
+    const size_t blocks = std::min<size_t>((words + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_workspace_init, dim3(unsigned(blocks)), dim3(256), 0, stream,
+                       static_cast<uint32_t *>(workspace), words);
+    return hipGetLastError();
+}
 
 FusedPlan plan_fused(int b, int L, int H, int P, int N, int G, int Q, bool bf16) {
     FusedPlan fp;

@@ -59,13 +59,19 @@ struct ChunkScanPlan {
 
 ChunkScanPlan plan_chunk_scan(int b, int L, int H, int P, int N, int G, int Q, bool bf16);
 
-// Single-pass kernel (bf16 I/O, P = 64, N in {16, 32, 64, 128, 256}): workspace holds
-// a ticket/error header, one ready flag per (batch, head, chunk) and a two-slot fp32
-// state ring per (batch, head) for the chunk-to-chunk hand-off.
+// Workspace of the single-pass kernel: a 256-byte header, one ready flag per (batch,
+// head, chunk) and a two-slot fp32 state ring per (batch, head) for the chunk-to-chunk
+// hand-off.  Header words: 0 = work-item count and 1 = call number (one 64-bit
+// word), 2 = time-out error word, 32 = magic word (its own cache line).
+// ssd_chunk_scan_workspace_init zeroes it and writes the magic word; every completed
+// call leaves the count at zero and advances the call number, which tags its flags.
+constexpr uint32_t kWsMagic = 0x55d5ca11u;
+constexpr int kWsErrorWord = 2;
+constexpr int kWsMagicWord = 32;
 struct FusedPlan {
     int nc = 0;
     int HB = 1;                 // heads per workgroup (the launch picks it per device)
-    size_t off_hdr = 0;         // uint32 [64]: ticket, time-out error word
+    size_t off_hdr = 0;         // uint32 [64]: ticket count, call number, error, magic
     size_t off_flags = 0;       // uint32 [b, H, nc]
     size_t off_hbuf = 0;        // fp32   [b, H, 2, P, N]
     size_t total = 0;
@@ -80,5 +86,7 @@ hipError_t launch_chunk_scan(const ChunkScanArgs &a, const ChunkScanPlan &plan,
 // final_state = init_state (or zeros) for an empty sequence.
 hipError_t launch_copy_state(const float *init_state, float *final_state, size_t count,
                              hipStream_t stream);
+// Zero the workspace and write the magic word.
+hipError_t launch_workspace_init(void *workspace, size_t bytes, hipStream_t stream);
 
 }  // namespace ssd

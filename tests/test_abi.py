@@ -107,6 +107,12 @@ def test_scan_misaligned(lib, name, mis):
     assert scan_call(lib, {name: addr(idx, mis)}) == ALIGN
 
 
+def test_workspace_init_checks(lib):
+    assert lib.ssd_chunk_scan_workspace_init(None, 0, None) == OK          # nothing to do
+    assert lib.ssd_chunk_scan_workspace_init(None, 4096, None) == NULL
+    assert lib.ssd_chunk_scan_workspace_init(addr(9, 8), 4096, None) == ALIGN
+
+
 def test_scan_workspace_checks(lib):
     need = bd.ssd_chunk_scan_workspace_bytes(1, 256, 4, 16, 16, 1, 64, 1)
     assert scan_call(lib, ws_bytes=need - 1) == WS

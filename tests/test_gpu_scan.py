@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import TOL, run_scan, scan_errors, to_f64
+from gpu_helpers import TOL, oracle_scan, run_scan, scan_errors, to_f64
 from selective_state_space_ssd_amd import binding as bd
 from selective_state_space_ssd_amd import inputs
 
@@ -130,3 +130,37 @@ def _extreme_decay_inputs(seed, heads_slow):
                          ids=["mixed", "all_extreme"])
 def test_extreme_decay_takes_exact_path(heads_slow):
     _check(_extreme_decay_inputs(17, heads_slow))
+
+
+def test_prepared_workspace_serves_calls_of_several_shapes():
+    """One workspace, prepared once, then reused by calls of different shapes: the
+    ticket counter and the ready flags must be left clean by every call."""
+    shapes = [(2, 700, 8, 64, 128, 2, 256), (1, 300, 4, 64, 64, 1, 128),
+              (2, 1100, 8, 64, 128, 2, 256), (1, 129, 2, 64, 16, 1, 64)]
+    need = max(bd.ssd_chunk_scan_workspace_bytes(b, L, H, P, N, G, Q, bd.SSD_DTYPE_BF16)
+               for b, L, H, P, N, G, Q in shapes)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    bd.ssd_chunk_scan_workspace_init(ws)
+    for rep in range(2):
+        for i, (b, L, H, P, N, G, Q) in enumerate(shapes):
+            inp = inputs.make_scan_inputs(b, L, H, P, N, G, Q, io="bf16", init=bool(i % 2),
+                                          seed=100 + i)
+            y, fs = run_scan(inp, workspace=ws)
+            ey, ef = scan_errors(inp, y, fs)
+            assert ey <= TOL["bf16"] and ef <= TOL["bf16"], (rep, i, ey, ef)
+
+
+def test_unprepared_workspace_gives_nan_not_garbage():
+    """A workspace that was never prepared: the call must not wait on it; the first
+    chunk is still exact and every output that depends on a handed-over state is NaN."""
+    inp = inputs.make_scan_inputs(1, 512, 4, 64, 128, 1, 256, io="bf16", init=False, seed=12)
+    n = bd.ssd_chunk_scan_workspace_bytes(1, 512, 4, 64, 128, 1, 256, bd.SSD_DTYPE_BF16)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")     # zero, but no marker
+    y, fs = run_scan(inp, workspace=ws)
+    yo = to_f64(y)
+    ref, _ = oracle_scan(inp)
+    first = yo[:, :256]
+    assert np.isfinite(first).all()
+    assert np.max(np.abs(first - ref[:, :256])) <= TOL["bf16"] * np.max(np.abs(ref[:, :256]))
+    assert np.isnan(yo[:, 256:]).all()
+    assert np.isnan(to_f64(fs)).all()
