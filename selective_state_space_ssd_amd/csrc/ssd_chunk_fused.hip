@@ -347,12 +347,7 @@ void k_ssd_fused(
         aq[1] = aq[0] + dq[1] * Al2;
         aq[2] = aq[1] + dq[2] * Al2;
         aq[3] = aq[2] + dq[3] * Al2;
-        float run = aq[3];
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float o = __shfl_up(run, off, 64);
-            if (lane >= off) run += o;
-        }
+        const float run = wave_inclusive_scan(aq[3]);
         const float excl = run - aq[3];
 #pragma unroll
         for (int k = 0; k < 4; ++k) aq[k] += excl;   // constant past qlen (dt = 0 there)

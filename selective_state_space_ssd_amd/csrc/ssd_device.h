@@ -103,6 +103,26 @@ __device__ __forceinline__ void transpose4x8_b16(const uint4 (&in)[4], uint2 (&o
     }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves (no LDS
+// traffic): a Hillis-Steele scan inside each row of 16 lanes (shift right by 1, 2,
+// 4, 8; lanes shifted in from outside the row add 0), then the total of row 0 is
+// added to rows 1 and 3 and the total of rows 0-1 to rows 2 and 3.
+__device__ __forceinline__ float wave_inclusive_scan(float v) {
+    constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+    constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+    auto shifted = [](float x, auto ctrl) {
+        return __int_as_float(
+            __builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value, 0xF, 0xF, true));
+    };
+    v += shifted(v, std::integral_constant<int, kRowShr1>{});
+    v += shifted(v, std::integral_constant<int, kRowShr2>{});
+    v += shifted(v, std::integral_constant<int, kRowShr4>{});
+    v += shifted(v, std::integral_constant<int, kRowShr8>{});
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kRowBcast15, 0xA, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kRowBcast31, 0xC, 0xF, false));
+    return v;
+}
+
 // Inclusive prefix sum over the first 64 * kWaves threads of the block (the other
 // waves only take part in the barriers).  `tmp` is LDS scratch of at least kWaves
 // floats; the call contains two block barriers.
