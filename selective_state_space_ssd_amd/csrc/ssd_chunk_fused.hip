@@ -693,7 +693,6 @@ void k_ssd_fused(
     }
 }
 
-
 // Heads per workgroup.  A workgroup computes the chunk's score tiles once (cost
 // about one head) and then runs its HB heads one after another, so a larger HB
 // amortises the score tiles but makes fewer, longer work items.  With `slots`
