@@ -684,8 +684,9 @@ void k_ssd_fused(
                     o[1] = acc[m][pt][1] + Dh * bf16_hi(xd[pt].x);
                     o[2] = acc[m][pt][2] + Dh * bf16_lo(xd[pt].y);
                     o[3] = acc[m][pt][3] + Dh * bf16_hi(xd[pt].y);
-                    *reinterpret_cast<uint2 *>(yrow + p0) =
-                        make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+                    // streaming store: y is not read again by this kernel
+                    const u32x2 v = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(yrow + p0));
                 }
             }
         }
