@@ -81,8 +81,13 @@ __global__ __launch_bounds__(256) void k_verify(
 #pragma unroll
     for (int j = 0; j < S::J; ++j) {
         const int n = j * 4 * S::LR + lr * 4;
-        s[j] = valid ? *reinterpret_cast<const float4 *>(state_in + row + n)
-                     : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (valid) {   // the state streams through once: non-temporal load and stores
+            const f32x4 t4 =
+                __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(state_in + row + n));
+            s[j] = make_float4(t4.x, t4.y, t4.z, t4.w);
+        } else {
+            s[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
     }
     // per-token inputs of this row, loaded before the staging barrier
     constexpr int kMaxK = 16;
@@ -109,7 +114,8 @@ __global__ __launch_bounds__(256) void k_verify(
     if (a == 0 && valid) {
 #pragma unroll
         for (int j = 0; j < S::J; ++j)
-            *reinterpret_cast<float4 *>(state_out + row + j * 4 * S::LR + lr * 4) = s[j];
+            __builtin_nontemporal_store(f32x4{s[j].x, s[j].y, s[j].z, s[j].w},
+                                            reinterpret_cast<f32x4 *>(state_out + row + j * 4 * S::LR + lr * 4));
     }
     __syncthreads();
 
@@ -142,12 +148,14 @@ __global__ __launch_bounds__(256) void k_verify(
                 float *dst = states_all + ((tk * H + h) * P + p) * N;
 #pragma unroll
                 for (int j = 0; j < S::J; ++j)
-                    *reinterpret_cast<float4 *>(dst + j * 4 * S::LR + lr * 4) = s[j];
+                    __builtin_nontemporal_store(f32x4{s[j].x, s[j].y, s[j].z, s[j].w},
+                                                reinterpret_cast<f32x4 *>(dst + j * 4 * S::LR + lr * 4));
             }
             if (k + 1 == a) {
 #pragma unroll
                 for (int j = 0; j < S::J; ++j)
-                    *reinterpret_cast<float4 *>(state_out + row + j * 4 * S::LR + lr * 4) = s[j];
+                    __builtin_nontemporal_store(f32x4{s[j].x, s[j].y, s[j].z, s[j].w},
+                                            reinterpret_cast<f32x4 *>(state_out + row + j * 4 * S::LR + lr * 4));
             }
         }
     }
