@@ -102,6 +102,15 @@ __device__ __forceinline__ uint4 ld_b128_off(const void *base, uint32_t byte_off
               : make_uint4(0, 0, 0, 0);
 }
 
+// A buffer resource over `bytes` bytes from `base` (raw addressing, stride 0): a
+// buffer access at a byte offset >= bytes is dropped (store) or reads 0 (load) by the
+// hardware range check.  The last word is the gfx9-family default (32-bit data format,
+// no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, int(bytes), 0x00020000);
+}
+constexpr int kBufNonTemporal = 2;   // cache-policy bits of a buffer access: nt
+
 // A decay factor 2^x, x <= 0, with the hardware transcendental (results below the
 // normal range flush to zero, which is what a decay factor that small means).  The
 // argument is clamped at 0 so that a value computed for a masked-out (s > t) pair can
@@ -212,6 +221,8 @@ void k_ssd_fused(
     const int t0 = c * Q, qlen = min(Q, L - t0);
     const size_t tok0 = size_t(bi) * L + t0;
     const bool last = (c == nc - 1);
+    const __amdgpu_buffer_rsrc_t yres =
+        buffer_rsrc(y + tok0 * H * P, uint32_t(qlen) * uint32_t(H * P) * 2u);
 
     // ---- global loads of the prologue, all issued before the first LDS store:
     // C rows of this wave's output tiles (B-operand layout: column t, k = n), kept for
@@ -228,14 +239,48 @@ void k_ssd_fused(
                                          T < F::NT && t < qlen && n0 < N);
         }
     }
-    // dt of the first head, thread tid < Q holding token tid (0 past the end)
-    if (tid < Q) dtn[tid] = tid < qlen ? dt[(tok0 + tid) * H + h0] : 0.f;
+    // x and dt are read through range-checked buffer views of the chunk's qlen rows:
+    // rows past them read 0, and no load sits behind a branch, so the compiler can
+    // count the memory operations in flight and wait only for the ones it needs.
+    // Thread tid < Q holds dt of token tid.  x is staged in blocks of 4 tokens x 8
+    // channels: lane l of wave w holds tokens xt0 .. xt0+3, xt0 = 32w + 4(l / 8), and
+    // channels xc0 .. xc0+7, xc0 = 8(l % 8), so that the 8 lanes of a group read one
+    // whole 128-byte row of x per load (8 rows per instruction).  The decay cumsum
+    // uses another layout (lane l: tokens 4l .. 4l+3, computed by every wave for the
+    // whole chunk); lane xsl of that layout holds the staging lane's tokens.
+    const __amdgpu_buffer_rsrc_t xres =
+        buffer_rsrc(x + tok0 * H * P, uint32_t(qlen) * uint32_t(H * P) * 2u);
+    const __amdgpu_buffer_rsrc_t dtres = buffer_rsrc(dt + tok0 * H, uint32_t(qlen) * uint32_t(H) * 4u);
+    const int tq0 = 4 * lane;
+    const int xsl = 8 * w + (lane >> 3), xt0 = 4 * xsl, xc0 = 8 * (lane & 7);
+    auto load_x = [&](uint4 (&xq)[4], int hx) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            xq[k] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                           xres, int((((xt0 + k) * H + hx) * P + xc0) * 2), 0, 0));
+    };
+    auto load_dt = [&](int hx) {   // 0 past qlen; a head past the block reads unused data
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(dtres, int((tid * H + hx) * 4), 0, 0));
+    };
+    // With one workgroup per CU nothing else covers load latency: x is loaded one
+    // head ahead and dt two heads ahead (the value for head h + 1 is loaded while
+    // head h - 1 is processed; one strided 4-byte read per token).  With two, the
+    // other workgroup covers it and the registers are worth more: x and dt are
+    // loaded at the start of the head before the one they serve.  The first head's
+    // loads are issued before B's, whose wait retires them.
+    constexpr bool kPrefetchX = F::kWgPerCu == 1;
+    const float dt_first = load_dt(h0);
+    float dt_pipe = kPrefetchX ? load_dt(h0 + 1) : 0.f;
+    uint4 xq[4];       // x of the lane's 4 staging tokens, channels xc0 .. xc0+7
+    if constexpr (kPrefetchX) load_x(xq, h0);
     // B of the chunk: transposed for the chunk-state contraction (step 2), and in
     // natural layout (over the x / state regions, free until the head loop) for the
     // score tiles
     bf16_bits *Bnat = XwT;   // [Q][HS]
     stage_B<kFT, Q, N, F::NPAD>(B + (tok0 * G + g) * N, size_t(G) * N, qlen, BT, F::QS, Bnat,
                                 F::HS);
+    if (tid < Q) dtn[tid] = dt_first;
     __syncthreads();
 
     // ---- G^T = B C^T tiles of this wave's output tiles, kept as MFMA B operands
@@ -302,20 +347,6 @@ void k_ssd_fused(
     constexpr int NT_STEP = kFW, PT_STEP = F::NTN >= kFW ? 1 : F::WPN;
     const bool s_active = pt_base < F::PT;
 
-    // ---- per-head x.  Lane l of every wave owns the four tokens 4l .. 4l+3 (for the
-    // decay cumsum, which each wave computes for the whole chunk on its own, and for
-    // staging x); wave w stages channels 8w .. 8w+7.  With one workgroup per CU, x is
-    // loaded one head ahead; with two, the other workgroup covers the load latency
-    // and the registers are worth more, so x is loaded at the start of its head.
-    constexpr bool kPrefetchX = F::kWgPerCu == 1;
-    const int tq0 = 4 * lane;
-    uint4 xq[4];       // x rows of the lane's 4 tokens, channels 8w .. 8w+7
-    if constexpr (kPrefetchX) {
-        const bf16_bits *src = x + (tok0 * H + h0) * P;   // uniform base
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            xq[k] = ld_b128_off(src, uint32_t(((tq0 + k) * H * P + 8 * w) * 2), tq0 + k < qlen);
-    }
     // zero the padding columns of the entering-state tile once
     if constexpr (F::NPAD > N) {
         for (int it = tid; it < P * (F::NPAD - N); it += kFT)
@@ -327,13 +358,7 @@ void k_ssd_fused(
         const size_t bh = size_t(bi) * H + h;
         // ---- discretisation and in-chunk decay cumsum (inclusive, log2 domain),
         // computed by every wave for all tokens: 4 tokens per lane + a wave scan
-        if constexpr (!kPrefetchX) {
-            const bf16_bits *src = x + (tok0 * H + h) * P;   // uniform base
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                xq[k] = ld_b128_off(src, uint32_t(((tq0 + k) * H * P + 8 * w) * 2),
-                                    tq0 + k < qlen);
-        }
+        if constexpr (!kPrefetchX) load_x(xq, h);
         const float Al2 = A[h] * kLog2e;
         float dq[4], aq[4];
         {
@@ -342,7 +367,7 @@ void k_ssd_fused(
         }
         // dt of the next head (thread tid < Q holds token tid), stored to dtn once
         // every wave has read this head's values (after the staging barrier)
-        const float dt_next = (hh + 1 < HB && tid < qlen) ? dt[(tok0 + tid) * H + h + 1] : 0.f;
+        const float dt_next = kPrefetchX ? dt_pipe : load_dt(h + 1);
         aq[0] = dq[0] * Al2;
         aq[1] = aq[0] + dq[1] * Al2;
         aq[2] = aq[1] + dq[2] * Al2;
@@ -359,14 +384,18 @@ void k_ssd_fused(
         }
         // ---- x of this head: x as given, token-major (for the D x term), and x
         // decayed to the chunk end (times dt), transposed to [channel][token]; 4 tokens
-        // x 8 channels per lane
-        if (tq0 < Q) {
+        // x 8 channels per lane.  The factors are computed in the cumsum layout and
+        // fetched from lane xsl.
+        float xf[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) xf[k] = __shfl(exp2_dec(aend - aq[k]) * dq[k], xsl, 64);
+        if (xt0 < Q) {
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                *reinterpret_cast<uint4 *>(XN + (tq0 + k) * F::XS + 8 * w) = xq[k];
+                *reinterpret_cast<uint4 *>(XN + (xt0 + k) * F::XS + xc0) = xq[k];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const float f = exp2_dec(aend - aq[k]) * dq[k];
+                const float f = xf[k];
                 uint4 &r = xq[k];
                 r = make_uint4(pack_bf16x2(bf16_lo(r.x) * f, bf16_hi(r.x) * f),
                                pack_bf16x2(bf16_lo(r.y) * f, bf16_hi(r.y) * f),
@@ -377,14 +406,7 @@ void k_ssd_fused(
             transpose4x8_b16(xq, cols);
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                *reinterpret_cast<uint2 *>(XwT + (8 * w + j) * F::QS + tq0) = cols[j];
-        }
-        if (kPrefetchX && hh + 1 < HB) {   // next head's x, in flight during this head
-            const bf16_bits *src = x + (tok0 * H + h + 1) * P;   // uniform base
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                xq[k] = ld_b128_off(src, uint32_t(((tq0 + k) * H * P + 8 * w) * 2),
-                                    tq0 + k < qlen);
+                *reinterpret_cast<uint2 *>(XwT + (xc0 + j) * F::QS + xt0) = cols[j];
         }
         __syncthreads();
 
@@ -536,6 +558,13 @@ void k_ssd_fused(
         __syncthreads();
         if (!last && tid == 0)
             __hip_atomic_store(flags + bh * nc + c, ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if constexpr (kPrefetchX) {
+            // loads for the heads ahead, issued after the hand-off so that its wait for
+            // the state stores does not wait for them too: x of the next head, in
+            // flight during this head's outputs, and dt of the head after it
+            if (hh + 1 < HB) load_x(xq, h + 1);
+            dt_pipe = load_dt(h + 2);
+        }
 
         // ---- steps 1 and 4 for this wave's output tiles
         const float Dh = D[h];
@@ -583,14 +612,17 @@ void k_ssd_fused(
         }
 #pragma unroll
         for (int m = 0; m < F::TPW; ++m) {
-            if (!slot_ok[m]) continue;
             const int T = tile_of(m, w);
             const int tl0 = 16 * T;
             const int t = tl0 + r16;
             const bool tv = t < qlen;
             const int nsb = T / 2;
-            const float at = acum[t];
-            if (fast) {
+            if (!slot_ok[m]) {
+                // nothing to compute; the epilogue still runs (its stores fall outside
+                // the chunk's rows and are dropped) so that every wave issues the same
+                // stores on every path
+            } else if (fast) {
+                const float at = acum[t];
                 // step 1, all blocks up to and including the diagonal one, against x
                 // decayed to the chunk end; then rescale column t to its own token.
                 // The x fragments of block S + kDepth - 1 are read while block S is
@@ -631,6 +663,7 @@ void k_ssd_fused(
                 // exact fallback: entering state decays by 2^acum_t; every score tile
                 // (off-diagonal and the masked diagonal one) is multiplied element by
                 // element by dt_s 2^(acum_t - acum_s) and contracted with x as given
+                const float at = acum[t];
                 const float e0 = tv ? exp2_dec(at) : 0.f;
 #pragma unroll
                 for (int pt = 0; pt < F::PT; ++pt) acc[m][pt] *= e0;
@@ -669,24 +702,42 @@ void k_ssd_fused(
                     }
                 }
             }
-            // epilogue: + D x, round to bf16, store y[t][p..p+3]
-            if (tv) {
+            // epilogue: + D x, round to bf16, store y[t][p..p+3].  The stores go through
+            // a buffer resource that covers the chunk's qlen rows: rows past them are
+            // dropped by the range check, so no lane or wave branches around a store
+            // (and the compiler can count the stores in flight when it waits for the
+            // next head's x).  Streaming (non-temporal): y is not read again here.
+            {
                 uint2 xd[F::PT];   // x[t][p0 .. p0+3]
+                const int tx = min(t, Q - 1);
 #pragma unroll
                 for (int pt = 0; pt < F::PT; ++pt)
-                    xd[pt] = *reinterpret_cast<const uint2 *>(XN + t * F::XS + pt * 16 + 4 * g4);
-                bf16_bits *yrow = y + (tok0 * H + h) * P + uint32_t(t * H * P);
+                    xd[pt] = *reinterpret_cast<const uint2 *>(XN + tx * F::XS + pt * 16 + 4 * g4);
+                const uint32_t row_off = uint32_t((t * H + h) * P) * 2u;
+                uint32_t v[F::PT][2];   // bf16 pairs of channels pt*16 + 4*g4 + 0..3
 #pragma unroll
                 for (int pt = 0; pt < F::PT; ++pt) {
-                    const int p0 = pt * 16 + 4 * g4;
                     float o[4];
                     o[0] = acc[m][pt][0] + Dh * bf16_lo(xd[pt].x);
                     o[1] = acc[m][pt][1] + Dh * bf16_hi(xd[pt].x);
                     o[2] = acc[m][pt][2] + Dh * bf16_lo(xd[pt].y);
                     o[3] = acc[m][pt][3] + Dh * bf16_hi(xd[pt].y);
-                    // streaming store: y is not read again by this kernel
-                    const u32x2 v = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-                    __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(yrow + p0));
+                    v[pt][0] = pack_bf16x2(o[0], o[1]);
+                    v[pt][1] = pack_bf16x2(o[2], o[3]);
+                }
+                // regroup channel tiles pt, pt+1 between lane rows (v_permlane16_swap:
+                // odd rows of the first operand trade places with even rows of the
+                // second) so that each lane holds 8 consecutive channels: row g4 gets
+                // channels (pt + (g4 & 1)) * 16 + (g4 >> 1) * 8 + 0..7, and the four
+                // lanes of a token write 64 contiguous bytes per store
+#pragma unroll
+                for (int pt = 0; pt < F::PT; pt += 2) {
+                    const auto s0 = __builtin_amdgcn_permlane16_swap(v[pt][0], v[pt + 1][0], false, false);
+                    const auto s1 = __builtin_amdgcn_permlane16_swap(v[pt][1], v[pt + 1][1], false, false);
+                    const u32x4 q = {s0[0], s1[0], s0[1], s1[1]};
+                    const int c0 = (pt + (g4 & 1)) * 16 + (g4 >> 1) * 8;
+                    __builtin_amdgcn_raw_buffer_store_b128(q, yres, int(row_off + 2u * c0), 0,
+                                                           kBufNonTemporal);
                 }
             }
         }
