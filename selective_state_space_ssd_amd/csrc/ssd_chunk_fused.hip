@@ -152,14 +152,13 @@ __device__ __forceinline__ void stage_B(const bf16_bits *__restrict__ src, size_
     }
 }
 
-// Device-coherent accesses for the chunk-to-chunk state hand-off (another
-// workgroup, possibly on another XCD, reads what this one writes).
-__device__ __forceinline__ float ld_coherent(const float *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_coherent(float *p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// The chunk-to-chunk state hand-off is read by another workgroup, possibly on another
+// XCD: its loads and stores carry the device-scope cache policy (sc1), the same bits
+// an agent-scope relaxed atomic access gets.  In the ring the state is kept in the
+// accumulator layout: 16x16 tile (pt, nt) at float offset (pt * N/16 + nt) * 256, lane
+// l's four values (rows 4(l/16) + i, column l % 16) at l * 4 + i, so that each lane
+// moves 16 bytes per access.
+constexpr int kBufDevice = 16;   // cache-policy bits of a buffer access: sc1
 // Wait until this wave's outstanding memory operations have completed.
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -500,12 +499,17 @@ void k_ssd_fused(
                         hp[k][j][i] = 0.f;
                     }
             if (coherent) {
+                const __amdgpu_buffer_rsrc_t ring = buffer_rsrc(hsrc, uint32_t(P * N * 4));
 #pragma unroll
                 for (int k = 0; k < F::PTW; ++k)
 #pragma unroll
-                    for (int j = 0; j < F::NTW; ++j)
+                    for (int j = 0; j < F::NTW; ++j) {
+                        const int tile = (pt_base + PT_STEP * k) * F::NTN + nt_base + NT_STEP * j;
+                        const f32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+                            ring, (tile * 64 + lane) * 16, 0, kBufDevice);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) hp[k][j][i] = ld_coherent(hsrc + off[k][j][i]);
+                        for (int i = 0; i < 4; ++i) hp[k][j][i] = v[i];
+                    }
             } else if (hsrc) {
 #pragma unroll
                 for (int k = 0; k < F::PTW; ++k)
@@ -537,13 +541,17 @@ void k_ssd_fused(
                         hp[k][j][i] = alpha * hp[k][j][i] + accS[k][j][i];
                     }
             if (!last) {
-                float *hdst = hbuf + (bh * 2 + (c & 1)) * size_t(P) * N;
+                const __amdgpu_buffer_rsrc_t ring =
+                    buffer_rsrc(hbuf + (bh * 2 + (c & 1)) * size_t(P) * N, uint32_t(P * N * 4));
 #pragma unroll
                 for (int k = 0; k < F::PTW; ++k)
 #pragma unroll
-                    for (int j = 0; j < F::NTW; ++j)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) st_coherent(hdst + off[k][j][i], hp[k][j][i]);
+                    for (int j = 0; j < F::NTW; ++j) {
+                        const int tile = (pt_base + PT_STEP * k) * F::NTN + nt_base + NT_STEP * j;
+                        const f32x4 v = {hp[k][j][0], hp[k][j][1], hp[k][j][2], hp[k][j][3]};
+                        __builtin_amdgcn_raw_buffer_store_b128(v, ring, (tile * 64 + lane) * 16, 0,
+                                                               kBufDevice);
+                    }
             } else if (final_state) {
                 float *fdst = final_state + bh * size_t(P) * N;
 #pragma unroll
