@@ -117,37 +117,65 @@ constexpr int kBufNonTemporal = 2;   // cache-policy bits of a buffer access: nt
 // never be inf and turn a discarded 0 * inf into NaN.
 __device__ __forceinline__ float exp2_dec(float x) { return __builtin_amdgcn_exp2f(fminf(x, 0.f)); }
 
+// Token order of the k dimension in the token-contiguous LDS tiles (x decayed, B
+// transposed).  Inside each 32-token block the 4-token groups are interleaved: token
+// 4g + i (g < 4) sits at 8g + i and token 16 + 4g + i at 8g + 4 + i.  The eight k
+// values a lane of lane group g4 supplies to a 16x16x32 product are then the tokens
+// 4g4 .. 4g4+3 and 16+4g4 .. 16+4g4+3 -- the rows of its score fragment, which comes
+// from an accumulator -- and they are one contiguous 16-byte read.  Both operands of
+// the chunk-state contraction use the same order, so it does not change that sum.
+__device__ __forceinline__ int tok_pos32(int u) {   // u = token within its 32-block
+    return ((u & 12) << 1) | ((u & 16) >> 2) | (u & 3);
+}
+
 // Stage the chunk's B rows ([Q tokens][N channels] bf16, token t at
-// src + t * tok_stride) into LDS twice from one read: transposed, bt[n * bt_stride + t]
-// (k = token contiguous, for the chunk-state contraction), and in natural order,
-// bn[t * bn_stride + n] for n < NPAD (zero padded; for the score tiles).  Work items
-// are blocks of 8 tokens x 8 channels: eight 16-byte row loads, all issued before
-// any LDS store, a register transpose, 16-byte LDS stores.  Consecutive lanes take
-// consecutive token blocks.
+// src + t * tok_stride) into LDS twice from one read: transposed, bt[n * bt_stride + k]
+// (k = token position, order above; for the chunk-state contraction), and in natural
+// order, bn[t * bn_stride + n] for n < NPAD (zero padded; for the score tiles).  Work
+// items are 8 tokens (the ones at 8 consecutive positions) x 8 channels: eight 16-byte
+// row loads, all issued before any LDS store, a register transpose, 16-byte LDS
+// stores.  With at least 8 channel blocks, the 64 items of a wave form an 8 x 8 block
+// of (token block, channel block) taken along diagonals: lane l has token block l % 8
+// and channel block (l % 8 + l / 8) % 8, so that each load instruction reads 8 rows
+// 128 contiguous bytes each, and every 8 consecutive lanes store to distinct banks in
+// both layouts.
 template <int kThreads, int Q, int N, int NPAD>
 __device__ __forceinline__ void stage_B(const bf16_bits *__restrict__ src, size_t tok_stride,
                                         int qlen, bf16_bits *bt, int bt_stride, bf16_bits *bn,
                                         int bn_stride) {
-    constexpr int TG = Q / 8, items = TG * (NPAD / 8);
+    constexpr int TG = Q / 8, CG = NPAD / 8, items = TG * CG;
+    constexpr bool kDiag = CG % 8 == 0 && TG % 8 == 0;
 #pragma unroll
     for (int it0 = 0; it0 < items; it0 += kThreads) {
         const int it = it0 + int(threadIdx.x);
         if (items % kThreads != 0 && it >= items) break;
-        const int t8 = 8 * (it % TG), w0 = 8 * (it / TG);
+        int tb, cb;
+        if constexpr (kDiag) {
+            const int blk = it >> 6, l = it & 63;
+            tb = 8 * (blk % (TG / 8)) + (l & 7);
+            cb = 8 * (blk / (TG / 8)) + (((l & 7) + (l >> 3)) & 7);
+        } else {
+            tb = it % TG;
+            cb = it / TG;
+        }
+        const int w0 = 8 * cb;
+        int tok[8];   // the tokens at positions 8 tb .. 8 tb + 7
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tok[i] = 32 * (tb >> 2) + (i < 4 ? 4 * (tb & 3) + i : 16 + 4 * (tb & 3) + i - 4);
         uint4 rows[8], cols[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            rows[i] = (t8 + i < qlen && w0 < N)
-                          ? *reinterpret_cast<const uint4 *>(src + size_t(t8 + i) * tok_stride + w0)
+            rows[i] = (tok[i] < qlen && w0 < N)
+                          ? *reinterpret_cast<const uint4 *>(src + size_t(tok[i]) * tok_stride + w0)
                           : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            *reinterpret_cast<uint4 *>(bn + (t8 + i) * bn_stride + w0) = rows[i];
+            *reinterpret_cast<uint4 *>(bn + tok[i] * bn_stride + w0) = rows[i];
         if (w0 < N) {
             transpose8x8_b16(rows, cols);
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                *reinterpret_cast<uint4 *>(bt + (w0 + j) * bt_stride + t8) = cols[j];
+                *reinterpret_cast<uint4 *>(bt + (w0 + j) * bt_stride + 8 * tb) = cols[j];
         }
     }
 }
@@ -242,16 +270,18 @@ void k_ssd_fused(
     // rows past them read 0, and no load sits behind a branch, so the compiler can
     // count the memory operations in flight and wait only for the ones it needs.
     // Thread tid < Q holds dt of token tid.  x is staged in blocks of 4 tokens x 8
-    // channels: lane l of wave w holds tokens xt0 .. xt0+3, xt0 = 32w + 4(l / 8), and
-    // channels xc0 .. xc0+7, xc0 = 8(l % 8), so that the 8 lanes of a group read one
-    // whole 128-byte row of x per load (8 rows per instruction).  The decay cumsum
-    // uses another layout (lane l: tokens 4l .. 4l+3, computed by every wave for the
-    // whole chunk); lane xsl of that layout holds the staging lane's tokens.
+    // channels: lane l of wave w holds tokens xt0 .. xt0+3, xt0 = 32w + 4(l % 8), and
+    // channels xc0 .. xc0+7, xc0 = 8(l / 8), so that 8 lanes read one whole 128-byte
+    // row of x per load (8 rows per instruction).  The decay cumsum uses another
+    // layout (lane l: tokens 4l .. 4l+3, computed by every wave for the whole chunk);
+    // lane xsl of that layout holds the staging lane's tokens.  In the decayed copy
+    // they sit at position xp0 (token order of the contraction tiles).
     const __amdgpu_buffer_rsrc_t xres =
         buffer_rsrc(x + tok0 * H * P, uint32_t(qlen) * uint32_t(H * P) * 2u);
     const __amdgpu_buffer_rsrc_t dtres = buffer_rsrc(dt + tok0 * H, uint32_t(qlen) * uint32_t(H) * 4u);
     const int tq0 = 4 * lane;
-    const int xsl = 8 * w + (lane >> 3), xt0 = 4 * xsl, xc0 = 8 * (lane & 7);
+    const int xsl = 8 * w + (lane & 7), xt0 = 4 * xsl, xc0 = 8 * (lane >> 3);
+    const int xp0 = 32 * w + tok_pos32(4 * (lane & 7));
     auto load_x = [&](uint4 (&xq)[4], int hx) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
@@ -405,7 +435,7 @@ void k_ssd_fused(
             transpose4x8_b16(xq, cols);
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                *reinterpret_cast<uint2 *>(XwT + (xc0 + j) * F::QS + xt0) = cols[j];
+                *reinterpret_cast<uint2 *>(XwT + (xc0 + j) * F::QS + xp0) = cols[j];
         }
         __syncthreads();
 
@@ -636,32 +666,28 @@ void k_ssd_fused(
                 // The x fragments of block S + kDepth - 1 are read while block S is
                 // multiplied.
                 constexpr int DP = F::kDepth;
-                uint2 xlo[DP][F::PT], xhi[DP][F::PT];
+                uint4 xf8[DP][F::PT];   // tokens 32S + 4g4 + 0..3 and 32S + 16 + 4g4 + 0..3
 #pragma unroll
                 for (int L = 0; L < DP - 1; ++L)
 #pragma unroll
-                    for (int pt = 0; pt < F::PT; ++pt) {
-                        const bf16_bits *xr = XwT + (pt * 16 + r16) * F::QS + 32 * L + 4 * g4;
-                        xlo[L][pt] = *reinterpret_cast<const uint2 *>(xr);
-                        xhi[L][pt] = *reinterpret_cast<const uint2 *>(xr + 16);
-                    }
+                    for (int pt = 0; pt < F::PT; ++pt)
+                        xf8[L][pt] = *reinterpret_cast<const uint4 *>(
+                            XwT + (pt * 16 + r16) * F::QS + 32 * L + 8 * g4);
 #pragma unroll
                 for (int S = 0; S <= (kFW / 2) * (m + 1) - 1; ++S) {   // nsb's bound
                     if (S > nsb) break;
                     const int L = S + DP - 1;
                     if (L <= nsb) {
 #pragma unroll
-                        for (int pt = 0; pt < F::PT; ++pt) {
-                            const bf16_bits *xr = XwT + (pt * 16 + r16) * F::QS + 32 * L + 4 * g4;
-                            xlo[L % DP][pt] = *reinterpret_cast<const uint2 *>(xr);
-                            xhi[L % DP][pt] = *reinterpret_cast<const uint2 *>(xr + 16);
-                        }
+                        for (int pt = 0; pt < F::PT; ++pt)
+                            xf8[L % DP][pt] = *reinterpret_cast<const uint4 *>(
+                                XwT + (pt * 16 + r16) * F::QS + 32 * L + 8 * g4);
                     }
                     if (DP > 1) __builtin_amdgcn_sched_barrier(0);
                     const uint4 gop = S < nsb ? gfrag[m][S] : gdmask[m];
 #pragma unroll
                     for (int pt = 0; pt < F::PT; ++pt)
-                        acc[m][pt] = mfma_bf16(as_bf16x8(xlo[S % DP][pt], xhi[S % DP][pt]),
+                        acc[m][pt] = mfma_bf16(as_bf16x8(xf8[S % DP][pt]),
                                                as_bf16x8(gop), acc[m][pt]);
                 }
                 const float u = tv ? __builtin_amdgcn_exp2f(at - aend) : 0.f;
