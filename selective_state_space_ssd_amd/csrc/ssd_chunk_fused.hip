@@ -62,13 +62,16 @@ struct Fz {
     static constexpr int NPAD = NK * 32;
     static constexpr int QS = Q + 8;               // LDS row stride, token-contiguous tiles
     static constexpr int HS = NPAD + 8;            // LDS row stride of the state tile
-    static constexpr int XS = P + 8;               // LDS row stride of x in token-major order
+    static constexpr int XS = P;                   // LDS row stride of x in token-major order
     static constexpr int NTN = N / 16;             // state column tiles
-    // state tiles of a wave: with >= 8 column tiles each wave owns whole columns,
-    // otherwise the waves of one column split its channel tiles
-    static constexpr int NTW = NTN >= kFW ? NTN / kFW : 1;
+    // state tiles of a wave (PTW row tiles x NTW column tiles; each operand fragment
+    // read from LDS feeds NTW or PTW products): with 8 column tiles the waves form a
+    // 2 x 4 grid of 2 x 2 blocks; with more, each wave owns whole columns; with fewer,
+    // the waves of one column split its channel tiles
+    static constexpr bool kGrid22 = NTN == 8 && kFW == 8 && PT == 4;
+    static constexpr int NTW = kGrid22 ? 2 : NTN >= kFW ? NTN / kFW : 1;
     static constexpr int WPN = NTN >= kFW ? 1 : kFW / NTN;     // waves per column tile
-    static constexpr int PTW = NTN >= kFW ? PT : (PT >= WPN ? PT / WPN : 1);
+    static constexpr int PTW = kGrid22 ? 2 : NTN >= kFW ? PT : (PT >= WPN ? PT / WPN : 1);
     static constexpr size_t kScalars = 3104;       // acum, dts, dtn [256], misc
     static constexpr size_t kLds = kScalars + size_t(N) * QS * 2 + size_t(P) * QS * 2 +
                                    size_t(Q) * XS * 2 + size_t(P) * HS * 2;
@@ -126,6 +129,14 @@ __device__ __forceinline__ float exp2_dec(float x) { return __builtin_amdgcn_exp
 // the chunk-state contraction use the same order, so it does not change that sum.
 __device__ __forceinline__ int tok_pos32(int u) {   // u = token within its 32-block
     return ((u & 12) << 1) | ((u & 16) >> 2) | (u & 3);
+}
+
+// Element offset of x[t][c] in the token-major LDS copy (64 channels per row, no
+// padding): the eight 8-channel blocks of row t are XOR-swizzled by (t / 4) % 8, so
+// that the 16-byte staging stores of 8 lanes holding 8 consecutive token groups hit
+// distinct banks.
+__device__ __forceinline__ int xn_off(int t, int c) {
+    return t * 64 + 8 * ((c >> 3) ^ ((t >> 2) & 7)) + (c & 7);
 }
 
 // Stage the chunk's B rows ([Q tokens][N channels] bf16, token t at
@@ -207,7 +218,7 @@ void k_ssd_fused(
     int *misc = reinterpret_cast<int *>(dtn + 256);     // [8]
     bf16_bits *BT = reinterpret_cast<bf16_bits *>(smem + F::kScalars);   // [N][QS]
     bf16_bits *XwT = BT + N * F::QS;                    // [P][QS] block-decayed dt x
-    bf16_bits *XN = XwT + P * F::QS;                    // [Q][XS] x as given, token-major
+    bf16_bits *XN = XwT + P * F::QS;                    // [Q][XS] x as given, token-major (xn_off)
     bf16_bits *Hs = XN + Q * F::XS;                     // [P][HS] entering state, bf16
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -371,9 +382,10 @@ void k_ssd_fused(
     }
 
     // state tiles of this wave (step 2 accumulators and the hand-off)
-    const int nt_base = F::NTN >= kFW ? w : (w % F::NTN);
-    const int pt_base = F::NTN >= kFW ? 0 : (w / F::NTN);
-    constexpr int NT_STEP = kFW, PT_STEP = F::NTN >= kFW ? 1 : F::WPN;
+    const int nt_base = F::kGrid22 ? 2 * (w % 4) : F::NTN >= kFW ? w : (w % F::NTN);
+    const int pt_base = F::kGrid22 ? 2 * (w / 4) : F::NTN >= kFW ? 0 : (w / F::NTN);
+    constexpr int NT_STEP = F::kGrid22 ? 1 : kFW;
+    constexpr int PT_STEP = F::kGrid22 || F::NTN >= kFW ? 1 : F::WPN;
     const bool s_active = pt_base < F::PT;
 
     // zero the padding columns of the entering-state tile once
@@ -421,7 +433,7 @@ void k_ssd_fused(
         if (xt0 < Q) {
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                *reinterpret_cast<uint4 *>(XN + (xt0 + k) * F::XS + xc0) = xq[k];
+                *reinterpret_cast<uint4 *>(XN + xn_off(xt0 + k, xc0)) = xq[k];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const float f = xf[k];
@@ -517,17 +529,16 @@ void k_ssd_fused(
             // one read of the entering state, in the accumulator layout: it feeds the
             // update and the bf16 copy in LDS; then the update and all stores
             float hp[F::PTW][F::NTW][4];
-            int off[F::PTW][F::NTW][4];
+            // offset of element (k, j, i) of the wave's tiles in a [P][N] state
+            auto off = [&](int k, int j, int i) {
+                return ((pt_base + PT_STEP * k) * 16 + 4 * g4 + i) * N + (nt_base + NT_STEP * j) * 16 + r16;
+            };
 #pragma unroll
             for (int k = 0; k < F::PTW; ++k)
 #pragma unroll
                 for (int j = 0; j < F::NTW; ++j)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        off[k][j][i] = ((pt_base + PT_STEP * k) * 16 + 4 * g4 + i) * N +
-                                       (nt_base + NT_STEP * j) * 16 + r16;
-                        hp[k][j][i] = 0.f;
-                    }
+                    for (int i = 0; i < 4; ++i) hp[k][j][i] = 0.f;
             if (coherent) {
                 const __amdgpu_buffer_rsrc_t ring = buffer_rsrc(hsrc, uint32_t(P * N * 4));
 #pragma unroll
@@ -546,7 +557,7 @@ void k_ssd_fused(
 #pragma unroll
                     for (int j = 0; j < F::NTW; ++j)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) hp[k][j][i] = hsrc[off[k][j][i]];
+                        for (int i = 0; i < 4; ++i) hp[k][j][i] = hsrc[off(k, j, i)];
             }
             if (poisoned) {
 #pragma unroll
@@ -589,7 +600,7 @@ void k_ssd_fused(
 #pragma unroll
                     for (int j = 0; j < F::NTW; ++j)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) fdst[off[k][j][i]] = hp[k][j][i];
+                        for (int i = 0; i < 4; ++i) fdst[off(k, j, i)] = hp[k][j][i];
             }
         }
         if (!last) wait_vm();   // this wave's state stores are complete and visible
@@ -724,12 +735,12 @@ void k_ssd_fused(
 #pragma unroll
                     for (int pt = 0; pt < F::PT; ++pt) {
                         // x as given, channel pt * 16 + r16, the fragment's eight tokens
-                        const bf16_bits *xc = XN + (32 * S + 4 * g4) * F::XS + pt * 16 + r16;
+                        const int c = pt * 16 + r16, s0 = 32 * S + 4 * g4;
                         uint32_t xw[4];
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
-                            const int s0 = (q < 2 ? 2 * q : 16 + 2 * (q - 2)) * F::XS;
-                            xw[q] = uint32_t(xc[s0]) | (uint32_t(xc[s0 + F::XS]) << 16);
+                            const int s = s0 + (q < 2 ? 2 * q : 16 + 2 * (q - 2));
+                            xw[q] = uint32_t(XN[xn_off(s, c)]) | (uint32_t(XN[xn_off(s + 1, c)]) << 16);
                         }
                         acc[m][pt] = mfma_bf16(as_bf16x8(make_uint4(xw[0], xw[1], xw[2], xw[3])),
                                                mop, acc[m][pt]);
@@ -746,7 +757,7 @@ void k_ssd_fused(
                 const int tx = min(t, Q - 1);
 #pragma unroll
                 for (int pt = 0; pt < F::PT; ++pt)
-                    xd[pt] = *reinterpret_cast<const uint2 *>(XN + tx * F::XS + pt * 16 + 4 * g4);
+                    xd[pt] = *reinterpret_cast<const uint2 *>(XN + xn_off(tx, pt * 16 + 4 * g4));
                 const uint32_t row_off = uint32_t((t * H + h) * P) * 2u;
                 uint32_t v[F::PT][2];   // bf16 pairs of channels pt*16 + 4*g4 + 0..3
 #pragma unroll
