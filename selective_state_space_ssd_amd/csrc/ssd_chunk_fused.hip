@@ -60,8 +60,12 @@ struct Fz {
     static constexpr int TPW = (NT + kFW - 1) / kFW;   // output tiles per wave
     static constexpr int NK = (N + 31) / 32;       // 32-wide k-steps over N
     static constexpr int NPAD = NK * 32;
-    static constexpr int QS = Q + 8;               // LDS row stride, token-contiguous tiles
-    static constexpr int HS = NPAD + 8;            // LDS row stride of the state tile
+    // LDS row strides of the token-contiguous tiles and of the state tile.  The pads
+    // of 16 elements make the 16-byte MFMA operand reads (16 rows x 4 lane groups)
+    // conflict-free on gfx950; a pad of 8 gives 2-way bank conflicts (measured with
+    // the LDS bank-conflict counter).
+    static constexpr int QS = Q + 16;
+    static constexpr int HS = NPAD + 16;
     static constexpr int XS = P;                   // LDS row stride of x in token-major order
     static constexpr int NTN = N / 16;             // state column tiles
     // state tiles of a wave (PTW row tiles x NTW column tiles; each operand fragment
@@ -132,11 +136,12 @@ __device__ __forceinline__ int tok_pos32(int u) {   // u = token within its 32-b
 }
 
 // Element offset of x[t][c] in the token-major LDS copy (64 channels per row, no
-// padding): the eight 8-channel blocks of row t are XOR-swizzled by (t / 4) % 8, so
-// that the 16-byte staging stores of 8 lanes holding 8 consecutive token groups hit
-// distinct banks.
+// padding): the eight 8-channel blocks of row t are XOR-swizzled by
+// ((t / 4) ^ 2 (t % 4)) % 8.  With it both the 16-byte staging stores (8 lanes on 8
+// consecutive token groups) and the 8-byte reads of the D x epilogue (16 lanes on 16
+// consecutive tokens) are free of bank conflicts (measured on gfx950).
 __device__ __forceinline__ int xn_off(int t, int c) {
-    return t * 64 + 8 * ((c >> 3) ^ ((t >> 2) & 7)) + (c & 7);
+    return t * 64 + 8 * ((c >> 3) ^ (((t >> 2) ^ ((t & 3) << 1)) & 7)) + (c & 7);
 }
 
 // Stage the chunk's B rows ([Q tokens][N channels] bf16, token t at
