@@ -109,14 +109,6 @@ __device__ __forceinline__ uint4 ld_b128_off(const void *base, uint32_t byte_off
               : make_uint4(0, 0, 0, 0);
 }
 
-// A buffer resource over `bytes` bytes from `base` (raw addressing, stride 0): a
-// buffer access at a byte offset >= bytes is dropped (store) or reads 0 (load) by the
-// hardware range check.  The last word is the gfx9-family default (32-bit data format,
-// no swizzle).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, int(bytes), 0x00020000);
-}
-constexpr int kBufNonTemporal = 2;   // cache-policy bits of a buffer access: nt
 
 // A decay factor 2^x, x <= 0, with the hardware transcendental (results below the
 // normal range flush to zero, which is what a decay factor that small means).  The

@@ -58,6 +58,16 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// A buffer resource over `bytes` bytes from `base` (raw addressing, stride 0): a
+// buffer access at a byte offset >= bytes is dropped (store) or reads 0 (load) by the
+// hardware range check, so accesses need no branch around them.  The last word is the
+// gfx9-family default (32-bit data format, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, int(bytes), 0x00020000);
+}
+constexpr int kBufNonTemporal = 2;           // cache-policy bits of a buffer access: nt
+constexpr uint32_t kBufOutOfRange = 0x7ffffff0u;   // a byte offset past any view
+
 // 16 bytes of bf16 bit patterns as an MFMA operand.
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 

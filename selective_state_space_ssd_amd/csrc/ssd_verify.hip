@@ -94,11 +94,27 @@ __global__ __launch_bounds__(256) void k_verify(
     // x and y of this (b, h): token k, row p at [k * H * P + p] from these bases
     const size_t xy0 = (size_t(bi) * K * H + h) * P;
     const uint32_t tok_stride = uint32_t(H) * uint32_t(P);
-    float xr[kMaxK];
+    // x of every token for this row and dt of every token for this head, all loads in
+    // flight at once: range-checked buffer views (K tokens; positions past K and rows
+    // past P read 0), so that no load sits behind a branch and waits on the last
+    float xr[kMaxK], dtr[kMaxK];
+    {
+        const __amdgpu_buffer_rsrc_t xres =
+            buffer_rsrc(x + xy0, (uint32_t(K - 1) * tok_stride + uint32_t(P)) * uint32_t(sizeof(IO)));
+        const __amdgpu_buffer_rsrc_t dres =
+            buffer_rsrc(dt + size_t(bi) * K * H + h, (uint32_t(K - 1) * uint32_t(H) + 1u) * 4u);
 #pragma unroll
-    for (int k = 0; k < kMaxK; ++k)
-        xr[k] = (k < K && valid) ? to_f32<IO>(x[xy0 + (uint32_t(k) * tok_stride + uint32_t(p))])
-                                 : 0.f;
+        for (int k = 0; k < kMaxK; ++k) {
+            const uint32_t off = valid ? (uint32_t(k) * tok_stride + uint32_t(p)) * uint32_t(sizeof(IO))
+                                       : kBufOutOfRange;
+            if constexpr (std::is_same_v<IO, float>)
+                xr[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xres, int(off), 0, 0));
+            else
+                xr[k] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(xres, int(off), 0, 0));
+            dtr[k] = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(dres, int(uint32_t(k) * uint32_t(H) * 4u), 0, 0));
+        }
+    }
     for (int i = 4 * int(threadIdx.x); i < K * N; i += 4 * 256) {
         const int k = i / N, n = i % N;
         const size_t src = ((size_t(bi) * K + k) * G + g) * N + n;
@@ -124,7 +140,7 @@ __global__ __launch_bounds__(256) void k_verify(
     for (int k = 0; k < kMaxK; ++k) {
         if (k >= K) break;
         const size_t tk = size_t(bi) * K + k;
-        const float d = dt[tk * H + h];
+        const float d = dtr[k];
         const float decay = expf(d * Ah);
         const float xk = xr[k];
         const float u = d * xk;
