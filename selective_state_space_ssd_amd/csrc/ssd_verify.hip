@@ -77,20 +77,30 @@ __global__ __launch_bounds__(256) void k_verify(
     const size_t bh = size_t(bi) * H + h;
     const size_t row = (bh * P + (valid ? p : 0)) * N;
 
-    float4 s[S::J];
-#pragma unroll
-    for (int j = 0; j < S::J; ++j) {
-        const int n = j * 4 * S::LR + lr * 4;
-        if (valid) {   // the state streams through once: non-temporal load and stores
-            const f32x4 t4 =
-                __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(state_in + row + n));
-            s[j] = make_float4(t4.x, t4.y, t4.z, t4.w);
+    // All global loads are issued up front, without branches around them (range-
+    // checked buffer views read 0 past their end), in the order they are needed: B
+    // and C of the K tokens (staged into LDS before the barrier), x and dt, then the
+    // state, so that the staging waits only for B and C.
+    constexpr int kMaxK = 16;
+    // the first 1024 elements of B and C ([K][N]; every K <= 1024 / N), one group of 4
+    // per thread, held raw until the LDS stores
+    using Raw = std::conditional_t<std::is_same_v<IO, float>, f32x4, u32x2>;
+    const int i0 = 4 * int(threadIdx.x);   // element k * N + n of [K][N]
+    Raw bq, cq;
+    {
+        const uint32_t bc_bytes = (uint32_t(K - 1) * uint32_t(G) * N + N) * uint32_t(sizeof(IO));
+        const __amdgpu_buffer_rsrc_t bres = buffer_rsrc(B + (size_t(bi) * K * G + g) * N, bc_bytes);
+        const __amdgpu_buffer_rsrc_t cres = buffer_rsrc(C + (size_t(bi) * K * G + g) * N, bc_bytes);
+        const uint32_t off = i0 < K * N ? (uint32_t(i0 / N) * uint32_t(G) * N + uint32_t(i0 % N)) * uint32_t(sizeof(IO))
+                                        : kBufOutOfRange;
+        if constexpr (std::is_same_v<IO, float>) {
+            bq = __builtin_amdgcn_raw_buffer_load_b128(bres, int(off), 0, 0);
+            cq = __builtin_amdgcn_raw_buffer_load_b128(cres, int(off), 0, 0);
         } else {
-            s[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            bq = __builtin_amdgcn_raw_buffer_load_b64(bres, int(off), 0, 0);
+            cq = __builtin_amdgcn_raw_buffer_load_b64(cres, int(off), 0, 0);
         }
     }
-    // per-token inputs of this row, loaded before the staging barrier
-    constexpr int kMaxK = 16;
     // x and y of this (b, h): token k, row p at [k * H * P + p] from these bases
     const size_t xy0 = (size_t(bi) * K * H + h) * P;
     const uint32_t tok_stride = uint32_t(H) * uint32_t(P);
@@ -115,7 +125,28 @@ __global__ __launch_bounds__(256) void k_verify(
                 __builtin_amdgcn_raw_buffer_load_b32(dres, int(uint32_t(k) * uint32_t(H) * 4u), 0, 0));
         }
     }
-    for (int i = 4 * int(threadIdx.x); i < K * N; i += 4 * 256) {
+    // the state streams through once: non-temporal loads and stores
+    float4 s[S::J];
+    {
+        const __amdgpu_buffer_rsrc_t sres = buffer_rsrc(state_in + bh * P * N, uint32_t(P) * N * 4u);
+#pragma unroll
+        for (int j = 0; j < S::J; ++j) {
+            const int n = j * 4 * S::LR + lr * 4;
+            const uint32_t off = valid ? (uint32_t(p) * N + uint32_t(n)) * 4u : kBufOutOfRange;
+            const f32x4 t4 = __builtin_amdgcn_raw_buffer_load_b128(sres, int(off), 0, kBufNonTemporal);
+            s[j] = make_float4(t4.x, t4.y, t4.z, t4.w);
+        }
+    }
+    if (i0 < K * N) {
+        if constexpr (std::is_same_v<IO, float>) {
+            *reinterpret_cast<float4 *>(sB + i0) = make_float4(bq.x, bq.y, bq.z, bq.w);
+            *reinterpret_cast<float4 *>(sC + i0) = make_float4(cq.x, cq.y, cq.z, cq.w);
+        } else {
+            *reinterpret_cast<float4 *>(sB + i0) = make_float4(bf16_lo(bq.x), bf16_hi(bq.x), bf16_lo(bq.y), bf16_hi(bq.y));
+            *reinterpret_cast<float4 *>(sC + i0) = make_float4(bf16_lo(cq.x), bf16_hi(cq.x), bf16_lo(cq.y), bf16_hi(cq.y));
+        }
+    }
+    for (int i = i0 + 1024; i < K * N; i += 1024) {   // K * N > 1024: the rest
         const int k = i / N, n = i % N;
         const size_t src = ((size_t(bi) * K + k) * G + g) * N + n;
         *reinterpret_cast<float4 *>(sB + i) = load4<IO>(B + src);
