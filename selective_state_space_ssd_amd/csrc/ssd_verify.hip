@@ -56,9 +56,8 @@ __device__ __forceinline__ float4 load4(const IO *p) {
 }
 
 // B and C of the K tokens (group g) are staged once per block into LDS as fp32
-// ([K][N] each); the state loads are issued before the staging so their latency
-// overlaps it.
-template <typename IO, int N>
+// ([K][N] each).  KM >= K bounds the per-token registers (x and dt of every token).
+template <typename IO, int N, int KM>
 __global__ __launch_bounds__(256) void k_verify(
     const float *state_in, const IO *__restrict__ x, const float *__restrict__ dt,
     const float *__restrict__ A, const IO *__restrict__ B, const IO *__restrict__ C,
@@ -81,7 +80,7 @@ __global__ __launch_bounds__(256) void k_verify(
     // checked buffer views read 0 past their end), in the order they are needed: B
     // and C of the K tokens (staged into LDS before the barrier), x and dt, then the
     // state, so that the staging waits only for B and C.
-    constexpr int kMaxK = 16;
+    constexpr int kMaxK = KM;
     // the first 1024 elements of B and C ([K][N]; every K <= 1024 / N), one group of 4
     // per thread, held raw until the LDS stores
     using Raw = std::conditional_t<std::is_same_v<IO, float>, f32x4, u32x2>;
@@ -208,16 +207,24 @@ __global__ __launch_bounds__(256) void k_verify(
     }
 }
 
-template <typename IO, int N>
-static hipError_t launch_verify_n(const VerifyArgs &a, hipStream_t stream) {
+template <typename IO, int N, int KM>
+static hipError_t launch_verify_nk(const VerifyArgs &a, hipStream_t stream) {
     using S = VerifyShape<N>;
     dim3 grid((a.P + S::RB - 1) / S::RB, a.H, a.b);
     const size_t lds = size_t(2) * a.K * N * sizeof(float);
-    hipLaunchKernelGGL((k_verify<IO, N>), grid, dim3(256), lds, stream, a.state_in,
+    hipLaunchKernelGGL((k_verify<IO, N, KM>), grid, dim3(256), lds, stream, a.state_in,
                        static_cast<const IO *>(a.x), a.dt, a.A, static_cast<const IO *>(a.B),
                        static_cast<const IO *>(a.C), a.D, a.accept_len, static_cast<IO *>(a.y),
                        a.state_out, a.states_all, a.err_flag, a.K, a.H, a.P, a.G);
     return hipGetLastError();
+}
+
+// the smallest register bound KM in {4, 8, 16} that holds K tokens
+template <typename IO, int N>
+static hipError_t launch_verify_n(const VerifyArgs &a, hipStream_t stream) {
+    if (a.K <= 4) return launch_verify_nk<IO, N, 4>(a, stream);
+    if (a.K <= 8) return launch_verify_nk<IO, N, 8>(a, stream);
+    return launch_verify_nk<IO, N, 16>(a, stream);
 }
 
 template <typename IO>

@@ -84,8 +84,9 @@ def test_verify_small_shapes(io, N):
 
 
 @pytest.mark.parametrize("io", ["bf16", "f32"])
-@pytest.mark.parametrize("K", [1, 16])
+@pytest.mark.parametrize("K", [1, 7, 16])
 def test_verify_K_extremes(K, io):
+    # the kernel holds per-token values for K <= 4, 8 or 16 tokens (one build each);
     # K = 16 at N = 128: B and C of the K tokens (2048 elements each) exceed what one
     # staging pass of the block covers, so the remainder path runs too
     v = inputs.make_verify_inputs(b=3, K=K, H=2, P=33, N=128, G=1, io=io, seed=K)
