@@ -10,6 +10,10 @@ Contents
     ctypes wrappers around ``ssd_oracle.c``: the plain sequential fp64
     recurrence (the definition of what the chunked scan and the verify step
     compute).  See the header of ``ssd_oracle.c`` for the cited passages.
+``selective_scan_f64``
+    the same recurrence with one channel per head and a diagonal A of N values
+    per channel (the selective scan the SSD layer replaces; the comparison
+    kernel's definition).
 ``forms``
     Two further fp64 NumPy formulations of the same map (the quadratic
     "masked attention" form over the semiseparable matrix, and the four-step
@@ -63,6 +67,8 @@ def load_library(path=None):
     lib.ssd_oracle_verify_f64.argtypes = (
         [dp] * 7 + [ctypes.POINTER(ctypes.c_int32)] + [dp] * 3 + [L] * 6)
     lib.ssd_oracle_verify_f64.restype = ctypes.c_int
+    lib.ssd_oracle_selective_scan_f64.argtypes = [dp] * 9 + [L] * 5
+    lib.ssd_oracle_selective_scan_f64.restype = ctypes.c_int
     return lib
 
 
@@ -127,3 +133,23 @@ def verify_f64(state_in, x, dt, A, B, C, D, accept_len, want_all=True, lib=None)
     if rc != ORACLE_OK:
         raise ValueError(f"ssd_oracle_verify_f64 failed with code {rc}")
     return y, so, sa
+
+
+def selective_scan_f64(x, dt, A, B, C, D, init_state=None, lib=None):
+    """Sequential fp64 selective scan with one channel per head (diagonal A).
+
+    x[b,L,Dch], dt[b,L,Dch], A[Dch,N], B/C[b,L,G,N], D[Dch], init_state[b,Dch,N] or None.
+    Returns (y[b,L,Dch], final_state[b,Dch,N]) as float64.
+    """
+    lib = lib or _load()
+    x, dt, A, B, C, D = map(_f64, (x, dt, A, B, C, D))
+    b, L, Dch = x.shape
+    G, N = B.shape[2], B.shape[3]
+    init = None if init_state is None else _f64(init_state)
+    y = np.empty((b, L, Dch))
+    fs = np.empty((b, Dch, N))
+    rc = lib.ssd_oracle_selective_scan_f64(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                           _ptr(init), _ptr(y), _ptr(fs), b, L, Dch, N, G)
+    if rc != ORACLE_OK:
+        raise ValueError(f"ssd_oracle_selective_scan_f64 failed with code {rc}")
+    return y, fs

@@ -172,3 +172,66 @@ int ssd_oracle_verify_f64(const double *state_in, const double *x, const double 
     free(hist);
     return ORACLE_OK;
 }
+
+/*
+ * Selective scan with one channel per head and a diagonal state matrix (the
+ * "selective SSM" the SSD layer replaces; kept as the comparison kernel):
+ *
+ *   For every (batch b, channel d), with group g = d / (Dch/G), and every state
+ *   index n (each has its own decay A[d][n]):
+ *     s[n] <- init_state[b,d,n]           (zeros when no initial state is given)
+ *     for t = 0 .. L-1:
+ *       s[n] <- exp(dt[b,t,d] * A[d][n]) * s[n] + dt[b,t,d] * x[b,t,d] * B[b,t,g,n]
+ *       y[b,t,d] = sum_n C[b,t,g,n] * s[n] + D[d] * x[b,t,d]
+ *     final_state[b,d] = s
+ *
+ * Sources (page title, section):
+ *  - "另辟蹊径--Mamba介绍", «Selectively Retain Information»: B, C and the step size
+ *    Delta are computed per token (they depend on the input), A is fixed.
+ *  - same page, «The Scan Operation»: each state is the previous state times A
+ *    plus the current input times B, computed with a scan.
+ *  - Bi-Mamba page, «Preliminary: Mamba Series»: SSD restricts A to a scalar times
+ *    the identity and uses a head dimension larger than the Mamba one, which is 1;
+ *    so here every channel is its own head and A is a full diagonal (N values).
+ *  - the discretisation and the output equation are those of ssd_oracle_scan_f64.
+ *
+ * Layouts: x, y [b,L,Dch]; dt [b,L,Dch]; A [Dch,N]; B, C [b,L,G,N]; D [Dch];
+ * init_state, final_state [b,Dch,N] (init_state may be NULL).
+ */
+int ssd_oracle_selective_scan_f64(const double *x, const double *dt, const double *A,
+                                  const double *B, const double *C, const double *D,
+                                  const double *init_state, double *y, double *final_state,
+                                  long b, long L, long Dch, long N, long G)
+{
+    if (b < 0 || L < 0 || Dch <= 0 || N <= 0 || G <= 0)
+        return ORACLE_ERR_DIM;
+    if (Dch % G != 0)
+        return ORACLE_ERR_GROUPS;
+    const long per_group = Dch / G;
+    double *s = (double *)malloc((size_t)N * sizeof(double));
+    if (!s)
+        return ORACLE_ERR_ALLOC;
+    for (long bi = 0; bi < b; ++bi) {
+        for (long d = 0; d < Dch; ++d) {
+            const long g = d / per_group;
+            for (long n = 0; n < N; ++n)
+                s[n] = init_state ? init_state[(bi * Dch + d) * N + n] : 0.0;
+            for (long t = 0; t < L; ++t) {
+                const double xv = x[(bi * L + t) * Dch + d];
+                const double dv = dt[(bi * L + t) * Dch + d];
+                const double *Bt = B + ((bi * L + t) * G + g) * N;
+                const double *Ct = C + ((bi * L + t) * G + g) * N;
+                double acc = 0.0;
+                for (long n = 0; n < N; ++n) {
+                    s[n] = exp(dv * A[d * N + n]) * s[n] + dv * xv * Bt[n];
+                    acc += Ct[n] * s[n];
+                }
+                y[(bi * L + t) * Dch + d] = acc + D[d] * xv;
+            }
+            for (long n = 0; n < N; ++n)
+                final_state[(bi * Dch + d) * N + n] = s[n];
+        }
+    }
+    free(s);
+    return ORACLE_OK;
+}
