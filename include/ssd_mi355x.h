@@ -12,6 +12,9 @@
  *                       back the state at the accepted position ("如何将 Llama 变成
  *                       Mamba？研究人员推出新工作并提高推理速度", «推测解码»).
  *
+ * and, as a comparison kernel on the same data, ssd_selective_scan_fwd: the
+ * selective scan with one channel per head and a diagonal A that SSD replaces.
+ *
  * Both compute, per batch row b and head h (group g = h / (H/G)):
  *
  *   h_t = exp(dt_t * A_h) * h_{t-1} + dt_t * x_t (outer) B_t      state [P x N]
@@ -165,6 +168,39 @@ ssd_status_t ssd_verify_step(const float *state_in, const void *x, const float *
                              const int32_t *accept_len, void *y, float *state_out,
                              float *states_all, int32_t *err_flag, int b, int K, int H, int P,
                              int N, int G, ssd_dtype_t io, void *hip_stream);
+
+/*
+ * ssd_selective_scan_fwd -- selective scan with one channel per head and a diagonal
+ * state matrix (the recurrence SSD replaces), for comparisons on the same data.
+ *
+ * B, C and the step dt depend on the token while A is fixed ("另辟蹊径--Mamba介绍",
+ * «Selectively Retain Information»); the state is carried by a scan («The Scan
+ * Operation»).  Against SSD the head dimension is 1 and A is a full diagonal of N
+ * values per channel instead of one scalar per head (Bi-Mamba page, «Preliminary:
+ * Mamba Series»).  Per (b, channel d), group g = d / (Dch/G), state index n:
+ *
+ *   h[n] <- exp(dt[b,t,d] * A[d][n]) * h[n] + dt[b,t,d] * x[b,t,d] * B[b,t,g,n]
+ *   y[b,t,d] = sum_n C[b,t,g,n] * h[n] + D[d] * x[b,t,d]
+ *
+ * Arguments (all device pointers):
+ *   x           [b, L, Dch]  io
+ *   dt          [b, L, Dch]  fp32   step per token and channel, taken as given
+ *   A           [Dch, N]     fp32   decay rate per channel and state (16-byte aligned)
+ *   B, C        [b, L, G, N] io
+ *   D           [Dch]        fp32
+ *   init_state  [b, Dch, N]  fp32   NULL means zeros (16-byte aligned)
+ *   y           [b, L, Dch]  io     written
+ *   final_state [b, Dch, N]  fp32   NULL, or the state after the last token (written;
+ *                                   with L = 0 it is init_state, or zeros)
+ * Supported: N in {16, 32, 64, 128, 256}; the channels of one group (Dch / G) must be
+ * a multiple of 1024 / N (one workgroup's channels).  Outputs must not overlap
+ * inputs or each other.  Errors as for the other entry points; nothing is enqueued
+ * when a check fails.
+ */
+ssd_status_t ssd_selective_scan_fwd(const void *x, const float *dt, const float *A, const void *B,
+                                    const void *C, const float *D, const float *init_state,
+                                    void *y, float *final_state, int b, int L, int Dch, int N,
+                                    int G, ssd_dtype_t io, void *hip_stream);
 
 /* Static, human-readable name of a status code. */
 const char *ssd_status_string(ssd_status_t status);

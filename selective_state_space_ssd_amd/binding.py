@@ -29,7 +29,8 @@ STATUS_NAMES = {
 
 # Every symbol declared in include/ssd_mi355x.h
 EXPORTED = ("ssd_chunk_scan_workspace_bytes", "ssd_chunk_scan_workspace_init",
-            "ssd_chunk_scan_fwd", "ssd_verify_step", "ssd_status_string", "ssd_version")
+            "ssd_chunk_scan_fwd", "ssd_verify_step", "ssd_selective_scan_fwd",
+            "ssd_status_string", "ssd_version")
 
 _lib = None
 
@@ -58,6 +59,8 @@ def lib() -> ctypes.CDLL:
         L.ssd_chunk_scan_fwd.restype = i32
         L.ssd_verify_step.argtypes = [vp] * 12 + [i32] * 6 + [i32, vp]
         L.ssd_verify_step.restype = i32
+        L.ssd_selective_scan_fwd.argtypes = [vp] * 9 + [i32] * 5 + [i32, vp]
+        L.ssd_selective_scan_fwd.restype = i32
         L.ssd_status_string.argtypes = [i32]
         L.ssd_status_string.restype = ctypes.c_char_p
         L.ssd_version.argtypes = []
@@ -156,6 +159,26 @@ def ssd_verify_step(state_in, x, dt, A, B, C, D, accept_len, y, state_out, state
         raise SSDError(st, "ssd_verify_step")
 
 
+def ssd_selective_scan_fwd(x, dt, A, B, C, D, init_state, y, final_state, stream=None) -> None:
+    """Enqueue the one-channel-per-head selective scan (diagonal A) on ``stream``.
+
+    x[b,L,Dch], B/C[b,L,G,N], y[b,L,Dch] share one dtype (float32 or bfloat16);
+    dt[b,L,Dch], A[Dch,N], D[Dch], init_state/final_state[b,Dch,N] are float32
+    (init_state and final_state may be None).
+    """
+    b, L, Dch = x.shape
+    G, N = B.shape[2], B.shape[3]
+    io = _io_code(x)
+    f32 = torch.float32
+    st = lib().ssd_selective_scan_fwd(
+        _ptr(x, "x", x.dtype), _ptr(dt, "dt", f32), _ptr(A, "A", f32), _ptr(B, "B", x.dtype),
+        _ptr(C, "C", x.dtype), _ptr(D, "D", f32), _ptr(init_state, "init_state", f32),
+        _ptr(y, "y", x.dtype), _ptr(final_state, "final_state", f32), b, L, Dch, N, G, io,
+        _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_selective_scan_fwd")
+
+
 # ------------------------------------------------------------ allocating wrappers
 def chunk_scan_workspace(x, B, Q, stream=None) -> torch.Tensor:
     """Allocate and prepare a workspace for chunk scans of x's and B's shapes."""
@@ -189,6 +212,16 @@ def verify_step(state, x, dt, A, B, C, D, accept_len, return_all_states=False, s
                   if return_all_states else None)
     ssd_verify_step(state, x, dt, A, B, C, D, accept_len, y, state_out, states_all, None, stream)
     return (y, state_out, states_all) if return_all_states else (y, state_out)
+
+
+def selective_scan_fwd(x, dt, A, B, C, D, init_state=None, stream=None):
+    """Allocate y and final_state; returns (y, final_state)."""
+    b, L, Dch = x.shape
+    N = B.shape[3]
+    y = torch.empty_like(x)
+    final_state = torch.empty((b, Dch, N), dtype=torch.float32, device=x.device)
+    ssd_selective_scan_fwd(x, dt, A, B, C, D, init_state, y, final_state, stream)
+    return y, final_state
 
 
 def to_device(arr, device="cuda"):

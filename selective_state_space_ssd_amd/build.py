@@ -20,7 +20,8 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libssd_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["ssd_api.hip", "ssd_verify.hip", "ssd_chunk_scan.hip", "ssd_chunk_fused.hip"]
+SOURCES = ["ssd_api.hip", "ssd_verify.hip", "ssd_chunk_scan.hip", "ssd_chunk_fused.hip",
+           "ssd_selective_scan.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

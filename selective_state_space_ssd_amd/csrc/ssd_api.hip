@@ -175,4 +175,49 @@ ssd_status_t ssd_verify_step(const float *state_in, const void *x, const float *
     return SSD_OK;
 }
 
+ssd_status_t ssd_selective_scan_fwd(const void *x, const float *dt, const float *A, const void *B,
+                                    const void *C, const float *D, const float *init_state,
+                                    void *y, float *final_state, int b, int L, int Dch, int N,
+                                    int G, ssd_dtype_t io, void *hip_stream) {
+    if (io != SSD_DTYPE_F32 && io != SSD_DTYPE_BF16) return SSD_ERR_UNSUPPORTED;
+    if (b < 0 || L < 0 || Dch <= 0 || N <= 0 || G <= 0) return SSD_ERR_BAD_DIM;
+    if (Dch % G != 0) return SSD_ERR_GROUPS;
+    const int dc = ssd::selective_channels_per_block(N);
+    if (dc == 0 || (Dch / G) % dc != 0 || b > 65535) return SSD_ERR_UNSUPPORTED;
+    const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    const size_t state_bytes = size_t(b) * Dch * N * 4;
+    if (b == 0 || L == 0) {   // empty sequence: the final state is the initial one
+        if (final_state && b > 0) {
+            if (!aligned(final_state, 16) || !aligned(init_state, 16)) return SSD_ERR_ALIGN;
+            const Range ri(init_state, state_bytes), rf(final_state, state_bytes);
+            if (ri.overlaps(rf) && !ri.same(rf)) return SSD_ERR_ALIAS;
+            if (ssd::launch_copy_state(init_state, final_state, state_bytes / 4, stream) != hipSuccess)
+                return SSD_ERR_HIP;
+        }
+        return SSD_OK;
+    }
+    if (!x || !dt || !A || !B || !C || !D || !y) return SSD_ERR_NULL_ARG;
+    const bool bf16 = io == SSD_DTYPE_BF16;
+    const size_t esz = bf16 ? 2 : 4;
+    if (!aligned(x, esz) || !aligned(y, esz) || !aligned(B, esz) || !aligned(C, esz) ||
+        !aligned(dt, 4) || !aligned(D, 4) || !aligned(A, 16) || !aligned(init_state, 16) ||
+        !aligned(final_state, 16))
+        return SSD_ERR_ALIGN;
+    const Range rx(x, size_t(b) * L * Dch * esz), ry(y, size_t(b) * L * Dch * esz);
+    const Range rdt(dt, size_t(b) * L * Dch * 4), rA(A, size_t(Dch) * N * 4);
+    const Range rB(B, size_t(b) * L * G * N * esz), rC(C, size_t(b) * L * G * N * esz);
+    const Range rD(D, size_t(Dch) * 4), rinit(init_state, state_bytes), rfin(final_state, state_bytes);
+    const Range inputs[] = {rx, rdt, rA, rB, rC, rD, rinit};
+    for (const Range &in : inputs)
+        if (ry.overlaps(in) || rfin.overlaps(in)) return SSD_ERR_ALIAS;
+    if (ry.overlaps(rfin)) return SSD_ERR_ALIAS;
+    ssd::SelectiveArgs a;
+    a.x = x; a.dt = dt; a.A = A; a.B = B; a.C = C; a.D = D; a.init_state = init_state;
+    a.y = y; a.final_state = final_state;
+    a.b = b; a.L = L; a.Dch = Dch; a.N = N; a.G = G;
+    a.bf16 = bf16;
+    if (ssd::launch_selective_scan(a, stream) != hipSuccess) return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
 }  // extern "C"

@@ -30,6 +30,26 @@ struct VerifyArgs {
 bool verify_supported_n(int N);
 hipError_t launch_verify(const VerifyArgs &a, hipStream_t stream);
 
+// selective scan, one channel per head, diagonal A (ssd_selective_scan.hip)
+struct SelectiveArgs {
+    const void *x;
+    const float *dt;
+    const float *A;
+    const void *B;
+    const void *C;
+    const float *D;
+    const float *init_state;
+    void *y;
+    float *final_state;
+    int b, L, Dch, N, G;
+    bool bf16;
+};
+
+// channels one workgroup covers for this N (0: N not supported); the channels of a
+// group must be a multiple of it
+int selective_channels_per_block(int N);
+hipError_t launch_selective_scan(const SelectiveArgs &a, hipStream_t stream);
+
 struct ChunkScanArgs {
     const void *x;
     const float *dt;

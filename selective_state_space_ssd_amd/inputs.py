@@ -9,6 +9,9 @@ Recipe (the same for tests and for the benchmark):
 * Generator: ``numpy.random.default_rng(seed)`` (PCG64), values drawn in float64.
 * Draw order, chunked scan: A, D, z (for dt), x, B, C, init_state.
   Draw order, verify step: A, D, state, z, x, B, C, accept_len.
+  Draw order, selective scan (one channel per head): A, D, z, x, B, C, init_state;
+  there A is drawn per (channel, state) and dt per (token, channel), with the same
+  distributions as below.
 * A_h = -exp(U(0, ln 16))            scalar per head, in [-16, -1]
 * D_h ~ N(0, 1)
 * dt = clip(softplus(z + DT_BIAS), 1e-3, 1e-1) with z ~ N(0, 1) and
@@ -55,6 +58,13 @@ WORKLOADS = {
                               io="bf16", init=False, seed=32),
     "dstate_sweep_N256": dict(kind="scan", b=8, L=4096, H=32, P=64, N=256, G=4, Q=128,
                               io="bf16", init=False, seed=33),
+    # the selective scan SSD replaces (one channel per head, diagonal A) on the same
+    # layer: 80 x 64 = 5120 channels, at the state size 16 it was used with and at
+    # SSD's 128
+    "mamba1_L2k_N16": dict(kind="selective", b=4, L=2048, Dch=5120, N=16, G=1, io="bf16",
+                           init=False, seed=40),
+    "mamba1_L2k_N128": dict(kind="selective", b=4, L=2048, Dch=5120, N=128, G=1, io="bf16",
+                            init=False, seed=41),
     # speculative-decoding verify on a Llama-3-8B-distilled hybrid layer shape
     "verify_b32_K4": dict(kind="verify", b=32, K=4, H=32, P=128, N=128, G=8, io="bf16",
                           seed=4),
@@ -145,6 +155,23 @@ class VerifyInputs:
         return dict(b=b, K=K, H=H, P=P, N=self.B.shape[3], G=self.B.shape[2])
 
 
+@dataclasses.dataclass
+class SelectiveInputs:
+    x: Tensor
+    dt: Tensor
+    A: Tensor
+    B: Tensor
+    C: Tensor
+    D: Tensor
+    init_state: Optional[Tensor]
+    io: str
+
+    @property
+    def dims(self):
+        b, L, Dch = self.x.shape
+        return dict(b=b, L=L, Dch=Dch, N=self.B.shape[3], G=self.B.shape[2])
+
+
 def _dt(rng, shape):
     z = rng.standard_normal(shape)
     return np.clip(_softplus(z + DT_BIAS), DT_MIN, DT_MAX)
@@ -185,6 +212,23 @@ def make_verify_inputs(b, K, H, P, N, G, io="bf16", seed=0) -> VerifyInputs:
                         D=_store(D, "f32"), accept_len=accept, io=io)
 
 
+def make_selective_inputs(b, L, Dch, N, G=1, io="bf16", init=False, seed=0) -> SelectiveInputs:
+    """Draw one selective-scan problem, one channel per head (see the module docstring)."""
+    if Dch % G:
+        raise ValueError("Dch must be a multiple of G")
+    rng = np.random.default_rng(seed)
+    A = -np.exp(rng.uniform(0.0, math.log(16.0), (Dch, N)))
+    D = rng.standard_normal(Dch)
+    dt = _dt(rng, (b, L, Dch))
+    x = rng.standard_normal((b, L, Dch))
+    B = rng.standard_normal((b, L, G, N))
+    C = rng.standard_normal((b, L, G, N))
+    init_state = _store(0.1 * rng.standard_normal((b, Dch, N)), "f32") if init else None
+    return SelectiveInputs(x=_store(x, io), dt=_store(dt, "f32"), A=_store(A, "f32"),
+                           B=_store(B, io), C=_store(C, io), D=_store(D, "f32"),
+                           init_state=init_state, io=io)
+
+
 def make_workload(name: str, **override):
     """Inputs of a named workload; keyword overrides change shape or seed."""
     cfg = dict(WORKLOADS[name])
@@ -192,4 +236,6 @@ def make_workload(name: str, **override):
     kind = cfg.pop("kind")
     if kind == "scan":
         return make_scan_inputs(**cfg)
+    if kind == "selective":
+        return make_selective_inputs(**cfg)
     return make_verify_inputs(**cfg)
