@@ -16,6 +16,11 @@ Printed: one JSON line with the contract fields plus
   cpu_baseline  the fp64 CPU oracle timed on this host's cores
   L16k          the long-context layer (L=16384, nonzero initial state)
   verify        the K=4 verify step (GB/s of algorithmic bytes)
+  selective_scan_comparison
+                the one-channel-per-head selective scan (diagonal A, the recurrence
+                SSD replaces) on the same layer shape (4 x 2048 tokens, 5120
+                channels) at N=16 and N=128, and how many times faster the SSD
+                chunked scan (N=128) is than each
 """
 import argparse
 import hashlib
@@ -120,6 +125,30 @@ def time_scan(name, steps, warmup, bd, inputs, torch):
     mean_ms, wall = _timed(call, warmup, steps, stream, torch)
     return dict(inp=inp, dims=d, alg_bytes=alg, flops=scan_alg_flops(d), wall_s=wall,
                 ms_per_step=wall * 1e3 / steps, call_ms_mean=mean_ms, nsets=nsets)
+
+
+def time_selective(name, steps, warmup, bd, inputs, torch):
+    """The comparison scan on its workload, inputs rotated like time_scan's."""
+    inp = inputs.make_workload(name)
+    d = inp.dims
+    io_bytes = 2 if inp.io == "bf16" else 4
+    # x, y, dt per (token, channel), B and C per token, A per (channel, state)
+    alg = (d["b"] * d["L"] * d["Dch"] * (2 * io_bytes + 4) + 2 * d["b"] * d["L"] * d["G"] * d["N"] *
+           io_bytes + d["Dch"] * d["N"] * 4 + 8 * d["Dch"])
+    nsets = max(2, math.ceil(3 * MALL_BYTES / alg))
+    sets = _copies(inp, nsets, bd)
+    ys = [torch.empty_like(s["x"]) for s in sets]
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        s = sets[i % nsets]
+        bd.ssd_selective_scan_fwd(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"], s["init_state"],
+                                  ys[i % nsets], None, stream)
+
+    for i in range(warmup):
+        call(i)
+    mean_ms, _ = _timed(call, warmup, steps, stream, torch)
+    return dict(dims=d, alg_bytes=alg, call_ms_mean=mean_ms)
 
 
 def _timed(call, first, steps, stream, torch):
@@ -276,6 +305,16 @@ def main():
         out["verify"] = {"workload": "verify_b32_K4", "GB_per_s": rv["gbs"],
                          "hbm_frac": rv["gbs"] / HBM_PEAK_GBS, "call_ms_mean": rv["call_ms_mean"],
                          "alg_bytes": rv["alg_bytes"]}
+        cmp = {}
+        ssd_tps = d["b"] * d["L"] / (r["call_ms_mean"] * 1e-3)   # both timed by HIP events
+        for n in (16, 128):
+            rs = time_selective(f"mamba1_L2k_N{n}", max(3, args.steps // 10), 1, bd, inputs, torch)
+            ds = rs["dims"]
+            tps = ds["b"] * ds["L"] / (rs["call_ms_mean"] * 1e-3)
+            cmp[f"N{n}"] = {"workload": f"mamba1_L2k_N{n}", "tokens_per_s": tps,
+                            "call_ms_mean": rs["call_ms_mean"],
+                            "ssd_N128_speedup": ssd_tps / tps}
+        out["selective_scan_comparison"] = cmp
     if args.sweep:
         sw = {}
         for n in (16, 64, 128, 256):
