@@ -14,6 +14,10 @@ Contents
     the same recurrence with one channel per head and a diagonal A of N values
     per channel (the selective scan the SSD layer replaces; the comparison
     kernel's definition).
+``backward.scan_bwd_f64``
+    fp64 gradients of the scan (reverse-mode automatic differentiation through a
+    plain torch transcription of the recurrence), pinned by finite differences of
+    ``scan_f64``.
 ``forms``
     Two further fp64 NumPy formulations of the same map (the quadratic
     "masked attention" form over the semiseparable matrix, and the four-step
