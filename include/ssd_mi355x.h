@@ -202,6 +202,53 @@ ssd_status_t ssd_selective_scan_fwd(const void *x, const float *dt, const float 
                                     void *y, float *final_state, int b, int L, int Dch, int N,
                                     int G, ssd_dtype_t io, void *hip_stream);
 
+/*
+ * Workspace size in bytes that ssd_chunk_scan_bwd needs for these dimensions (0 for
+ * an empty problem).  Returns (size_t)-1 when the dimensions are invalid.
+ */
+size_t ssd_chunk_scan_bwd_workspace_bytes(int b, int L, int H, int P, int N, int G,
+                                          ssd_dtype_t io);
+
+/*
+ * ssd_chunk_scan_bwd -- gradients of ssd_chunk_scan_fwd.
+ *
+ * For upstream gradients dy (of y) and d_final (of final_state), the gradients of
+ * sum(dy * y) + sum(d_final * final_state) with respect to every input of the
+ * recurrence at the top of this file.  The intermediate states are not kept by the
+ * forward pass; they are recomputed here ("另辟蹊径--Mamba介绍", «Hardware-aware
+ * Algorithm»: recomputation in the backward pass).  The computation runs the
+ * chunked decomposition of the forward pass (Mamba-2 article, «SSD 算法：分块和形态
+ * 传递») in reverse: the states entering every 64-token chunk, the adjoint state
+ * recurrence from d_final back to d_init, then every in-chunk gradient on the
+ * matrix cores.  Sums over heads (dB, dC), batch and chunks (dA, dD) run in a fixed
+ * order, so the results are deterministic.  Every gradient is accumulated in fp32;
+ * dx, dB and dC are rounded to the I/O type once at the end.
+ *
+ * Arguments (all device pointers; shapes as for ssd_chunk_scan_fwd):
+ *   x, dt, A, B, C, D, init_state   the forward inputs (init_state NULL = zeros)
+ *   dy         [b, L, H, P]  io     gradient of y
+ *   d_final    [b, H, P, N]  fp32   gradient of final_state; NULL = zero
+ *   dx         [b, L, H, P]  io     written
+ *   ddt        [b, L, H]     fp32   written
+ *   dA, dD     [H]           fp32   written (summed over batch and tokens)
+ *   dB, dC     [b, L, G, N]  io     written (summed over the heads of each group)
+ *   d_init     [b, H, P, N]  fp32   gradient of init_state (written); NULL = skip
+ *   workspace, workspace_bytes      at least ssd_chunk_scan_bwd_workspace_bytes(...)
+ *                                   bytes, 16-byte aligned; scratch, no preparation
+ * Supported on this build: P in {32, 64}, N a multiple of 16 with the chunk tiles in
+ * the 160 KiB LDS of one CU (N <= 128 at P = 64), else SSD_ERR_UNSUPPORTED.  b == 0
+ * or L == 0 is a valid empty problem: dA and dD are zero and d_init equals d_final
+ * (or zeros).  Pointers to io arrays, states and the workspace must be 16-byte
+ * aligned, dt, A, D, ddt, dA, dD 4-byte.  Outputs must not overlap inputs, each
+ * other or the workspace.
+ */
+ssd_status_t ssd_chunk_scan_bwd(const void *x, const float *dt, const float *A, const void *B,
+                                const void *C, const float *D, const float *init_state,
+                                const void *dy, const float *d_final, void *dx, float *ddt,
+                                float *dA, void *dB, void *dC, float *dD, float *d_init, int b,
+                                int L, int H, int P, int N, int G, ssd_dtype_t io,
+                                void *workspace, size_t workspace_bytes, void *hip_stream);
+
 /* Static, human-readable name of a status code. */
 const char *ssd_status_string(ssd_status_t status);
 

@@ -30,6 +30,7 @@ STATUS_NAMES = {
 # Every symbol declared in include/ssd_mi355x.h
 EXPORTED = ("ssd_chunk_scan_workspace_bytes", "ssd_chunk_scan_workspace_init",
             "ssd_chunk_scan_fwd", "ssd_verify_step", "ssd_selective_scan_fwd",
+            "ssd_chunk_scan_bwd_workspace_bytes", "ssd_chunk_scan_bwd",
             "ssd_status_string", "ssd_version")
 
 _lib = None
@@ -61,6 +62,10 @@ def lib() -> ctypes.CDLL:
         L.ssd_verify_step.restype = i32
         L.ssd_selective_scan_fwd.argtypes = [vp] * 9 + [i32] * 5 + [i32, vp]
         L.ssd_selective_scan_fwd.restype = i32
+        L.ssd_chunk_scan_bwd_workspace_bytes.argtypes = [i32] * 6 + [i32]
+        L.ssd_chunk_scan_bwd_workspace_bytes.restype = sz
+        L.ssd_chunk_scan_bwd.argtypes = [vp] * 16 + [i32] * 6 + [i32, vp, sz, vp]
+        L.ssd_chunk_scan_bwd.restype = i32
         L.ssd_status_string.argtypes = [i32]
         L.ssd_status_string.restype = ctypes.c_char_p
         L.ssd_version.argtypes = []
@@ -179,6 +184,39 @@ def ssd_selective_scan_fwd(x, dt, A, B, C, D, init_state, y, final_state, stream
         raise SSDError(st, "ssd_selective_scan_fwd")
 
 
+def ssd_chunk_scan_bwd_workspace_bytes(b, L, H, P, N, G, io: int) -> int:
+    n = lib().ssd_chunk_scan_bwd_workspace_bytes(b, L, H, P, N, G, io)
+    if n == ctypes.c_size_t(-1).value:
+        raise SSDError(2, "ssd_chunk_scan_bwd_workspace_bytes")
+    return n
+
+
+def ssd_chunk_scan_bwd(x, dt, A, B, C, D, init_state, dy, d_final, dx, ddt, dA, dB, dC, dD,
+                       d_init, workspace, stream=None) -> None:
+    """Enqueue the gradients of the chunked scan on ``stream``.
+
+    Inputs as for ssd_chunk_scan_fwd plus dy (like x) and d_final[b,H,P,N] float32
+    (may be None); outputs dx (like x), ddt[b,L,H], dA[H], dD[H] float32, dB/dC (like
+    B), d_init[b,H,P,N] float32 (may be None); workspace is a uint8 tensor of at least
+    ssd_chunk_scan_bwd_workspace_bytes(...) bytes.
+    """
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    io = _io_code(x)
+    f32 = torch.float32
+    st = lib().ssd_chunk_scan_bwd(
+        _ptr(x, "x", x.dtype), _ptr(dt, "dt", f32), _ptr(A, "A", f32), _ptr(B, "B", x.dtype),
+        _ptr(C, "C", x.dtype), _ptr(D, "D", f32), _ptr(init_state, "init_state", f32),
+        _ptr(dy, "dy", x.dtype), _ptr(d_final, "d_final", f32), _ptr(dx, "dx", x.dtype),
+        _ptr(ddt, "ddt", f32), _ptr(dA, "dA", f32), _ptr(dB, "dB", x.dtype),
+        _ptr(dC, "dC", x.dtype), _ptr(dD, "dD", f32), _ptr(d_init, "d_init", f32),
+        b, L, H, P, N, G, io, _ptr(workspace, "workspace"),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_chunk_scan_bwd")
+
+
 # ------------------------------------------------------------ allocating wrappers
 def chunk_scan_workspace(x, B, Q, stream=None) -> torch.Tensor:
     """Allocate and prepare a workspace for chunk scans of x's and B's shapes."""
@@ -200,6 +238,27 @@ def chunk_scan_fwd(x, dt, A, B, C, D, Q, init_state=None, workspace=None, stream
         workspace = chunk_scan_workspace(x, B, Q)
     ssd_chunk_scan_fwd(x, dt, A, B, C, D, init_state, y, final_state, Q, workspace, stream)
     return y, final_state
+
+
+def chunk_scan_bwd(x, dt, A, B, C, D, dy, init_state=None, d_final=None, workspace=None,
+                   stream=None):
+    """Allocate the gradients (and the workspace if not given); returns
+    (dx, ddt, dA, dB, dC, dD, d_init)."""
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev = x.device
+    f32 = torch.float32
+    dx, dB, dC = torch.empty_like(x), torch.empty_like(B), torch.empty_like(C)
+    ddt = torch.empty((b, L, H), dtype=f32, device=dev)
+    dA = torch.empty((H,), dtype=f32, device=dev)
+    dD = torch.empty((H,), dtype=f32, device=dev)
+    d_init = torch.empty((b, H, P, N), dtype=f32, device=dev)
+    if workspace is None:
+        n = ssd_chunk_scan_bwd_workspace_bytes(b, L, H, P, N, G, _io_code(x))
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+    ssd_chunk_scan_bwd(x, dt, A, B, C, D, init_state, dy, d_final, dx, ddt, dA, dB, dC, dD,
+                       d_init, workspace, stream)
+    return dx, ddt, dA, dB, dC, dD, d_init
 
 
 def verify_step(state, x, dt, A, B, C, D, accept_len, return_all_states=False, stream=None):

@@ -220,4 +220,81 @@ ssd_status_t ssd_selective_scan_fwd(const void *x, const float *dt, const float 
     return SSD_OK;
 }
 
+size_t ssd_chunk_scan_bwd_workspace_bytes(int b, int L, int H, int P, int N, int G,
+                                          ssd_dtype_t io) {
+    if (b < 0 || L < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0) return size_t(-1);
+    if (io != SSD_DTYPE_F32 && io != SSD_DTYPE_BF16) return size_t(-1);
+    if (b == 0 || L == 0) return 0;
+    return ssd::plan_chunk_scan_bwd(b, L, H, P, N, G).total;
+}
+
+ssd_status_t ssd_chunk_scan_bwd(const void *x, const float *dt, const float *A, const void *B,
+                                const void *C, const float *D, const float *init_state,
+                                const void *dy, const float *d_final, void *dx, float *ddt,
+                                float *dA, void *dB, void *dC, float *dD, float *d_init, int b,
+                                int L, int H, int P, int N, int G, ssd_dtype_t io,
+                                void *workspace, size_t workspace_bytes, void *hip_stream) {
+    if (io != SSD_DTYPE_F32 && io != SSD_DTYPE_BF16) return SSD_ERR_UNSUPPORTED;
+    if (b < 0 || L < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0) return SSD_ERR_BAD_DIM;
+    if (H % G != 0) return SSD_ERR_GROUPS;
+    if (!dA || !dD) return SSD_ERR_NULL_ARG;
+    if (!aligned(dA, 4) || !aligned(dD, 4)) return SSD_ERR_ALIGN;
+    const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    const size_t state_bytes = size_t(b) * H * P * N * 4;
+    const Range rdA(dA, size_t(H) * 4), rdD(dD, size_t(H) * 4);
+    if (rdA.overlaps(rdD)) return SSD_ERR_ALIAS;
+
+    if (b == 0 || L == 0) {   // empty sequence: d_init = d_final, no parameter gradient
+        const Range rdf(d_final, state_bytes), rdi(d_init, state_bytes);
+        if (!aligned(d_final, 16) || !aligned(d_init, 16)) return SSD_ERR_ALIGN;
+        if (rdi.overlaps(rdf) && !rdi.same(rdf)) return SSD_ERR_ALIAS;
+        if (rdi.overlaps(rdA) || rdi.overlaps(rdD)) return SSD_ERR_ALIAS;
+        if (ssd::launch_copy_state(nullptr, dA, size_t(H), stream) != hipSuccess ||
+            ssd::launch_copy_state(nullptr, dD, size_t(H), stream) != hipSuccess)
+            return SSD_ERR_HIP;
+        if (d_init && b > 0 &&
+            ssd::launch_copy_state(d_final, d_init, state_bytes / 4, stream) != hipSuccess)
+            return SSD_ERR_HIP;
+        return SSD_OK;
+    }
+    if (!x || !dt || !A || !B || !C || !D || !dy || !dx || !ddt || !dB || !dC)
+        return SSD_ERR_NULL_ARG;
+    const ssd::ChunkScanBwdPlan plan = ssd::plan_chunk_scan_bwd(b, L, H, P, N, G);
+    if (!plan.supported) return SSD_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(dy, 16) ||
+        !aligned(dx, 16) || !aligned(dB, 16) || !aligned(dC, 16) || !aligned(init_state, 16) ||
+        !aligned(d_final, 16) || !aligned(d_init, 16) || !aligned(workspace, 16) ||
+        !aligned(dt, 4) || !aligned(A, 4) || !aligned(D, 4) || !aligned(ddt, 4))
+        return SSD_ERR_ALIGN;
+    if (!workspace || workspace_bytes < plan.total) return SSD_ERR_WORKSPACE;
+
+    const bool bf16 = io == SSD_DTYPE_BF16;
+    const size_t esz = bf16 ? 2 : 4;
+    const size_t xb = size_t(b) * L * H * P * esz, bcb = size_t(b) * L * G * N * esz;
+    const Range inputs[] = {Range(x, xb), Range(dt, size_t(b) * L * H * 4), Range(A, size_t(H) * 4),
+                            Range(B, bcb), Range(C, bcb), Range(D, size_t(H) * 4),
+                            Range(init_state, state_bytes), Range(dy, xb),
+                            Range(d_final, state_bytes)};
+    const Range outputs[] = {Range(dx, xb), Range(ddt, size_t(b) * L * H * 4), rdA, Range(dB, bcb),
+                             Range(dC, bcb), rdD, Range(d_init, state_bytes),
+                             Range(workspace, plan.total)};
+    const int n_out = sizeof(outputs) / sizeof(outputs[0]);
+    for (int i = 0; i < n_out; ++i) {
+        for (const Range &in : inputs)
+            if (outputs[i].overlaps(in)) return SSD_ERR_ALIAS;
+        for (int j = i + 1; j < n_out; ++j)
+            if (outputs[i].overlaps(outputs[j])) return SSD_ERR_ALIAS;
+    }
+
+    ssd::ChunkScanBwdArgs a;
+    a.x = x; a.dt = dt; a.A = A; a.B = B; a.C = C; a.D = D; a.init_state = init_state;
+    a.dy = dy; a.d_final = d_final;
+    a.dx = dx; a.ddt = ddt; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD; a.d_init = d_init;
+    a.b = b; a.L = L; a.H = H; a.P = P; a.N = N; a.G = G;
+    a.bf16 = bf16;
+    a.workspace = workspace;
+    if (ssd::launch_chunk_scan_bwd(a, plan, stream) != hipSuccess) return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
 }  // extern "C"

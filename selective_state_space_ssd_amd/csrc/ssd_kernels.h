@@ -103,6 +103,48 @@ FusedPlan plan_fused(int b, int L, int H, int P, int N, int G, int Q, bool bf16)
 hipError_t launch_fused(const ChunkScanArgs &a, const FusedPlan &plan, hipStream_t stream);
 hipError_t launch_chunk_scan(const ChunkScanArgs &a, const ChunkScanPlan &plan,
                              hipStream_t stream);
+// gradients of the chunked scan (ssd_chunk_bwd.hip)
+struct ChunkScanBwdArgs {
+    const void *x;
+    const float *dt;
+    const float *A;
+    const void *B;
+    const void *C;
+    const float *D;
+    const float *init_state;    // may be null (zero initial state)
+    const void *dy;
+    const float *d_final;       // may be null (no final-state gradient)
+    void *dx;
+    float *ddt;
+    float *dA;
+    void *dB;
+    void *dC;
+    float *dD;
+    float *d_init;              // may be null (not wanted)
+    int b, L, H, P, N, G;
+    bool bf16;
+    void *workspace;
+};
+
+struct ChunkScanBwdPlan {
+    int nc = 0;                 // 64-token chunks
+    size_t off_hin = 0;         // fp32 [b, H, nc, P, N]: chunk states, then Hin
+    size_t off_gh = 0;          // fp32 [b, H, nc, P, N]: adjoint sources, then Gh
+    size_t off_alpha = 0;       // fp32 [b, H, nc]
+    size_t off_dbp = 0;         // fp32 [b, L, H, N]: per-head dB
+    size_t off_dcp = 0;         // fp32 [b, L, H, N]: per-head dC
+    size_t off_dap = 0;         // fp32 [b, H, nc]
+    size_t off_ddp = 0;         // fp32 [b, H, nc]
+    size_t total = 0;
+    size_t lds_states = 0;
+    size_t lds_chunk = 0;
+    bool supported = false;
+};
+
+ChunkScanBwdPlan plan_chunk_scan_bwd(int b, int L, int H, int P, int N, int G);
+hipError_t launch_chunk_scan_bwd(const ChunkScanBwdArgs &a, const ChunkScanBwdPlan &plan,
+                                 hipStream_t stream);
+
 // final_state = init_state (or zeros) for an empty sequence.
 hipError_t launch_copy_state(const float *init_state, float *final_state, size_t count,
                              hipStream_t stream);

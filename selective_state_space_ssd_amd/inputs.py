@@ -20,6 +20,8 @@ Recipe (the same for tests and for the benchmark):
 * x, B, C ~ N(0, 1)
 * init_state / state ~ N(0, 0.1^2)   (standard deviation 0.1)
 * accept_len ~ U{0, ..., K}
+* Upstream gradients of the chunked scan (its backward pass), from a generator of
+  their own seed: dy ~ N(0, 1) stored like x, then d_final ~ N(0, 1) in float32.
 * Storage: dt, A, D and every state in float32.  x, B, C are float32 for the
   fp32 workload and bfloat16 (float64 -> float32 -> bfloat16, both roundings to
   nearest-even) for the bf16 workloads.
@@ -227,6 +229,17 @@ def make_selective_inputs(b, L, Dch, N, G=1, io="bf16", init=False, seed=0) -> S
     return SelectiveInputs(x=_store(x, io), dt=_store(dt, "f32"), A=_store(A, "f32"),
                            B=_store(B, io), C=_store(C, io), D=_store(D, "f32"),
                            init_state=init_state, io=io)
+
+
+def make_upstream_grads(inp: ScanInputs, seed: int, final: bool = True):
+    """Upstream gradients (dy, d_final) for the backward pass of a chunked-scan problem:
+    dy like x, d_final like the state (None unless ``final``)."""
+    d = inp.dims
+    rng = np.random.default_rng(seed)
+    dy = _store(rng.standard_normal((d["b"], d["L"], d["H"], d["P"])), inp.io)
+    d_final = (_store(rng.standard_normal((d["b"], d["H"], d["P"], d["N"])), "f32")
+               if final else None)
+    return dy, d_final
 
 
 def make_workload(name: str, **override):

@@ -172,3 +172,67 @@ def test_verify_alignment_and_alias(lib):
 def test_verify_empty_batch_is_ok(lib):
     assert verify_call(lib, {k: None for k in ("state_in", "x", "y", "state_out")},
                        dims=dict(b=0)) == OK
+
+
+def bwd_call(lib, over=None, dims=None, io=1, ws_bytes=1 << 40):
+    p = dict(x=addr(1), dt=addr(2), A=addr(3), B=addr(4), C=addr(5), D=addr(6), init=None,
+             dy=addr(7), dfin=None, dx=addr(8), ddt=addr(9), dA=addr(10), dB=addr(11),
+             dC=addr(12), dD=addr(13), dinit=addr(14), ws=addr(15))
+    p.update(over or {})
+    d = dict(b=1, L=256, H=4, P=64, N=32, G=1)
+    d.update(dims or {})
+    return lib.ssd_chunk_scan_bwd(p["x"], p["dt"], p["A"], p["B"], p["C"], p["D"], p["init"],
+                                  p["dy"], p["dfin"], p["dx"], p["ddt"], p["dA"], p["dB"],
+                                  p["dC"], p["dD"], p["dinit"], d["b"], d["L"], d["H"], d["P"],
+                                  d["N"], d["G"], io, p["ws"], ws_bytes, None)
+
+
+def test_bwd_workspace_bytes(lib):
+    b, L, H, P, N, G = 4, 2048, 80, 64, 128, 1
+    n = bd.ssd_chunk_scan_bwd_workspace_bytes(b, L, H, P, N, G, bd.SSD_DTYPE_BF16)
+    units = b * H * (L // 64)
+    # entering states and state gradients (fp32), per-head dB / dC partials (fp32),
+    # three per-chunk scalars
+    need = 2 * units * P * N * 4 + 2 * b * L * H * N * 4 + 3 * units * 4
+    assert need <= n < need + 7 * 256
+    assert bd.ssd_chunk_scan_bwd_workspace_bytes(0, L, H, P, N, G, 1) == 0
+    assert bd.ssd_chunk_scan_bwd_workspace_bytes(b, 0, H, P, N, G, 1) == 0
+    with pytest.raises(bd.SSDError):
+        bd.ssd_chunk_scan_bwd_workspace_bytes(b, L, H, -1, N, G, 1)
+
+
+@pytest.mark.parametrize("name", ["x", "dt", "A", "B", "C", "D", "dy", "dx", "ddt", "dA",
+                                  "dB", "dC", "dD"])
+def test_bwd_null_required_pointer(lib, name):
+    assert bwd_call(lib, {name: None}) == NULL
+
+
+@pytest.mark.parametrize("dims,code", [
+    (dict(b=-1), DIM), (dict(L=-1), DIM), (dict(H=0), DIM), (dict(P=0), DIM), (dict(N=0), DIM),
+    (dict(G=0), DIM), (dict(G=3), GROUPS), (dict(P=16), UNSUP), (dict(P=128), UNSUP),
+    (dict(N=24), UNSUP), (dict(N=256), UNSUP),
+])
+def test_bwd_bad_dims(lib, dims, code):
+    assert bwd_call(lib, dims=dims) == code
+
+
+def test_bwd_bad_dtype(lib):
+    assert bwd_call(lib, io=3) == UNSUP
+
+
+@pytest.mark.parametrize("name,idx,mis", [("x", 1, 8), ("dy", 7, 2), ("dx", 8, 8), ("dB", 11, 4),
+                                          ("ddt", 9, 2), ("dA", 10, 1), ("dinit", 14, 8),
+                                          ("ws", 15, 8), ("dfin", 16, 4)])
+def test_bwd_misaligned(lib, name, idx, mis):
+    assert bwd_call(lib, {name: addr(idx, mis)}) == ALIGN
+
+
+def test_bwd_workspace_and_alias_checks(lib):
+    need = bd.ssd_chunk_scan_bwd_workspace_bytes(1, 256, 4, 64, 32, 1, 1)
+    assert bwd_call(lib, ws_bytes=need - 1) == WS
+    assert bwd_call(lib, {"ws": None}) == WS
+    assert bwd_call(lib, {"dx": addr(7)}) == ALIAS                  # dx on dy
+    assert bwd_call(lib, {"dB": addr(12)}) == ALIAS                 # dB on dC
+    assert bwd_call(lib, {"ws": addr(1)}) == ALIAS                  # workspace on x
+    assert bwd_call(lib, {"dinit": addr(16), "dfin": addr(16)}) == ALIAS
+    assert bwd_call(lib, {"dD": addr(10)}) == ALIAS                 # dD on dA

@@ -1,0 +1,143 @@
+"""GPU parity of ssd_chunk_scan_bwd (gradients of the chunked scan) against the fp64
+gradient oracle (MI355X only)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import TOL, slice_err, to_f64
+from oracle import backward
+from selective_state_space_ssd_amd import binding as bd
+from selective_state_space_ssd_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dx", "ddt", "dA", "dB", "dC", "dD", "d_init")
+
+
+def _run(inp, dy, d_final):
+    dev = lambda a: bd.to_device(a)
+    x, dt, A, B, C, D = (dev(getattr(inp, n)) for n in ("x", "dt", "A", "B", "C", "D"))
+    grads = bd.chunk_scan_bwd(x, dt, A, B, C, D, dev(dy), init_state=dev(inp.init_state),
+                              d_final=dev(d_final))
+    torch.cuda.synchronize()
+    return [to_f64(g) for g in grads]
+
+
+def _oracle(inp, dy, d_final, rows=slice(None), heads=slice(None)):
+    """Oracle gradients for a block of batch rows and heads (one group only when heads
+    is not the full range)."""
+    f = lambda t: None if t is None else t.f64()
+    x, dt, A, B, C, D = (f(getattr(inp, n)) for n in ("x", "dt", "A", "B", "C", "D"))
+    h0 = f(inp.init_state)
+    dfin = f(d_final)
+    return backward.scan_bwd_f64(
+        x[rows][:, :, heads], dt[rows][:, :, heads], A[heads], B[rows], C[rows], D[heads],
+        None if h0 is None else h0[rows][:, heads], dy.f64()[rows][:, :, heads],
+        None if dfin is None else dfin[rows][:, heads])
+
+
+# slice axes of every gradient: per (batch, head) for dx, ddt, d_init; per (batch,
+# group) for dB, dC; the whole vector for dA, dD
+AXES = {"dx": (1, 3), "ddt": (1,), "dA": (0,), "dB": (1, 3), "dC": (1, 3), "dD": (0,),
+        "d_init": (2, 3)}
+
+
+def _errors(got, ref, names=NAMES):
+    return {n: slice_err(got[NAMES.index(n)], ref[NAMES.index(n)], AXES[n]) for n in names}
+
+
+def _assert(errs, tol):
+    print("  " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()) + f"  (tol {tol})", flush=True)
+    for n, e in errs.items():
+        assert np.isfinite(e) and e <= tol, f"{n}: {e:.3e} > {tol}"
+
+
+# Several 64-token chunks with ragged last ones, initial states, final-state gradients
+# or none, P in {32, 64}, N from 16 to 128, groups of 1, 2 and 4 heads, both dtypes.
+SMALL = [
+    # b,  L,  H,  P,   N, G,  io,    init, final
+    (2, 300, 4, 64, 128, 2, "bf16", True, True),
+    (1, 200, 4, 32, 16, 1, "bf16", False, False),
+    (2, 130, 2, 32, 64, 1, "f32", True, True),
+    (1, 64, 2, 64, 32, 2, "f32", False, True),        # exactly one chunk
+    (1, 63, 4, 64, 48, 4, "f32", True, False),        # one group per head, short
+    (1, 1, 2, 32, 16, 1, "f32", True, True),          # one token
+    (2, 517, 4, 64, 128, 1, "f32", True, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "b{}L{}H{}P{}N{}G{}{}{}{}".format(
+    *c[:7], "init" if c[7] else "", "dfin" if c[8] else ""))
+def test_backward_small_full_oracle(case):
+    b, L, H, P, N, G, io, init, final = case
+    inp = inputs.make_scan_inputs(b, L, H, P, N, G, 64, io=io, init=init, seed=L + N + P)
+    dy, d_final = inputs.make_upstream_grads(inp, seed=1000 + L, final=final)
+    got = _run(inp, dy, d_final)
+    _assert(_errors(got, _oracle(inp, dy, d_final)), TOL[io])
+
+
+def test_backward_is_deterministic():
+    inp = inputs.make_scan_inputs(2, 300, 8, 64, 64, 2, 64, io="bf16", init=True, seed=5)
+    dy, d_final = inputs.make_upstream_grads(inp, seed=6)
+    a, b = _run(inp, dy, d_final), _run(inp, dy, d_final)
+    for n, u, v in zip(NAMES, a, b):
+        assert np.array_equal(u, v), n
+
+
+def test_backward_empty_sequence():
+    inp = inputs.make_scan_inputs(2, 0, 4, 64, 32, 1, 64, io="f32", init=True, seed=8)
+    dy, d_final = inputs.make_upstream_grads(inp, seed=9)
+    dx, ddt, dA, dB, dC, dD, d_init = _run(inp, dy, d_final)
+    assert dx.size == 0 and ddt.size == 0 and dB.size == 0 and dC.size == 0
+    assert not np.any(dA) and not np.any(dD)
+    assert np.array_equal(d_init, d_final.f64())
+
+
+def test_backward_unsupported_head_dim_is_rejected():
+    inp = inputs.make_scan_inputs(1, 64, 2, 16, 16, 1, 64, io="f32", seed=10)
+    dy, _ = inputs.make_upstream_grads(inp, seed=11, final=False)
+    with pytest.raises(bd.SSDError) as e:
+        _run(inp, dy, None)
+    assert e.value.status == 4   # SSD_ERR_UNSUPPORTED
+
+
+@pytest.fixture(scope="module")
+def full_size():
+    """The Mamba-2-2.7B-shaped layer at L = 2048 (b=4, H=80, P=64, N=128, bf16) with
+    upstream gradients for y and the final state, run once on the GPU."""
+    inp = inputs.make_workload("mamba2_2p7b_L2k")
+    dy, d_final = inputs.make_upstream_grads(inp, seed=77)
+    return inp, dy, d_final, _run(inp, dy, d_final)
+
+
+def test_backward_full_size_batch_row(full_size):
+    """Batch row 0 of the full-size layer, every head: dx, ddt, d_init per head and dB,
+    dC (the sum over all 80 heads), from the oracle run on blocks of 8 heads."""
+    inp, dy, d_final, got = full_size
+    H = inp.dims["H"]
+    ref = None
+    for h0 in range(0, H, 8):
+        part = _oracle(inp, dy, d_final, rows=slice(0, 1), heads=slice(h0, h0 + 8))
+        if ref is None:
+            ref = [np.zeros((1,) + g.shape[1:]) if n in ("dx", "ddt", "d_init") else
+                   np.zeros_like(part[i]) for i, (n, g) in enumerate(zip(NAMES, got))]
+        ref[0][:, :, h0:h0 + 8] = part[0]
+        ref[1][:, :, h0:h0 + 8] = part[1]
+        ref[3] += part[3]
+        ref[4] += part[4]
+        ref[6][:, h0:h0 + 8] = part[6]
+    row0 = [g[:1] if n in ("dx", "ddt", "dB", "dC", "d_init") else g for n, g in zip(NAMES, got)]
+    _assert(_errors(row0, ref, ("dx", "ddt", "dB", "dC", "d_init")), TOL["bf16"])
+
+
+def test_backward_full_size_head_parameters(full_size):
+    """dA and dD of the full-size layer for a sample of heads (sums over all batch rows
+    and tokens)."""
+    inp, dy, d_final, got = full_size
+    for h in (0, 41, 79):
+        ref = _oracle(inp, dy, d_final, heads=slice(h, h + 1))
+        for n in ("dA", "dD"):
+            i = NAMES.index(n)
+            err = abs(got[i][h] - ref[i][0]) / max(abs(ref[i][0]), 1e-30)
+            print(f"  head {h} {n} rel err {err:.2e}", flush=True)
+            assert err <= TOL["bf16"]
