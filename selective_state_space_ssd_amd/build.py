@@ -21,7 +21,8 @@ LIB_NAME = "libssd_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 SOURCES = ["ssd_api.hip", "ssd_verify.hip", "ssd_chunk_scan.hip", "ssd_chunk_fused.hip",
-           "ssd_selective_scan.hip", "ssd_chunk_bwd.hip"]
+           "ssd_selective_scan.hip", "ssd_chunk_bwd.hip",
+           "ssd_chunk_bwd_bf16.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -225,7 +225,7 @@ size_t ssd_chunk_scan_bwd_workspace_bytes(int b, int L, int H, int P, int N, int
     if (b < 0 || L < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0) return size_t(-1);
     if (io != SSD_DTYPE_F32 && io != SSD_DTYPE_BF16) return size_t(-1);
     if (b == 0 || L == 0) return 0;
-    return ssd::plan_chunk_scan_bwd(b, L, H, P, N, G).total;
+    return ssd::plan_chunk_scan_bwd(b, L, H, P, N, G, io == SSD_DTYPE_BF16).total;
 }
 
 ssd_status_t ssd_chunk_scan_bwd(const void *x, const float *dt, const float *A, const void *B,
@@ -259,7 +259,7 @@ ssd_status_t ssd_chunk_scan_bwd(const void *x, const float *dt, const float *A, 
     }
     if (!x || !dt || !A || !B || !C || !D || !dy || !dx || !ddt || !dB || !dC)
         return SSD_ERR_NULL_ARG;
-    const ssd::ChunkScanBwdPlan plan = ssd::plan_chunk_scan_bwd(b, L, H, P, N, G);
+    const ssd::ChunkScanBwdPlan plan = ssd::plan_chunk_scan_bwd(b, L, H, P, N, G, io == SSD_DTYPE_BF16);
     if (!plan.supported) return SSD_ERR_UNSUPPORTED;
     if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(dy, 16) ||
         !aligned(dx, 16) || !aligned(dB, 16) || !aligned(dC, 16) || !aligned(init_state, 16) ||

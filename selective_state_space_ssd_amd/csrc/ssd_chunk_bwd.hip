@@ -41,22 +41,10 @@ namespace {
 constexpr int QB = 64;     // tokens per backward chunk
 constexpr int kPad = 4;    // fp32 LDS row padding (floats)
 
-// Sum over the 16 lanes of a DPP row; every lane of the row ends with the total.
-__device__ __forceinline__ float row16_sum(float v) {
-    constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kQuadSwap1, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kQuadSwap2, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kRowHalfMirror, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kRowMirror, 0xF, 0xF, false));
-    return v;
-}
-
 // Sum of one value per thread over the 256-thread block, in a fixed order; every
 // thread returns the total.  `red` is LDS scratch of 4 floats.  Starts with a barrier.
 __device__ __forceinline__ float block_sum(float v, float *red) {
-    v = row16_sum(v);
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
+    v = wave_sum(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
@@ -362,20 +350,21 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chunk(
 }
 
 // ------------------------------------------------------------ step 4
-// dB[row, g, n] = sum over the heads of group g of dBp[row, h, n]; dC alike.
+// dB[row, g, n] = sum over the nparts / G parts of group g of dBp[row, part, n] (parts
+// are heads, or blocks of heads); dC alike.
 template <typename IO>
 __global__ __launch_bounds__(kThreads) void k_bwd_reduce_bc(
     const float *__restrict__ dBp, const float *__restrict__ dCp, IO *__restrict__ dB,
-    IO *__restrict__ dC, size_t rows, int H, int G, int N) {
+    IO *__restrict__ dC, size_t rows, int nparts, int G, int N) {
     const size_t i = size_t(blockIdx.x) * kThreads + threadIdx.x;
     if (i >= rows * G * N) return;
     const int n = int(i % N);
     const int g = int((i / N) % G);
     const size_t row = i / (size_t(G) * N);
-    const int hpg = H / G;
+    const int ppg = nparts / G;
     float sb = 0.f, sc = 0.f;
-    for (int k = 0; k < hpg; ++k) {
-        const size_t src = (row * H + g * hpg + k) * N + n;
+    for (int k = 0; k < ppg; ++k) {
+        const size_t src = (row * nparts + g * ppg + k) * N + n;
         sb += dBp[src];
         sc += dCp[src];
     }
@@ -439,15 +428,7 @@ hipError_t launch_bwd_p(const ChunkScanBwdArgs &a, const ChunkScanBwdPlan &pl, h
                        dDp, a.L, a.H, a.N, a.G, pl.nc);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    const size_t rows = size_t(a.b) * a.L;
-    const size_t cnt = rows * a.G * a.N;
-    hipLaunchKernelGGL((k_bwd_reduce_bc<IO>), dim3(unsigned((cnt + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, stream, dBp, dCp, static_cast<IO *>(a.dB),
-                       static_cast<IO *>(a.dC), rows, a.H, a.G, a.N);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_bwd_reduce_h, dim3(a.H), dim3(kThreads), 0, stream, dAp, dDp, a.dA, a.dD,
-                       a.b, a.H, pl.nc);
-    return hipGetLastError();
+    return launch_bwd_reduce(a, pl, stream);
 }
 
 template <typename IO>
@@ -463,11 +444,33 @@ size_t align256b(size_t v) { return (v + 255) / 256 * 256; }
 
 }  // namespace
 
-ChunkScanBwdPlan plan_chunk_scan_bwd(int b, int L, int H, int P, int N, int G) {
+ChunkScanBwdPlan plan_chunk_scan_bwd(int b, int L, int H, int P, int N, int G, bool bf16) {
     ChunkScanBwdPlan pl;
-    if (b <= 0 || L <= 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0) return pl;
+    if (b <= 0 || L <= 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G) return pl;
     pl.nc = (L + QB - 1) / QB;
     const size_t units = size_t(b) * H * pl.nc;
+    pl.bf16_path = bf16 && P == 64 && chunk_bwd_bf16_lds(N) != 0;
+    if (pl.bf16_path) {
+        // heads per workgroup: the largest divisor of the group size up to 8
+        const int hpg = H / G;
+        for (int d = 1; d <= 8 && d <= hpg; ++d)
+            if (hpg % d == 0) pl.hb = d;
+        pl.nparts = H / pl.hb;
+        const size_t st = units * size_t(P) * N * 2;
+        const size_t part = size_t(b) * L * pl.nparts * N * 4;
+        pl.off_hin = 0;
+        pl.off_gh = align256b(st);
+        pl.off_ghn = pl.off_gh + align256b(st);
+        pl.off_dbp = pl.off_ghn + align256b(st);
+        pl.off_dcp = pl.off_dbp + align256b(part);
+        pl.off_dap = pl.off_dcp + align256b(part);
+        pl.off_ddp = pl.off_dap + align256b(units * 4);
+        pl.total = pl.off_ddp + align256b(units * 4);
+        pl.lds_chunk = chunk_bwd_bf16_lds(N);
+        pl.supported = H <= 65535 && b <= 65535 && pl.lds_chunk <= kMaxLds;
+        return pl;
+    }
+    pl.nparts = H;
     const size_t st = units * size_t(P) * N * 4;
     const size_t part = size_t(b) * L * H * N * 4;
     pl.off_hin = 0;
@@ -480,14 +483,43 @@ ChunkScanBwdPlan plan_chunk_scan_bwd(int b, int L, int H, int P, int N, int G) {
     pl.total = pl.off_ddp + align256b(units * 4);
     pl.lds_states = states_lds_bytes(P, N);
     pl.lds_chunk = chunk_lds_bytes(P, N);
-    pl.supported = (P == 32 || P == 64) && N % 16 == 0 && N >= 16 && H % G == 0 &&
-                   H <= 65535 && b <= 65535 && pl.lds_chunk <= kMaxLds &&
-                   pl.lds_states <= kMaxLds;
+    pl.supported = (P == 32 || P == 64) && N % 16 == 0 && N >= 16 && H <= 65535 &&
+                   b <= 65535 && pl.lds_chunk <= kMaxLds && pl.lds_states <= kMaxLds;
     return pl;
+}
+
+hipError_t launch_bwd_reduce(const ChunkScanBwdArgs &a, const ChunkScanBwdPlan &pl,
+                             hipStream_t stream) {
+    char *ws = static_cast<char *>(a.workspace);
+    const float *dBp = reinterpret_cast<const float *>(ws + pl.off_dbp);
+    const float *dCp = reinterpret_cast<const float *>(ws + pl.off_dcp);
+    const float *dAp = reinterpret_cast<const float *>(ws + pl.off_dap);
+    const float *dDp = reinterpret_cast<const float *>(ws + pl.off_ddp);
+    const size_t rows = size_t(a.b) * a.L;
+    const size_t cnt = rows * a.G * a.N;
+    const dim3 grid(unsigned((cnt + kThreads - 1) / kThreads));
+    if (a.bf16)
+        hipLaunchKernelGGL((k_bwd_reduce_bc<bf16_bits>), grid, dim3(kThreads), 0, stream, dBp, dCp,
+                           static_cast<bf16_bits *>(a.dB), static_cast<bf16_bits *>(a.dC), rows,
+                           pl.nparts, a.G, a.N);
+    else
+        hipLaunchKernelGGL((k_bwd_reduce_bc<float>), grid, dim3(kThreads), 0, stream, dBp, dCp,
+                           static_cast<float *>(a.dB), static_cast<float *>(a.dC), rows,
+                           pl.nparts, a.G, a.N);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_bwd_reduce_h, dim3(a.H), dim3(kThreads), 0, stream, dAp, dDp, a.dA, a.dD,
+                       a.b, a.H, pl.nc);
+    return hipGetLastError();
 }
 
 hipError_t launch_chunk_scan_bwd(const ChunkScanBwdArgs &a, const ChunkScanBwdPlan &pl,
                                  hipStream_t stream) {
+    if (pl.bf16_path) {
+        const hipError_t e = launch_chunk_scan_bwd_bf16(a, pl, stream);
+        if (e != hipSuccess) return e;
+        return launch_bwd_reduce(a, pl, stream);
+    }
     if (a.bf16) return launch_bwd_io<bf16_bits>(a, pl, stream);
     return launch_bwd_io<float>(a, pl, stream);
 }

@@ -115,6 +115,31 @@ __device__ __forceinline__ void transpose4x8_b16(const uint4 (&in)[4], uint2 (&o
     }
 }
 
+// Sum over the 16 lanes of a DPP row; every lane of the row ends with the total.
+__device__ __forceinline__ float row16_sum(float v) {
+    constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kQuadSwap1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kQuadSwap2, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kRowHalfMirror, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kRowMirror, 0xF, 0xF, false));
+    return v;
+}
+
+// Sum over the 64 lanes of a wave; every lane ends with the total.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row16_sum(v);
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// Sum over the 4 lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48) of a wave.
+__device__ __forceinline__ float group4_sum(float v) {
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves (no LDS
 // traffic): a Hillis-Steele scan inside each row of 16 lanes (shift right by 1, 2,
 // 4, 8; lanes shifted in from outside the row add 0), then the total of row 0 is

@@ -126,13 +126,20 @@ struct ChunkScanBwdArgs {
     void *workspace;
 };
 
+// Two implementations: the bf16 matrix-core path (bf16 I/O, P = 64, N in {64, 128};
+// states in bf16, dB / dC partials per block of heads) and the fp32 path (everything
+// else; fp32 states, partials per head).
 struct ChunkScanBwdPlan {
     int nc = 0;                 // 64-token chunks
-    size_t off_hin = 0;         // fp32 [b, H, nc, P, N]: chunk states, then Hin
-    size_t off_gh = 0;          // fp32 [b, H, nc, P, N]: adjoint sources, then Gh
-    size_t off_alpha = 0;       // fp32 [b, H, nc]
-    size_t off_dbp = 0;         // fp32 [b, L, H, N]: per-head dB
-    size_t off_dcp = 0;         // fp32 [b, L, H, N]: per-head dC
+    bool bf16_path = false;
+    int hb = 1;                 // heads per workgroup (bf16 path)
+    int nparts = 0;             // dB / dC partials per token: H (fp32 path) or H / hb
+    size_t off_hin = 0;         // fp32 [b,H,nc,P,N] chunk states then Hin | bf16 Hin^T
+    size_t off_gh = 0;          // fp32 [b,H,nc,P,N] adjoint sources then Gh | bf16 Gh^T
+    size_t off_ghn = 0;         // bf16 path: bf16 Gh [b,H,nc,P,N]
+    size_t off_alpha = 0;       // fp32 path: fp32 [b,H,nc]
+    size_t off_dbp = 0;         // fp32 [b, L, nparts, N]
+    size_t off_dcp = 0;         // fp32 [b, L, nparts, N]
     size_t off_dap = 0;         // fp32 [b, H, nc]
     size_t off_ddp = 0;         // fp32 [b, H, nc]
     size_t total = 0;
@@ -141,9 +148,16 @@ struct ChunkScanBwdPlan {
     bool supported = false;
 };
 
-ChunkScanBwdPlan plan_chunk_scan_bwd(int b, int L, int H, int P, int N, int G);
+ChunkScanBwdPlan plan_chunk_scan_bwd(int b, int L, int H, int P, int N, int G, bool bf16);
 hipError_t launch_chunk_scan_bwd(const ChunkScanBwdArgs &a, const ChunkScanBwdPlan &plan,
                                  hipStream_t stream);
+// bf16 path (ssd_chunk_bwd_bf16.hip): LDS bytes of its chunk kernel (0: N unsupported)
+size_t chunk_bwd_bf16_lds(int N);
+hipError_t launch_chunk_scan_bwd_bf16(const ChunkScanBwdArgs &a, const ChunkScanBwdPlan &plan,
+                                      hipStream_t stream);
+// dB, dC = sums of the fp32 partials over the parts of each group
+hipError_t launch_bwd_reduce(const ChunkScanBwdArgs &a, const ChunkScanBwdPlan &plan,
+                             hipStream_t stream);
 
 // final_state = init_state (or zeros) for an empty sequence.
 hipError_t launch_copy_state(const float *init_state, float *final_state, size_t count,

@@ -189,12 +189,16 @@ def bwd_call(lib, over=None, dims=None, io=1, ws_bytes=1 << 40):
 
 def test_bwd_workspace_bytes(lib):
     b, L, H, P, N, G = 4, 2048, 80, 64, 128, 1
-    n = bd.ssd_chunk_scan_bwd_workspace_bytes(b, L, H, P, N, G, bd.SSD_DTYPE_BF16)
     units = b * H * (L // 64)
-    # entering states and state gradients (fp32), per-head dB / dC partials (fp32),
-    # three per-chunk scalars
-    need = 2 * units * P * N * 4 + 2 * b * L * H * N * 4 + 3 * units * 4
+    # bf16 I/O, P = 64: bf16 entering states and state gradients (two layouts), fp32
+    # dB / dC partials per block of 8 heads, two per-chunk scalars
+    n = bd.ssd_chunk_scan_bwd_workspace_bytes(b, L, H, P, N, G, bd.SSD_DTYPE_BF16)
+    need = 3 * units * P * N * 2 + 2 * b * L * (H // 8) * N * 4 + 2 * units * 4
     assert need <= n < need + 7 * 256
+    # fp32 I/O: fp32 states and state gradients, per-head partials, three scalars
+    n32 = bd.ssd_chunk_scan_bwd_workspace_bytes(b, L, H, P, N, G, bd.SSD_DTYPE_F32)
+    need32 = 2 * units * P * N * 4 + 2 * b * L * H * N * 4 + 3 * units * 4
+    assert need32 <= n32 < need32 + 7 * 256
     assert bd.ssd_chunk_scan_bwd_workspace_bytes(0, L, H, P, N, G, 1) == 0
     assert bd.ssd_chunk_scan_bwd_workspace_bytes(b, 0, H, P, N, G, 1) == 0
     with pytest.raises(bd.SSDError):

@@ -53,7 +53,9 @@ def _assert(errs, tol):
 
 
 # Several 64-token chunks with ragged last ones, initial states, final-state gradients
-# or none, P in {32, 64}, N from 16 to 128, groups of 1, 2 and 4 heads, both dtypes.
+# or none, P in {32, 64}, N from 16 to 128, groups of 1, 2, 4 and 12 heads, both
+# dtypes; bf16 with P = 64 and N in {64, 128} takes the bf16 matrix-core path (blocks
+# of up to 8 heads of a group per workgroup), the rest the fp32 path.
 SMALL = [
     # b,  L,  H,  P,   N, G,  io,    init, final
     (2, 300, 4, 64, 128, 2, "bf16", True, True),
@@ -63,6 +65,8 @@ SMALL = [
     (1, 63, 4, 64, 48, 4, "f32", True, False),        # one group per head, short
     (1, 1, 2, 32, 16, 1, "f32", True, True),          # one token
     (2, 517, 4, 64, 128, 1, "f32", True, True),
+    (1, 190, 12, 64, 64, 1, "bf16", True, True),      # blocks of 6 heads
+    (2, 129, 2, 64, 128, 2, "bf16", False, False),    # one head per group
 ]
 
 
