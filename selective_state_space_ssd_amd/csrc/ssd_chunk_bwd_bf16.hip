@@ -6,7 +6,8 @@
 // reverse; intermediate states recomputed rather than stored, "另辟蹊径--Mamba介绍",
 // «Hardware-aware Algorithm»), organised for fewer HBM bytes:
 //
-//   k_bwd_chain    one workgroup per (direction, head, batch) walks the 64-token chunks
+//   k_bwd_chain_fwd / k_bwd_chain_rev
+//                  one workgroup per (head, batch) walks the 64-token chunks
 //                  in order (forward) or in reverse, keeping the P x N state in MFMA
 //                  accumulators: the forward walk writes the state entering each chunk,
 //                  Hin_c; the reverse walk writes the gradient of the state leaving it,
@@ -15,8 +16,8 @@
 //                  one bf16 MFMA product added onto the decayed state, so no per-chunk
 //                  state ever goes to HBM in fp32.  The states are stored in bf16, in
 //                  the layouts the next kernel reads as MFMA operands.
-//   k_bwd_chunk_bf one workgroup per (chunk, block of up to 8 heads of one group,
-//                  batch): C B^T once per block, then per head the score tiles, dx,
+//   k_bwd_chunk_bf one workgroup of 8 waves per (chunk, block of up to 8 heads of one
+//                  group, batch): C B^T once per block, then per head the score tiles, dx,
 //                  and the head's dB / dC contributions, which stay in registers across
 //                  the block so only one fp32 partial per block reaches HBM.
 //
@@ -42,108 +43,107 @@ __device__ __forceinline__ bf16x8 lds16(const bf16_bits *p) {
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0, 0, 0, 0); }
 
 // ------------------------------------------------------------ state chains
-// dir 0: Hin_c for c = 0 .. nc-1 (HinT, [n][p] per chunk).
-// dir 1: Gh_c for c = nc-1 .. 0 (GhT [n][p] and Gh [p][n]), then d_init.
-// The state is held twice in the reverse walk, as tiles with rows p (written as GhT)
-// and with rows n (written as Gh), so every store writes 4 consecutive values.
-template <int N>
-__global__ __launch_bounds__(kThreads) void k_bwd_chain(
-    const bf16_bits *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
-    const bf16_bits *__restrict__ B, const bf16_bits *__restrict__ C,
-    const bf16_bits *__restrict__ dy, const float *__restrict__ init_state,
-    const float *__restrict__ d_final, bf16_bits *__restrict__ hinT, bf16_bits *__restrict__ ghT,
-    bf16_bits *__restrict__ ghN, float *__restrict__ d_init, int L, int H, int G, int nc) {
+__device__ __forceinline__ uint4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0));
+}
+
+// Inputs of one chunk step, loaded two steps ahead: the token pair (2 tpu, 2 tpu + 1)
+// of u (x or dy) at p group pgu, two token-pair items of v (B or C), and dt.
+struct ChainPf {
+    uint4 ua, ub, va[2], vb[2];
+    float d;
+};
+
+// DIR 0: Hin_c for c = 0 .. nc-1 (Hin^T, [n][p] per chunk).
+// DIR 1: Gh_c for c = nc-1 .. 0 (Gh^T [n][p] and Gh [p][n]), then d_init.
+// The reverse walk holds its state twice, as tiles with rows p (stored as Gh^T) and
+// with rows n (stored as Gh), so every store writes 4 consecutive values.  Loads go
+// through buffer resources sized to the chunk's valid tokens: tokens past the end of
+// the sequence read as zero without a branch.
+template <int N, int DIR>
+__device__ __forceinline__ void chain_walk(
+    const bf16_bits *__restrict__ u, const float *__restrict__ dt, float Ah,
+    const bf16_bits *__restrict__ v, const float *__restrict__ s0,
+    bf16_bits *__restrict__ dstT, bf16_bits *__restrict__ ghN, float *__restrict__ d_init,
+    int bi, int h, int L, int H, int G, int nc, bf16_bits *AT, bf16_bits *VT, float *wts) {
     constexpr int NT = N / 16, NTW = NT / 4, NG = N / 8, PN = HP * N;
-    const int dir = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
+    constexpr int kVItems = (32 * NG + kThreads - 1) / kThreads;
     const int g = h / (H / G);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
     const size_t bh = size_t(bi) * H + h;
-    const float Ah = A[h];
+    const int tpu = tid >> 3, pgu = tid & 7;
 
-    __shared__ __align__(16) bf16_bits AT[HP * RS];    // [p][t] weighted x or dy
-    __shared__ __align__(16) bf16_bits VT[N * RS];     // [n][t] B or C
-    __shared__ float wts[QB];
-    __shared__ float al_sh;
-
-    const bf16_bits *u = dir == 0 ? x : dy;
-    const bf16_bits *v = dir == 0 ? B : C;
-
-    // state tiles: rows p (tile nt: p = 16w + 4g4 + i, n = 16nt + r16)
     f32x4 accP[NT];
-    // reverse walk only: rows n (tile j, pt: n = 16(NTW w + j) + 4g4 + i, p = 16pt + r16)
-    f32x4 accN[NTW][4];
-    {
-        const float *s0 = dir == 0 ? init_state : d_final;
+    f32x4 accN[DIR ? NTW : 1][4];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                accP[nt][i] = s0 ? s0[bh * PN + (16 * w + 4 * g4 + i) * N + 16 * nt + r16] : 0.f;
+        for (int i = 0; i < 4; ++i)
+            accP[nt][i] = s0 ? s0[bh * PN + (16 * w + 4 * g4 + i) * N + 16 * nt + r16] : 0.f;
+    if constexpr (DIR == 1) {
 #pragma unroll
         for (int j = 0; j < NTW; ++j)
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) {
                 float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (dir == 1 && d_final)
+                if (s0)
                     q = *reinterpret_cast<const float4 *>(
-                        d_final + bh * PN + (16 * pt + r16) * N + 16 * (NTW * w + j) + 4 * g4);
+                        s0 + bh * PN + (16 * pt + r16) * N + 16 * (NTW * w + j) + 4 * g4);
                 accN[j][pt] = {q.x, q.y, q.z, q.w};
             }
     }
 
-    // prefetch registers: u rows (token pair tpu, p group pgu), v rows (2 items)
-    const int tpu = tid >> 3, pgu = tid & 7;
-    uint4 ua, ub, va[2], vb[2];
-    float dreg = 0.f;
-    auto load = [&](int c) {
-        const int t0 = c * QB, qlen = min(QB, L - t0);
-        const int ta = 2 * tpu, tb = ta + 1;
-        ua = ta < qlen ? *reinterpret_cast<const uint4 *>(u + ((size_t(bi) * L + t0 + ta) * H + h) * HP + 8 * pgu) : zero4();
-        ub = tb < qlen ? *reinterpret_cast<const uint4 *>(u + ((size_t(bi) * L + t0 + tb) * H + h) * HP + 8 * pgu) : zero4();
+    auto chunk_of = [&](int step) { return DIR == 0 ? step : nc - 1 - step; };
+    auto load = [&](ChainPf &f, int step) {
+        const int c = chunk_of(step);
+        const bool live = step < nc;
+        const int t0 = live ? c * QB : 0;
+        const int qlen = live ? min(QB, L - t0) : 0;
+        const size_t tok0 = size_t(bi) * L + t0;
+        const auto ur = buffer_rsrc(u + tok0 * H * HP, uint32_t(qlen) * uint32_t(H * HP) * 2u);
+        const auto vr = buffer_rsrc(v + tok0 * G * N, uint32_t(qlen) * uint32_t(G * N) * 2u);
+        const auto dr = buffer_rsrc(dt + tok0 * H, uint32_t(qlen) * uint32_t(H) * 4u);
+        const uint32_t uo = (uint32_t(2 * tpu) * H + h) * HP + 8 * pgu;
+        f.ua = ld128(ur, uo * 2u);
+        f.ub = ld128(ur, (uo + H * HP) * 2u);
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int item = tid + k * kThreads;
+        for (int k = 0; k < kVItems; ++k) {
+            const int item = min(tid + k * kThreads, 32 * NG - 1);
             const int tp = item / NG, ng = item % NG;
-            const int t = 2 * tp;
-            va[k] = (item < 32 * NG && t < qlen)
-                        ? *reinterpret_cast<const uint4 *>(v + ((size_t(bi) * L + t0 + t) * G + g) * N + 8 * ng)
-                        : zero4();
-            vb[k] = (item < 32 * NG && t + 1 < qlen)
-                        ? *reinterpret_cast<const uint4 *>(v + ((size_t(bi) * L + t0 + t + 1) * G + g) * N + 8 * ng)
-                        : zero4();
+            const uint32_t vo = (uint32_t(2 * tp) * G + g) * N + 8 * ng;
+            f.va[k] = ld128(vr, vo * 2u);
+            f.vb[k] = ld128(vr, (vo + G * N) * 2u);
         }
-        dreg = lane < qlen ? dt[(size_t(bi) * L + t0 + lane) * H + h] : 0.f;
+        f.d = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(dr, int((lane * H + h) * 4), 0, 0));
     };
 
-    load(dir == 0 ? 0 : nc - 1);
-    for (int step = 0; step < nc; ++step) {
-        const int c = dir == 0 ? step : nc - 1 - step;
+    auto step_fn = [&](ChainPf &f, int step) {
+        const int c = chunk_of(step);
         const int qlen = min(QB, L - c * QB);
-        if (w == 0) {
-            const float cs = wave_inclusive_scan(lane < qlen ? dreg * Ah * kLog2e : 0.f);
-            const float aend = __shfl(cs, qlen - 1, 64);
-            wts[lane] = lane < qlen ? (dir == 0 ? exp2f(aend - cs) * dreg : exp2f(cs)) : 0.f;
-            if (lane == 0) al_sh = exp2f(aend);
-        }
+        // every wave scans the chunk's decays (no branch, so the compiler can keep
+        // counting the loads in flight); the waves write identical weights
+        const float cs = wave_inclusive_scan(f.d * Ah * kLog2e);
+        const float aend = __shfl(cs, qlen - 1, 64);
+        const float al = exp2f(aend);
+        wts[lane] = lane < qlen ? (DIR == 0 ? exp2f(aend - cs) * f.d : exp2f(cs)) : 0.f;
         __syncthreads();
-        const float al = al_sh;
-        {   // stage the weighted u transposed and v transposed, token pairs
+        {   // stage the weighted u and v transposed, token pairs
             const float wa = wts[2 * tpu], wb = wts[2 * tpu + 1];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const uint32_t ea = (&ua.x)[j >> 1], eb = (&ub.x)[j >> 1];
+                const uint32_t ea = (&f.ua.x)[j >> 1], eb = (&f.ub.x)[j >> 1];
                 const float fa = (j & 1) ? bf16_hi(ea) : bf16_lo(ea);
                 const float fb = (j & 1) ? bf16_hi(eb) : bf16_lo(eb);
                 *reinterpret_cast<uint32_t *>(AT + (8 * pgu + j) * RS + 2 * tpu) = pack_bf16x2(fa * wa, fb * wb);
             }
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
+            for (int k = 0; k < kVItems; ++k) {
                 const int item = tid + k * kThreads;
                 if (item < 32 * NG) {
                     const int tp = item / NG, ng = item % NG;
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        const uint32_t ea = (&va[k].x)[j >> 1], eb = (&vb[k].x)[j >> 1];
+                        const uint32_t ea = (&f.va[k].x)[j >> 1], eb = (&f.vb[k].x)[j >> 1];
                         const uint32_t lo = (j & 1) ? (ea >> 16) : (ea & 0xffffu);
                         const uint32_t hi = (j & 1) ? (eb & 0xffff0000u) : (eb << 16);
                         *reinterpret_cast<uint32_t *>(VT + (8 * ng + j) * RS + 2 * tp) = lo | hi;
@@ -151,17 +151,16 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chain(
                 }
             }
         }
-        if (step + 1 < nc) load(dir == 0 ? c + 1 : c - 1);
+        load(f, step + 2);
         __syncthreads();
 
         // store the state (entering chunk c forward, leaving chunk c in reverse)
         const size_t so = (bh * nc + c) * size_t(PN);
-        bf16_bits *dstT = dir == 0 ? hinT : ghT;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
             *reinterpret_cast<uint2 *>(dstT + so + (16 * nt + r16) * HP + 16 * w + 4 * g4) =
                 make_uint2(pack_bf16x2(accP[nt][0], accP[nt][1]), pack_bf16x2(accP[nt][2], accP[nt][3]));
-        if (dir == 1) {
+        if constexpr (DIR == 1) {
 #pragma unroll
             for (int j = 0; j < NTW; ++j)
 #pragma unroll
@@ -172,15 +171,15 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chain(
         }
 
         // state <- al * state + (this chunk's contribution)
-        bf16x8 a0 = lds16(AT + (16 * w + r16) * RS + 8 * g4);
-        bf16x8 a1 = lds16(AT + (16 * w + r16) * RS + 32 + 8 * g4);
+        const bf16x8 a0 = lds16(AT + (16 * w + r16) * RS + 8 * g4);
+        const bf16x8 a1 = lds16(AT + (16 * w + r16) * RS + 32 + 8 * g4);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             f32x4 s = accP[nt] * al;
             s = mfma_bf16(a0, lds16(VT + (16 * nt + r16) * RS + 8 * g4), s);
             accP[nt] = mfma_bf16(a1, lds16(VT + (16 * nt + r16) * RS + 32 + 8 * g4), s);
         }
-        if (dir == 1) {
+        if constexpr (DIR == 1) {
 #pragma unroll
             for (int j = 0; j < NTW; ++j) {
                 const int nt = NTW * w + j;
@@ -194,22 +193,71 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chain(
                 }
             }
         }
+    };
+
+    ChainPf f0, f1;
+    load(f0, 0);
+    load(f1, 1);
+    int step = 0;
+    for (; step + 1 < nc; step += 2) {
+        step_fn(f0, step);
+        step_fn(f1, step + 1);
     }
-    if (dir == 1 && d_init) {
+    if (step < nc) step_fn(f0, step);
+    if constexpr (DIR == 1) {
+        if (d_init) {
 #pragma unroll
-        for (int j = 0; j < NTW; ++j)
+            for (int j = 0; j < NTW; ++j)
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt)
-                *reinterpret_cast<float4 *>(d_init + bh * PN + (16 * pt + r16) * N + 16 * (NTW * w + j) + 4 * g4) =
-                    make_float4(accN[j][pt][0], accN[j][pt][1], accN[j][pt][2], accN[j][pt][3]);
+                for (int pt = 0; pt < 4; ++pt)
+                    *reinterpret_cast<float4 *>(d_init + bh * PN + (16 * pt + r16) * N + 16 * (NTW * w + j) + 4 * g4) =
+                        make_float4(accN[j][pt][0], accN[j][pt][1], accN[j][pt][2], accN[j][pt][3]);
+        }
     }
 }
 
+// The two walks are separate kernels so that each gets the registers it needs (the
+// reverse walk holds two copies of the state).
+template <int N>
+__global__ __launch_bounds__(kThreads) void k_bwd_chain_fwd(
+    const bf16_bits *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
+    const bf16_bits *__restrict__ B, const float *__restrict__ init_state,
+    bf16_bits *__restrict__ hinT, int L, int H, int G, int nc) {
+    __shared__ __align__(16) bf16_bits AT[HP * RS];    // [p][t] weighted x
+    __shared__ __align__(16) bf16_bits VT[N * RS];     // [n][t] B
+    __shared__ float wts[QB];
+    const int h = blockIdx.x, bi = blockIdx.y;
+    chain_walk<N, 0>(x, dt, A[h], B, init_state, hinT, nullptr, nullptr, bi, h, L, H, G, nc, AT,
+                     VT, wts);
+}
+
+template <int N>
+__global__ __launch_bounds__(kThreads, 2) void k_bwd_chain_rev(
+    const bf16_bits *__restrict__ dy, const float *__restrict__ dt, const float *__restrict__ A,
+    const bf16_bits *__restrict__ C, const float *__restrict__ d_final,
+    bf16_bits *__restrict__ ghT, bf16_bits *__restrict__ ghN, float *__restrict__ d_init, int L,
+    int H, int G, int nc) {
+    __shared__ __align__(16) bf16_bits AT[HP * RS];    // [p][t] weighted dy
+    __shared__ __align__(16) bf16_bits VT[N * RS];     // [n][t] C
+    __shared__ float wts[QB];
+    const int h = blockIdx.x, bi = blockIdx.y;
+    chain_walk<N, 1>(dy, dt, A[h], C, d_final, ghT, ghN, d_init, bi, h, L, H, G, nc, AT, VT, wts);
+}
+
 // ------------------------------------------------------------ in-chunk gradients
+// 8 waves (two per SIMD: the 143 KiB of LDS allow one workgroup per CU).  Tile
+// ownership, with hw = w / 4 and q = w % 4:
+//   scores W, M, dS       rows t of block q, s tiles 2 hw, 2 hw + 1
+//   dx^T, U^T             rows p of block q, s tiles 2 hw, 2 hw + 1
+//   V^T, dC^T, X2^T, dB^T rows n of tile w % NT, t (or s) tiles TW (w / NT) .. + TW - 1
+constexpr int kChunkThreads = 512;
+
 template <int N>
 struct ChunkLds {
+    static constexpr int NT = N / 16;
     static constexpr int NS = N + 16;                      // row stride of [t][n]
-    static constexpr int kScalars = 4 * QB + QB + 4 * 4 * QB + 8;
+    // acum, dts, wsv, eac, rowR parts [2], colR [4], colGLW [4], vsp [4], yocp [NT], red
+    static constexpr int kScalars = (4 + 2 + 4 + 4 + 4 + NT) * QB + 16;
     static constexpr size_t off_Bn = size_t(kScalars) * 4;
     static constexpr size_t off_Cn = off_Bn + size_t(QB) * NS * 2;
     static constexpr size_t off_BT = off_Cn + size_t(QB) * NS * 2;
@@ -224,7 +272,7 @@ struct ChunkLds {
 };
 
 template <int N>
-__global__ __launch_bounds__(kThreads) void k_bwd_chunk_bf(
+__global__ __launch_bounds__(kChunkThreads) void k_bwd_chunk_bf(
     const bf16_bits *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
     const bf16_bits *__restrict__ B, const bf16_bits *__restrict__ C, const float *__restrict__ D,
     const bf16_bits *__restrict__ dy, const bf16_bits *__restrict__ hinT,
@@ -233,25 +281,28 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chunk_bf(
     float *__restrict__ dCp, float *__restrict__ dAp, float *__restrict__ dDp, int L, int H,
     int G, int nc, int HB) {
     using Lay = ChunkLds<N>;
-    constexpr int NS = Lay::NS, NT = N / 16, NTW = NT / 4, KN = N / 32, NG = N / 8, PN = HP * N;
+    constexpr int NS = Lay::NS, NT = N / 16, KN = N / 32, NG = N / 8, PN = HP * N;
+    constexpr int TW = NT / 2;                 // t (s) tiles per wave in the n phases
     const int c = blockIdx.x, hbk = blockIdx.y, bi = blockIdx.z;
     const int nblk = gridDim.y;
     const int h0 = hbk * HB;
     const int g = h0 / (H / G);
     const int t0 = c * QB, qlen = min(QB, L - t0);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
+    const int q = w & 3, hw = w >> 2;          // row block and column half (scores, dx)
+    const int ntw = w % NT, tb0 = (w / NT) * TW;   // n tile and first t tile (n phases)
 
     extern __shared__ __align__(16) unsigned char smem[];
     float *acum = reinterpret_cast<float *>(smem);   // [QB]
     float *dts = acum + QB;                          // [QB]
     float *wsv = dts + QB;                           // [QB] e^{cum_end - cum_s} dt_s
     float *eac = wsv + QB;                           // [QB] e^{cum_t}
-    float *rowR = eac + QB;                          // [QB]
-    float *colR = rowR + QB;                         // [4][QB]
-    float *colGLW = colR + 4 * QB;                   // [4][QB]
-    float *vsp = colGLW + 4 * QB;                    // [4][QB] per-wave parts of v_s
-    float *yocp = vsp + 4 * QB;                      // [4][QB] per-wave parts of C_t . V_t
-    float *red = yocp + 4 * QB;                      // [8]
+    float *rowR = eac + QB;                          // [2][QB] parts of sum_s R[t][s]
+    float *colR = rowR + 2 * QB;                     // [4][QB] parts of sum_t R[t][s]
+    float *colGLW = colR + 4 * QB;                   // [4][QB] parts of sum_t (G Lm W)[t][s]
+    float *vsp = colGLW + 4 * QB;                    // [4][QB] parts of v_s
+    float *yocp = vsp + 4 * QB;                      // [NT][QB] parts of C_t . V_t
+    float *red = yocp + NT * QB;                     // [16]
     bf16_bits *Bn = reinterpret_cast<bf16_bits *>(smem + Lay::off_Bn);     // [s][n]
     bf16_bits *Cn = reinterpret_cast<bf16_bits *>(smem + Lay::off_Cn);     // [t][n]
     bf16_bits *BT = reinterpret_cast<bf16_bits *>(smem + Lay::off_BT);     // [n][s]
@@ -263,121 +314,119 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chunk_bf(
     bf16_bits *DS = reinterpret_cast<bf16_bits *>(smem + Lay::off_DS);     // [t][s]
     bf16_bits *DST = reinterpret_cast<bf16_bits *>(smem + Lay::off_DST);   // [s][t]
 
-    // x / dy of one head: token pair tpu, p group pgu
-    const int tpu = tid >> 3, pgu = tid & 7;
-    uint4 xa, xb, ya, yb;
-    auto load_xy = [&](int h) {
+    // one head's x (threads 0-255) or dy (threads 256-511): token pair tpu, p group pgu
+    const bool is_dy = tid >= kThreads;
+    const int tpu = (tid & 255) >> 3, pgu = tid & 7;
+    const bf16_bits *src_xy = is_dy ? dy : x;
+    uint4 ra, rb;
+    float dnext;
+    auto load_head = [&](int h) {
         const int ta = 2 * tpu, tb = ta + 1;
-        const size_t ra = ((size_t(bi) * L + t0 + ta) * H + h) * HP + 8 * pgu;
-        const size_t rb = ra + size_t(H) * HP;
-        xa = ta < qlen ? *reinterpret_cast<const uint4 *>(x + ra) : zero4();
-        xb = tb < qlen ? *reinterpret_cast<const uint4 *>(x + rb) : zero4();
-        ya = ta < qlen ? *reinterpret_cast<const uint4 *>(dy + ra) : zero4();
-        yb = tb < qlen ? *reinterpret_cast<const uint4 *>(dy + rb) : zero4();
+        const size_t o = ((size_t(bi) * L + t0 + ta) * H + h) * HP + 8 * pgu;
+        ra = ta < qlen ? *reinterpret_cast<const uint4 *>(src_xy + o) : zero4();
+        rb = tb < qlen ? *reinterpret_cast<const uint4 *>(src_xy + o + size_t(H) * HP) : zero4();
+        dnext = lane < qlen ? dt[(size_t(bi) * L + t0 + lane) * H + h] : 0.f;
     };
-    load_xy(h0);
+    load_head(h0);
 
-    // B and C of the group, natural and transposed
+    // B and C of the group, natural and transposed (one token-pair item of each)
+    for (int item = tid; item < 32 * NG; item += kChunkThreads) {
+        const int tp = item / NG, ng = item % NG, t = 2 * tp;
+        const size_t r0 = ((size_t(bi) * L + t0 + t) * G + g) * N + 8 * ng;
+        const size_t r1 = r0 + size_t(G) * N;
+        const uint4 b0 = t < qlen ? *reinterpret_cast<const uint4 *>(B + r0) : zero4();
+        const uint4 b1 = t + 1 < qlen ? *reinterpret_cast<const uint4 *>(B + r1) : zero4();
+        const uint4 c0 = t < qlen ? *reinterpret_cast<const uint4 *>(C + r0) : zero4();
+        const uint4 c1 = t + 1 < qlen ? *reinterpret_cast<const uint4 *>(C + r1) : zero4();
+        *reinterpret_cast<uint4 *>(Bn + t * NS + 8 * ng) = b0;
+        *reinterpret_cast<uint4 *>(Bn + (t + 1) * NS + 8 * ng) = b1;
+        *reinterpret_cast<uint4 *>(Cn + t * NS + 8 * ng) = c0;
+        *reinterpret_cast<uint4 *>(Cn + (t + 1) * NS + 8 * ng) = c1;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int item = tid + k * kThreads;
-        if (item < 32 * NG) {
-            const int tp = item / NG, ng = item % NG, t = 2 * tp;
-            const size_t r0 = ((size_t(bi) * L + t0 + t) * G + g) * N + 8 * ng;
-            const size_t r1 = r0 + size_t(G) * N;
-            const uint4 b0 = t < qlen ? *reinterpret_cast<const uint4 *>(B + r0) : zero4();
-            const uint4 b1 = t + 1 < qlen ? *reinterpret_cast<const uint4 *>(B + r1) : zero4();
-            const uint4 c0 = t < qlen ? *reinterpret_cast<const uint4 *>(C + r0) : zero4();
-            const uint4 c1 = t + 1 < qlen ? *reinterpret_cast<const uint4 *>(C + r1) : zero4();
-            *reinterpret_cast<uint4 *>(Bn + t * NS + 8 * ng) = b0;
-            *reinterpret_cast<uint4 *>(Bn + (t + 1) * NS + 8 * ng) = b1;
-            *reinterpret_cast<uint4 *>(Cn + t * NS + 8 * ng) = c0;
-            *reinterpret_cast<uint4 *>(Cn + (t + 1) * NS + 8 * ng) = c1;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int sh = 16 * (j & 1);
-                const uint32_t bl = ((&b0.x)[j >> 1] >> sh) & 0xffffu, bh = ((&b1.x)[j >> 1] >> sh) & 0xffffu;
-                const uint32_t cl = ((&c0.x)[j >> 1] >> sh) & 0xffffu, ch = ((&c1.x)[j >> 1] >> sh) & 0xffffu;
-                *reinterpret_cast<uint32_t *>(BT + (8 * ng + j) * RS + t) = bl | (bh << 16);
-                *reinterpret_cast<uint32_t *>(CT + (8 * ng + j) * RS + t) = cl | (ch << 16);
-            }
+        for (int j = 0; j < 8; ++j) {
+            const int sh = 16 * (j & 1);
+            const uint32_t bl = ((&b0.x)[j >> 1] >> sh) & 0xffffu, bh = ((&b1.x)[j >> 1] >> sh) & 0xffffu;
+            const uint32_t cl = ((&c0.x)[j >> 1] >> sh) & 0xffffu, ch = ((&c1.x)[j >> 1] >> sh) & 0xffffu;
+            *reinterpret_cast<uint32_t *>(BT + (8 * ng + j) * RS + t) = bl | (bh << 16);
+            *reinterpret_cast<uint32_t *>(CT + (8 * ng + j) * RS + t) = cl | (ch << 16);
         }
     }
     __syncthreads();
 
-    // G[t][s] = C_t . B_s for this wave's rows t, all s (shared by the heads)
-    f32x4 Gt[4];
+    // G[t][s] = C_t . B_s on this wave's score tiles (shared by the heads)
+    f32x4 Gt[2];
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
+    for (int k = 0; k < 2; ++k) {
+        const int sb = 2 * hw + k;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kq = 0; kq < KN; ++kq)
-            acc = mfma_bf16(lds16(Cn + (16 * w + r16) * NS + 32 * kq + 8 * g4),
+            acc = mfma_bf16(lds16(Cn + (16 * q + r16) * NS + 32 * kq + 8 * g4),
                             lds16(Bn + (16 * sb + r16) * NS + 32 * kq + 8 * g4), acc);
-        Gt[sb] = acc;
+        Gt[k] = acc;
     }
 
-    f32x4 accB[NTW][4], accC[NTW][4];
+    f32x4 accB[TW], accC[TW];
 #pragma unroll
-    for (int j = 0; j < NTW; ++j)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            accB[j][k] = {0.f, 0.f, 0.f, 0.f};
-            accC[j][k] = {0.f, 0.f, 0.f, 0.f};
-        }
+    for (int k = 0; k < TW; ++k) {
+        accB[k] = {0.f, 0.f, 0.f, 0.f};
+        accC[k] = {0.f, 0.f, 0.f, 0.f};
+    }
 
     for (int hh = 0; hh < HB; ++hh) {
         const int h = h0 + hh;
         const size_t bhc = (size_t(bi) * H + h) * nc + c;
         const size_t so = bhc * size_t(PN);
-        // states of this head as MFMA A operands (rows owned by this wave)
-        uint4 ghp[KN], ght[NTW][2], hnt[NTW][2];
+        // this head's states as MFMA A operands (rows owned by this wave)
+        uint4 ghp[KN], ght[2], hnt[2];
 #pragma unroll
         for (int kq = 0; kq < KN; ++kq)
-            ghp[kq] = *reinterpret_cast<const uint4 *>(ghN + so + (16 * w + r16) * N + 32 * kq + 8 * g4);
+            ghp[kq] = *reinterpret_cast<const uint4 *>(ghN + so + (16 * q + r16) * N + 32 * kq + 8 * g4);
 #pragma unroll
-        for (int j = 0; j < NTW; ++j)
-#pragma unroll
-            for (int kp = 0; kp < 2; ++kp) {
-                const size_t o = so + (16 * (NTW * w + j) + r16) * HP + 32 * kp + 8 * g4;
-                ght[j][kp] = *reinterpret_cast<const uint4 *>(ghT + o);
-                hnt[j][kp] = *reinterpret_cast<const uint4 *>(hinT + o);
-            }
-        const float dreg = lane < qlen ? dt[(size_t(bi) * L + t0 + lane) * H + h] : 0.f;
+        for (int kp = 0; kp < 2; ++kp) {
+            const size_t o = so + (16 * ntw + r16) * HP + 32 * kp + 8 * g4;
+            ght[kp] = *reinterpret_cast<const uint4 *>(ghT + o);
+            hnt[kp] = *reinterpret_cast<const uint4 *>(hinT + o);
+        }
+        const float dreg = dnext;
         const float Ah = A[h];
-        const float cs = wave_inclusive_scan(lane < qlen ? dreg * Ah * kLog2e : 0.f);
+        const float cs = wave_inclusive_scan(dreg * Ah * kLog2e);
         const float aend = __shfl(cs, qlen - 1, 64);
-        if (w == 0) {
+        if (w == 0) {   // wave 0 reads the previous head's scalars until here
             const bool valid = lane < qlen;
             acum[lane] = valid ? cs : 0.f;
             dts[lane] = dreg;
             wsv[lane] = valid ? exp2f(aend - cs) * dreg : 0.f;
             eac[lane] = valid ? exp2f(cs) : 0.f;
         }
-        // stage x, dy (natural) and dy transposed
-        *reinterpret_cast<uint4 *>(Xn + (2 * tpu) * RS + 8 * pgu) = xa;
-        *reinterpret_cast<uint4 *>(Xn + (2 * tpu + 1) * RS + 8 * pgu) = xb;
-        *reinterpret_cast<uint4 *>(DYn + (2 * tpu) * RS + 8 * pgu) = ya;
-        *reinterpret_cast<uint4 *>(DYn + (2 * tpu + 1) * RS + 8 * pgu) = yb;
+        // stage x (natural) or dy (natural and transposed)
+        {
+            bf16_bits *dstn = is_dy ? DYn : Xn;
+            *reinterpret_cast<uint4 *>(dstn + (2 * tpu) * RS + 8 * pgu) = ra;
+            *reinterpret_cast<uint4 *>(dstn + (2 * tpu + 1) * RS + 8 * pgu) = rb;
+            if (is_dy) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int sh = 16 * (j & 1);
-            const uint32_t lo = ((&ya.x)[j >> 1] >> sh) & 0xffffu, hi = ((&yb.x)[j >> 1] >> sh) & 0xffffu;
-            *reinterpret_cast<uint32_t *>(DYT + (8 * pgu + j) * RS + 2 * tpu) = lo | (hi << 16);
+                for (int j = 0; j < 8; ++j) {
+                    const int sh = 16 * (j & 1);
+                    const uint32_t lo = ((&ra.x)[j >> 1] >> sh) & 0xffffu, hi = ((&rb.x)[j >> 1] >> sh) & 0xffffu;
+                    *reinterpret_cast<uint32_t *>(DYT + (8 * pgu + j) * RS + 2 * tpu) = lo | (hi << 16);
+                }
+            }
         }
-        if (hh + 1 < HB) load_xy(h + 1);
+        if (hh + 1 < HB) load_head(h + 1);
         __syncthreads();
 
-        // ---- scores of this wave's rows t: W = dy x^T, then M, dS and the sums
+        // ---- scores on this wave's tiles: W = dy x^T, then M, dS and the sums
         {
             float rsum[4] = {0.f, 0.f, 0.f, 0.f};
-            const bf16x8 d0 = lds16(DYn + (16 * w + r16) * RS + 8 * g4);
-            const bf16x8 d1 = lds16(DYn + (16 * w + r16) * RS + 32 + 8 * g4);
+            const bf16x8 d0 = lds16(DYn + (16 * q + r16) * RS + 8 * g4);
+            const bf16x8 d1 = lds16(DYn + (16 * q + r16) * RS + 32 + 8 * g4);
             float at[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) at[i] = acum[16 * w + 4 * g4 + i];
+            for (int i = 0; i < 4; ++i) at[i] = acum[16 * q + 4 * g4 + i];
 #pragma unroll
-            for (int sb = 0; sb < 4; ++sb) {
+            for (int k = 0; k < 2; ++k) {
+                const int sb = 2 * hw + k;
                 f32x4 Wt = {0.f, 0.f, 0.f, 0.f};
                 Wt = mfma_bf16(d0, lds16(Xn + (16 * sb + r16) * RS + 8 * g4), Wt);
                 Wt = mfma_bf16(d1, lds16(Xn + (16 * sb + r16) * RS + 32 + 8 * g4), Wt);
@@ -386,45 +435,45 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chunk_bf(
                 float mv[4], sv[4], cr = 0.f, cglw = 0.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * w + 4 * g4 + i;
+                    const int t = 16 * q + 4 * g4 + i;
                     const float lm = (s <= t && t < qlen) ? exp2f(at[i] - as) : 0.f;
-                    const float gl = Gt[sb][i] * lm;
+                    const float gl = Gt[k][i] * lm;
                     mv[i] = gl * ds;
                     sv[i] = Wt[i] * lm * ds;
-                    const float r = sv[i] * Gt[sb][i];
+                    const float r = sv[i] * Gt[k][i];
                     rsum[i] += r;
                     cr += r;
                     cglw += gl * Wt[i];
                     DS[t * RS + s] = f32_to_bf16(sv[i]);
                 }
-                *reinterpret_cast<uint2 *>(MT + s * RS + 16 * w + 4 * g4) =
+                *reinterpret_cast<uint2 *>(MT + s * RS + 16 * q + 4 * g4) =
                     make_uint2(pack_bf16x2(mv[0], mv[1]), pack_bf16x2(mv[2], mv[3]));
-                *reinterpret_cast<uint2 *>(DST + s * RS + 16 * w + 4 * g4) =
+                *reinterpret_cast<uint2 *>(DST + s * RS + 16 * q + 4 * g4) =
                     make_uint2(pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3]));
                 cr = group4_sum(cr);
                 cglw = group4_sum(cglw);
                 if (g4 == 0) {
-                    colR[w * QB + s] = cr;
-                    colGLW[w * QB + s] = cglw;
+                    colR[q * QB + s] = cr;
+                    colGLW[q * QB + s] = cglw;
                 }
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float v = row16_sum(rsum[i]);
-                if (r16 == 0) rowR[16 * w + 4 * g4 + i] = v;
+                if (r16 == 0) rowR[hw * QB + 16 * q + 4 * g4 + i] = v;
             }
         }
         __syncthreads();
 
-        // ---- dx^T[p][s] (rows p of this wave) and U^T[p][s] = Gh[p] . B_s
+        // ---- dx^T[p][s] (rows p of block q) and U^T[p][s] = Gh[p] . B_s
         {
             const float Dh = D[h];
-            const bf16x8 e0 = lds16(DYT + (16 * w + r16) * RS + 8 * g4);
-            const bf16x8 e1 = lds16(DYT + (16 * w + r16) * RS + 32 + 8 * g4);
-            const int p0 = 16 * w + 4 * g4;
+            const bf16x8 e0 = lds16(DYT + (16 * q + r16) * RS + 8 * g4);
+            const bf16x8 e1 = lds16(DYT + (16 * q + r16) * RS + 32 + 8 * g4);
+            const int p0 = 16 * q + 4 * g4;
 #pragma unroll
-            for (int sb = 0; sb < 4; ++sb) {
-                const int s = 16 * sb + r16;
+            for (int k = 0; k < 2; ++k) {
+                const int s = 16 * (2 * hw + k) + r16;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f}, U = {0.f, 0.f, 0.f, 0.f};
                 acc = mfma_bf16(e0, lds16(MT + s * RS + 8 * g4), acc);
                 acc = mfma_bf16(e1, lds16(MT + s * RS + 32 + 8 * g4), acc);
@@ -446,94 +495,81 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chunk_bf(
                     *reinterpret_cast<uint2 *>(dx + ((size_t(bi) * L + t0 + s) * H + h) * HP + p0) =
                         make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
                 vp = group4_sum(vp);
-                if (g4 == 0) vsp[w * QB + s] = vp;
+                if (g4 == 0) vsp[q * QB + s] = vp;
             }
         }
 
         // ---- dC^T[n][t] += BT dS^T + e^{cum_t} V^T,  V^T[n][t] = Hin^T[n] . dy_t
         {
-            float yp[4] = {0.f, 0.f, 0.f, 0.f};
+            const bf16x8 b0 = lds16(BT + (16 * ntw + r16) * RS + 8 * g4);
+            const bf16x8 b1 = lds16(BT + (16 * ntw + r16) * RS + 32 + 8 * g4);
 #pragma unroll
-            for (int j = 0; j < NTW; ++j) {
-                const int nt = NTW * w + j;
-                const bf16x8 b0 = lds16(BT + (16 * nt + r16) * RS + 8 * g4);
-                const bf16x8 b1 = lds16(BT + (16 * nt + r16) * RS + 32 + 8 * g4);
+            for (int k = 0; k < TW; ++k) {
+                const int t = 16 * (tb0 + k) + r16;
+                f32x4 V = {0.f, 0.f, 0.f, 0.f}, dc = {0.f, 0.f, 0.f, 0.f};
+                V = mfma_bf16(as_bf16x8(hnt[0]), lds16(DYn + t * RS + 8 * g4), V);
+                V = mfma_bf16(as_bf16x8(hnt[1]), lds16(DYn + t * RS + 32 + 8 * g4), V);
+                dc = mfma_bf16(b0, lds16(DS + t * RS + 8 * g4), dc);
+                dc = mfma_bf16(b1, lds16(DS + t * RS + 32 + 8 * g4), dc);
+                const float e = eac[t];
+                const uint2 c4 = *reinterpret_cast<const uint2 *>(Cn + t * NS + 16 * ntw + 4 * g4);
+                const float cv[4] = {bf16_lo(c4.x), bf16_hi(c4.x), bf16_lo(c4.y), bf16_hi(c4.y)};
+                float yp = 0.f;
 #pragma unroll
-                for (int tb = 0; tb < 4; ++tb) {
-                    const int t = 16 * tb + r16;
-                    f32x4 V = {0.f, 0.f, 0.f, 0.f}, dc = {0.f, 0.f, 0.f, 0.f};
-                    V = mfma_bf16(as_bf16x8(hnt[j][0]), lds16(DYn + t * RS + 8 * g4), V);
-                    V = mfma_bf16(as_bf16x8(hnt[j][1]), lds16(DYn + t * RS + 32 + 8 * g4), V);
-                    dc = mfma_bf16(b0, lds16(DS + t * RS + 8 * g4), dc);
-                    dc = mfma_bf16(b1, lds16(DS + t * RS + 32 + 8 * g4), dc);
-                    const float e = eac[t];
-                    const uint2 c4 = *reinterpret_cast<const uint2 *>(Cn + t * NS + 16 * nt + 4 * g4);
-                    const float cv[4] = {bf16_lo(c4.x), bf16_hi(c4.x), bf16_lo(c4.y), bf16_hi(c4.y)};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        accC[j][tb][i] += dc[i] + e * V[i];
-                        yp[tb] += cv[i] * V[i];
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    accC[k][i] += dc[i] + e * V[i];
+                    yp += cv[i] * V[i];
                 }
-            }
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                const float v = group4_sum(yp[tb]);
-                if (g4 == 0) yocp[w * QB + 16 * tb + r16] = v;
+                yp = group4_sum(yp);
+                if (g4 == 0) yocp[ntw * QB + t] = yp;
             }
         }
 
         // ---- dB^T[n][s] += CT dS + w_s X2^T,  X2^T[n][s] = Gh^T[n] . x_s
+        {
+            const bf16x8 c0 = lds16(CT + (16 * ntw + r16) * RS + 8 * g4);
+            const bf16x8 c1 = lds16(CT + (16 * ntw + r16) * RS + 32 + 8 * g4);
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) {
-            const int nt = NTW * w + j;
-            const bf16x8 c0 = lds16(CT + (16 * nt + r16) * RS + 8 * g4);
-            const bf16x8 c1 = lds16(CT + (16 * nt + r16) * RS + 32 + 8 * g4);
-#pragma unroll
-            for (int sb = 0; sb < 4; ++sb) {
-                const int s = 16 * sb + r16;
+            for (int k = 0; k < TW; ++k) {
+                const int s = 16 * (tb0 + k) + r16;
                 f32x4 X2 = {0.f, 0.f, 0.f, 0.f}, db = {0.f, 0.f, 0.f, 0.f};
-                X2 = mfma_bf16(as_bf16x8(ght[j][0]), lds16(Xn + s * RS + 8 * g4), X2);
-                X2 = mfma_bf16(as_bf16x8(ght[j][1]), lds16(Xn + s * RS + 32 + 8 * g4), X2);
+                X2 = mfma_bf16(as_bf16x8(ght[0]), lds16(Xn + s * RS + 8 * g4), X2);
+                X2 = mfma_bf16(as_bf16x8(ght[1]), lds16(Xn + s * RS + 32 + 8 * g4), X2);
                 db = mfma_bf16(c0, lds16(DST + s * RS + 8 * g4), db);
                 db = mfma_bf16(c1, lds16(DST + s * RS + 32 + 8 * g4), db);
                 const float ws = wsv[s];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) accB[j][sb][i] += db[i] + ws * X2[i];
+                for (int i = 0; i < 4; ++i) accB[k][i] += db[i] + ws * X2[i];
             }
         }
 
-        // ---- <Gh, Hin> and sum x . dy of this head
+        // ---- <Gh, Hin> (waves 0 .. NT-1 hold each n row once) and sum x . dy
         {
             float gp = 0.f, xp = 0.f;
-#pragma unroll
-            for (int j = 0; j < NTW; ++j)
+            if (w < NT) {
 #pragma unroll
                 for (int kp = 0; kp < 2; ++kp)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const uint32_t a = (&ght[j][kp].x)[q], b = (&hnt[j][kp].x)[q];
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t a = (&ght[kp].x)[j], b = (&hnt[kp].x)[j];
                         gp += bf16_lo(a) * bf16_lo(b) + bf16_hi(a) * bf16_hi(b);
                     }
-            {   // x . dy from LDS (the registers already hold the next head): token
-                // tid / 4, 16 values
-                const int t = tid >> 2, p0 = 16 * (tid & 3);
+            }
+            {   // token tid / 8, 8 values at 8 (tid % 8)
+                const int t = tid >> 3, p0 = 8 * (tid & 7);
+                const uint4 xv = *reinterpret_cast<const uint4 *>(Xn + t * RS + p0);
+                const uint4 yv = *reinterpret_cast<const uint4 *>(DYn + t * RS + p0);
 #pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    const uint4 xv = *reinterpret_cast<const uint4 *>(Xn + t * RS + p0 + 8 * k);
-                    const uint4 yv = *reinterpret_cast<const uint4 *>(DYn + t * RS + p0 + 8 * k);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const uint32_t a = (&xv.x)[q], b = (&yv.x)[q];
-                        xp += bf16_lo(a) * bf16_lo(b) + bf16_hi(a) * bf16_hi(b);
-                    }
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t a = (&xv.x)[j], b = (&yv.x)[j];
+                    xp += bf16_lo(a) * bf16_lo(b) + bf16_hi(a) * bf16_hi(b);
                 }
             }
             gp = wave_sum(gp);
             xp = wave_sum(xp);
             if (lane == 0) {
                 red[w] = gp;
-                red[4 + w] = xp;
+                red[8 + w] = xp;
             }
         }
         __syncthreads();
@@ -542,15 +578,24 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chunk_bf(
         if (w == 0) {
             const int t = lane;
             const bool valid = t < qlen;
-            const float v = (vsp[t] + vsp[QB + t]) + (vsp[2 * QB + t] + vsp[3 * QB + t]);
-            const float y = (yocp[t] + yocp[QB + t]) + (yocp[2 * QB + t] + yocp[3 * QB + t]);
-            const float cr = (colR[t] + colR[QB + t]) + (colR[2 * QB + t] + colR[3 * QB + t]);
-            const float glw = (colGLW[t] + colGLW[QB + t]) + (colGLW[2 * QB + t] + colGLW[3 * QB + t]);
-            const float ghin = (red[0] + red[1]) + (red[2] + red[3]);
-            const float xdy = (red[4] + red[5]) + (red[6] + red[7]);
+            float v = 0.f, y = 0.f, cr = 0.f, glw = 0.f, ghin = 0.f, xdy = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                v += vsp[k * QB + t];
+                cr += colR[k * QB + t];
+                glw += colGLW[k * QB + t];
+            }
+#pragma unroll
+            for (int k = 0; k < NT; ++k) y += yocp[k * QB + t];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                ghin += red[k];
+                xdy += red[8 + k];
+            }
+            const float rr = rowR[t] + rowR[QB + t];
             const float wt = wsv[t];
             const float dend = exp2f(aend) * ghin + wave_sum(wt * v);
-            float dc = valid ? rowR[t] - cr + eac[t] * y - wt * v : 0.f;
+            float dc = valid ? rr - cr + eac[t] * y - wt * v : 0.f;
             if (t == qlen - 1) dc += dend;
             const float inc = wave_inclusive_scan(dc);
             const float da = __shfl(inc, 63, 64) - inc + dc;     // sum over tau >= t
@@ -565,19 +610,14 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chunk_bf(
     }
 
     // per-block partials of dB and dC: tiles with rows n, columns s (or t)
+    const int n0 = 16 * ntw + 4 * g4;
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-        const int n0 = 16 * (NTW * w + j) + 4 * g4;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int s = 16 * k + r16;
-            if (s < qlen) {
-                const size_t o = ((size_t(bi) * L + t0 + s) * nblk + hbk) * N + n0;
-                *reinterpret_cast<float4 *>(dBp + o) =
-                    make_float4(accB[j][k][0], accB[j][k][1], accB[j][k][2], accB[j][k][3]);
-                *reinterpret_cast<float4 *>(dCp + o) =
-                    make_float4(accC[j][k][0], accC[j][k][1], accC[j][k][2], accC[j][k][3]);
-            }
+    for (int k = 0; k < TW; ++k) {
+        const int s = 16 * (tb0 + k) + r16;
+        if (s < qlen) {
+            const size_t o = ((size_t(bi) * L + t0 + s) * nblk + hbk) * N + n0;
+            *reinterpret_cast<float4 *>(dBp + o) = make_float4(accB[k][0], accB[k][1], accB[k][2], accB[k][3]);
+            *reinterpret_cast<float4 *>(dCp + o) = make_float4(accC[k][0], accC[k][1], accC[k][2], accC[k][3]);
         }
     }
 }
@@ -595,15 +635,17 @@ hipError_t launch_n(const ChunkScanBwdArgs &a, const ChunkScanBwdPlan &pl, hipSt
     const bf16_bits *x = static_cast<const bf16_bits *>(a.x), *B = static_cast<const bf16_bits *>(a.B);
     const bf16_bits *C = static_cast<const bf16_bits *>(a.C), *dy = static_cast<const bf16_bits *>(a.dy);
     hipError_t e;
-    hipLaunchKernelGGL((k_bwd_chain<N>), dim3(2, a.H, a.b), dim3(kThreads), 0, stream, x, a.dt, a.A,
-                       B, C, dy, a.init_state, a.d_final, hinT, ghT, ghN, a.d_init, a.L, a.H, a.G,
-                       pl.nc);
+    hipLaunchKernelGGL((k_bwd_chain_fwd<N>), dim3(a.H, a.b), dim3(kThreads), 0, stream, x, a.dt,
+                       a.A, B, a.init_state, hinT, a.L, a.H, a.G, pl.nc);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((k_bwd_chain_rev<N>), dim3(a.H, a.b), dim3(kThreads), 0, stream, dy, a.dt,
+                       a.A, C, a.d_final, ghT, ghN, a.d_init, a.L, a.H, a.G, pl.nc);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t lds = ChunkLds<N>::bytes;
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_bwd_chunk_bf<N>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_bwd_chunk_bf<N>), dim3(pl.nc, a.H / pl.hb, a.b), dim3(kThreads), lds,
+    hipLaunchKernelGGL((k_bwd_chunk_bf<N>), dim3(pl.nc, a.H / pl.hb, a.b), dim3(kChunkThreads), lds,
                        stream, x, a.dt, a.A, B, C, a.D, dy, hinT, ghT, ghN,
                        static_cast<bf16_bits *>(a.dx), a.ddt, dBp, dCp, dAp, dDp, a.L, a.H, a.G,
                        pl.nc, pl.hb);
