@@ -6,16 +6,16 @@
 // reverse; intermediate states recomputed rather than stored, "另辟蹊径--Mamba介绍",
 // «Hardware-aware Algorithm»), organised for fewer HBM bytes:
 //
-//   k_bwd_chain_fwd / k_bwd_chain_rev
-//                  one workgroup per (head, batch) walks the 64-token chunks
-//                  in order (forward) or in reverse, keeping the P x N state in MFMA
+//   k_bwd_chain    one workgroup per (head, batch) walks the 64-token chunks in
+//                  order (forward) or in reverse, keeping the P x N state in MFMA
 //                  accumulators: the forward walk writes the state entering each chunk,
 //                  Hin_c; the reverse walk writes the gradient of the state leaving it,
 //                  Gh_c, and finally d init_state.  Each chunk's contribution
 //                  (sum_t w_t x_t (outer) B_t, or sum_t e^{cum_t} dy_t (outer) C_t) is
 //                  one bf16 MFMA product added onto the decayed state, so no per-chunk
 //                  state ever goes to HBM in fp32.  The states are stored in bf16, in
-//                  the layouts the next kernel reads as MFMA operands.
+//                  MFMA accumulator tile order (contiguous stores; the next kernel
+//                  assembles its operands from two 8-byte pieces).
 //   k_bwd_chunk_bf one workgroup of 8 waves per (chunk, block of up to 8 heads of one
 //                  group, batch): C B^T once per block, then per head the score tiles, dx,
 //                  and the head's dB / dC contributions, which stay in registers across
@@ -47,94 +47,105 @@ __device__ __forceinline__ uint4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0));
 }
 
-// Inputs of one chunk step, loaded two steps ahead: the token pair (2 tpu, 2 tpu + 1)
+constexpr int kChainThreads = 512;   // 4 loader waves + 4 state waves
+
+// Stored states keep the MFMA accumulator order: 16 x 16 tiles of 256 values, lane l
+// of the producing wave holding 4 consecutive bf16 at 4 l (tile element (4 (l / 16) +
+// i, l % 16) at 4 l + i), so every store writes 512 contiguous bytes.
+//   Hin^T, Gh^T: tile nt * 4 + pt holds rows p 16 pt .. (i), columns n 16 nt .. (l % 16)
+//   Gh:          tile pt * NT + nt holds rows n 16 nt .. (i), columns p 16 pt .. (l % 16)
+__device__ __forceinline__ int tile_off(int tile, int l) { return tile * 256 + 4 * l; }
+
+// The 8 consecutive values (along the tile rows) that lane (r16, g4) of a consumer
+// supplies as an MFMA operand at k step kk (32 values): rows 32 kk + 8 g4 .. + 7 of
+// column r16, taken from tiles t_base + (2 kk + g4 / 2) * t_stride as two 8-byte
+// pieces of lanes r16 + 32 (g4 & 1) and r16 + 32 (g4 & 1) + 16.
+__device__ __forceinline__ uint4 tile_operand(const bf16_bits *base, int t_base, int t_stride,
+                                              int kk, int r16, int g4) {
+    const int tile = t_base + (2 * kk + (g4 >> 1)) * t_stride;
+    const int l = r16 + 32 * (g4 & 1);
+    const uint2 lo = *reinterpret_cast<const uint2 *>(base + tile_off(tile, l));
+    const uint2 hi = *reinterpret_cast<const uint2 *>(base + tile_off(tile, l + 16));
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+// Inputs of one chunk step held by a loader thread: the token pair (2 tpu, 2 tpu + 1)
 // of u (x or dy) at p group pgu, two token-pair items of v (B or C), and dt.
 struct ChainPf {
     uint4 ua, ub, va[2], vb[2];
     float d;
 };
 
-// DIR 0: Hin_c for c = 0 .. nc-1 (Hin^T, [n][p] per chunk).
-// DIR 1: Gh_c for c = nc-1 .. 0 (Gh^T [n][p] and Gh [p][n]), then d_init.
+// One chain walk per workgroup of 8 waves with split roles, so that no wave waits on
+// another kind of memory traffic (the vector-memory counter is per wave and in order):
+//   loader waves 0-3  load chunk inputs two steps ahead through buffer resources
+//                     sized to the chunk's valid tokens (tokens past the end read as
+//                     zero), scan the chunk's decays, and stage the weighted u and v
+//                     transposed into one of two LDS buffers;
+//   state waves 4-7   hold the P x N state in MFMA accumulators, store it, and add the
+//                     staged chunk's contribution: state <- alpha state + U^T V.
+// One barrier per step hands a staged buffer from the loaders to the state waves.
+// DIR 0: Hin_c for c = 0 .. nc-1 (as Hin^T tiles), starting from init_state.
+// DIR 1: Gh_c for c = nc-1 .. 0 (as Gh^T and Gh tiles) from d_final, then d_init.
 // The reverse walk holds its state twice, as tiles with rows p (stored as Gh^T) and
-// with rows n (stored as Gh), so every store writes 4 consecutive values.  Loads go
-// through buffer resources sized to the chunk's valid tokens: tokens past the end of
-// the sequence read as zero without a branch.
+// with rows n (stored as Gh).
 template <int N, int DIR>
-__device__ __forceinline__ void chain_walk(
-    const bf16_bits *__restrict__ u, const float *__restrict__ dt, float Ah,
-    const bf16_bits *__restrict__ v, const float *__restrict__ s0,
-    bf16_bits *__restrict__ dstT, bf16_bits *__restrict__ ghN, float *__restrict__ d_init,
-    int bi, int h, int L, int H, int G, int nc, bf16_bits *AT, bf16_bits *VT, float *wts) {
+__global__ __launch_bounds__(kChainThreads, 4) void k_bwd_chain(
+    const bf16_bits *__restrict__ u, const float *__restrict__ dt, const float *__restrict__ A,
+    const bf16_bits *__restrict__ v, const float *__restrict__ s0, bf16_bits *__restrict__ dstT,
+    bf16_bits *__restrict__ ghN, float *__restrict__ d_init, int L, int H, int G, int nc) {
     constexpr int NT = N / 16, NTW = NT / 4, NG = N / 8, PN = HP * N;
     constexpr int kVItems = (32 * NG + kThreads - 1) / kThreads;
+    __shared__ __align__(16) bf16_bits AT[2][HP * RS];   // [p][t] weighted u
+    __shared__ __align__(16) bf16_bits VT[2][N * RS];    // [n][t] v
+    __shared__ float al_sh[2];
+    const int h = blockIdx.x, bi = blockIdx.y;
     const int g = h / (H / G);
+    const float Ah = A[h];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
     const size_t bh = size_t(bi) * H + h;
-    const int tpu = tid >> 3, pgu = tid & 7;
-
-    f32x4 accP[NT];
-    f32x4 accN[DIR ? NTW : 1][4];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            accP[nt][i] = s0 ? s0[bh * PN + (16 * w + 4 * g4 + i) * N + 16 * nt + r16] : 0.f;
-    if constexpr (DIR == 1) {
-#pragma unroll
-        for (int j = 0; j < NTW; ++j)
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
-                float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (s0)
-                    q = *reinterpret_cast<const float4 *>(
-                        s0 + bh * PN + (16 * pt + r16) * N + 16 * (NTW * w + j) + 4 * g4);
-                accN[j][pt] = {q.x, q.y, q.z, q.w};
-            }
-    }
-
     auto chunk_of = [&](int step) { return DIR == 0 ? step : nc - 1 - step; };
-    auto load = [&](ChainPf &f, int step) {
-        const int c = chunk_of(step);
-        const bool live = step < nc;
-        const int t0 = live ? c * QB : 0;
-        const int qlen = live ? min(QB, L - t0) : 0;
-        const size_t tok0 = size_t(bi) * L + t0;
-        const auto ur = buffer_rsrc(u + tok0 * H * HP, uint32_t(qlen) * uint32_t(H * HP) * 2u);
-        const auto vr = buffer_rsrc(v + tok0 * G * N, uint32_t(qlen) * uint32_t(G * N) * 2u);
-        const auto dr = buffer_rsrc(dt + tok0 * H, uint32_t(qlen) * uint32_t(H) * 4u);
-        const uint32_t uo = (uint32_t(2 * tpu) * H + h) * HP + 8 * pgu;
-        f.ua = ld128(ur, uo * 2u);
-        f.ub = ld128(ur, (uo + H * HP) * 2u);
-#pragma unroll
-        for (int k = 0; k < kVItems; ++k) {
-            const int item = min(tid + k * kThreads, 32 * NG - 1);
-            const int tp = item / NG, ng = item % NG;
-            const uint32_t vo = (uint32_t(2 * tp) * G + g) * N + 8 * ng;
-            f.va[k] = ld128(vr, vo * 2u);
-            f.vb[k] = ld128(vr, (vo + G * N) * 2u);
-        }
-        f.d = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(dr, int((lane * H + h) * 4), 0, 0));
-    };
 
-    auto step_fn = [&](ChainPf &f, int step) {
-        const int c = chunk_of(step);
-        const int qlen = min(QB, L - c * QB);
-        // every wave scans the chunk's decays (no branch, so the compiler can keep
-        // counting the loads in flight); the waves write identical weights
-        const float cs = wave_inclusive_scan(f.d * Ah * kLog2e);
-        const float aend = __shfl(cs, qlen - 1, 64);
-        const float al = exp2f(aend);
-        wts[lane] = lane < qlen ? (DIR == 0 ? exp2f(aend - cs) * f.d : exp2f(cs)) : 0.f;
-        __syncthreads();
-        {   // stage the weighted u and v transposed, token pairs
-            const float wa = wts[2 * tpu], wb = wts[2 * tpu + 1];
+    if (w < 4) {
+        // ------------------------------------------------ loader waves
+        const int tpu = tid >> 3, pgu = tid & 7;
+        auto load = [&](ChainPf &f, int step) {
+            const bool live = step < nc;
+            const int t0 = live ? chunk_of(step) * QB : 0;
+            const int qlen = live ? min(QB, L - t0) : 0;
+            const size_t tok0 = size_t(bi) * L + t0;
+            const auto ur = buffer_rsrc(u + tok0 * H * HP, uint32_t(qlen) * uint32_t(H * HP) * 2u);
+            const auto vr = buffer_rsrc(v + tok0 * G * N, uint32_t(qlen) * uint32_t(G * N) * 2u);
+            const auto dr = buffer_rsrc(dt + tok0 * H, uint32_t(qlen) * uint32_t(H) * 4u);
+            const uint32_t uo = (uint32_t(2 * tpu) * H + h) * HP + 8 * pgu;
+            f.ua = ld128(ur, uo * 2u);
+            f.ub = ld128(ur, (uo + H * HP) * 2u);
+#pragma unroll
+            for (int k = 0; k < kVItems; ++k) {
+                const int item = min(tid + k * kThreads, 32 * NG - 1);
+                const int tp = item / NG, ng = item % NG;
+                const uint32_t vo = (uint32_t(2 * tp) * G + g) * N + 8 * ng;
+                f.va[k] = ld128(vr, vo * 2u);
+                f.vb[k] = ld128(vr, (vo + G * N) * 2u);
+            }
+            f.d = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(dr, int((lane * H + h) * 4), 0, 0));
+        };
+        auto stage = [&](const ChainPf &f, int step) {
+            const bool live = step < nc;
+            const int qlen = live ? min(QB, L - chunk_of(step) * QB) : 1;
+            const int buf = step & 1;
+            const float cs = wave_inclusive_scan(f.d * Ah * kLog2e);
+            const float aend = __shfl(cs, qlen - 1, 64);
+            const float wv = lane < qlen ? (DIR == 0 ? exp2f(aend - cs) * f.d : exp2f(cs)) : 0.f;
+            if (tid == 0) al_sh[buf] = exp2f(aend);
+            const float wa = __shfl(wv, 2 * tpu, 64), wb = __shfl(wv, 2 * tpu + 1, 64);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const uint32_t ea = (&f.ua.x)[j >> 1], eb = (&f.ub.x)[j >> 1];
                 const float fa = (j & 1) ? bf16_hi(ea) : bf16_lo(ea);
                 const float fb = (j & 1) ? bf16_hi(eb) : bf16_lo(eb);
-                *reinterpret_cast<uint32_t *>(AT + (8 * pgu + j) * RS + 2 * tpu) = pack_bf16x2(fa * wa, fb * wb);
+                *reinterpret_cast<uint32_t *>(&AT[buf][(8 * pgu + j) * RS + 2 * tpu]) =
+                    pack_bf16x2(fa * wa, fb * wb);
             }
 #pragma unroll
             for (int k = 0; k < kVItems; ++k) {
@@ -146,102 +157,108 @@ __device__ __forceinline__ void chain_walk(
                         const uint32_t ea = (&f.va[k].x)[j >> 1], eb = (&f.vb[k].x)[j >> 1];
                         const uint32_t lo = (j & 1) ? (ea >> 16) : (ea & 0xffffu);
                         const uint32_t hi = (j & 1) ? (eb & 0xffff0000u) : (eb << 16);
-                        *reinterpret_cast<uint32_t *>(VT + (8 * ng + j) * RS + 2 * tp) = lo | hi;
+                        *reinterpret_cast<uint32_t *>(&VT[buf][(8 * ng + j) * RS + 2 * tp]) = lo | hi;
                     }
                 }
             }
-        }
-        load(f, step + 2);
+        };
+        ChainPf f0, f1;
+        load(f0, 0);
+        load(f1, 1);
+        stage(f0, 0);
+        load(f0, 2);
         __syncthreads();
+        // iteration s stages step s + 1 (set (s + 1) & 1) and refills that set with s + 3
+        int s = 0;
+        for (; s + 1 < nc; s += 2) {
+            stage(f1, s + 1);
+            load(f1, s + 3);
+            __syncthreads();
+            stage(f0, s + 2);
+            load(f0, s + 4);
+            __syncthreads();
+        }
+        if (s < nc) __syncthreads();
+        return;
+    }
 
+    // ---------------------------------------------------- state waves
+    const int sw = w - 4;
+    f32x4 accP[NT];
+    f32x4 accN[DIR ? NTW : 1][4];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            accP[nt][i] = s0 ? s0[bh * PN + (16 * sw + 4 * g4 + i) * N + 16 * nt + r16] : 0.f;
+    if constexpr (DIR == 1) {
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (s0)
+                    q = *reinterpret_cast<const float4 *>(
+                        s0 + bh * PN + (16 * pt + r16) * N + 16 * (NTW * sw + j) + 4 * g4);
+                accN[j][pt] = {q.x, q.y, q.z, q.w};
+            }
+    }
+    __syncthreads();
+    for (int step = 0; step < nc; ++step) {
+        const int c = chunk_of(step);
+        const int buf = step & 1;
         // store the state (entering chunk c forward, leaving chunk c in reverse)
         const size_t so = (bh * nc + c) * size_t(PN);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-            *reinterpret_cast<uint2 *>(dstT + so + (16 * nt + r16) * HP + 16 * w + 4 * g4) =
+            *reinterpret_cast<uint2 *>(dstT + so + tile_off(nt * 4 + sw, lane)) =
                 make_uint2(pack_bf16x2(accP[nt][0], accP[nt][1]), pack_bf16x2(accP[nt][2], accP[nt][3]));
         if constexpr (DIR == 1) {
 #pragma unroll
             for (int j = 0; j < NTW; ++j)
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt)
-                    *reinterpret_cast<uint2 *>(ghN + so + (16 * pt + r16) * N + 16 * (NTW * w + j) + 4 * g4) =
+                    *reinterpret_cast<uint2 *>(ghN + so + tile_off(pt * NT + NTW * sw + j, lane)) =
                         make_uint2(pack_bf16x2(accN[j][pt][0], accN[j][pt][1]),
                                    pack_bf16x2(accN[j][pt][2], accN[j][pt][3]));
         }
-
         // state <- al * state + (this chunk's contribution)
-        const bf16x8 a0 = lds16(AT + (16 * w + r16) * RS + 8 * g4);
-        const bf16x8 a1 = lds16(AT + (16 * w + r16) * RS + 32 + 8 * g4);
+        const float al = al_sh[buf];
+        const bf16_bits *at = AT[buf], *vt = VT[buf];
+        const bf16x8 a0 = lds16(at + (16 * sw + r16) * RS + 8 * g4);
+        const bf16x8 a1 = lds16(at + (16 * sw + r16) * RS + 32 + 8 * g4);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            f32x4 s = accP[nt] * al;
-            s = mfma_bf16(a0, lds16(VT + (16 * nt + r16) * RS + 8 * g4), s);
-            accP[nt] = mfma_bf16(a1, lds16(VT + (16 * nt + r16) * RS + 32 + 8 * g4), s);
+            f32x4 t = accP[nt] * al;
+            t = mfma_bf16(a0, lds16(vt + (16 * nt + r16) * RS + 8 * g4), t);
+            accP[nt] = mfma_bf16(a1, lds16(vt + (16 * nt + r16) * RS + 32 + 8 * g4), t);
         }
         if constexpr (DIR == 1) {
 #pragma unroll
             for (int j = 0; j < NTW; ++j) {
-                const int nt = NTW * w + j;
-                const bf16x8 c0 = lds16(VT + (16 * nt + r16) * RS + 8 * g4);
-                const bf16x8 c1 = lds16(VT + (16 * nt + r16) * RS + 32 + 8 * g4);
+                const int nt = NTW * sw + j;
+                const bf16x8 c0 = lds16(vt + (16 * nt + r16) * RS + 8 * g4);
+                const bf16x8 c1 = lds16(vt + (16 * nt + r16) * RS + 32 + 8 * g4);
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) {
-                    f32x4 s = accN[j][pt] * al;
-                    s = mfma_bf16(c0, lds16(AT + (16 * pt + r16) * RS + 8 * g4), s);
-                    accN[j][pt] = mfma_bf16(c1, lds16(AT + (16 * pt + r16) * RS + 32 + 8 * g4), s);
+                    f32x4 t = accN[j][pt] * al;
+                    t = mfma_bf16(c0, lds16(at + (16 * pt + r16) * RS + 8 * g4), t);
+                    accN[j][pt] = mfma_bf16(c1, lds16(at + (16 * pt + r16) * RS + 32 + 8 * g4), t);
                 }
             }
         }
-    };
-
-    ChainPf f0, f1;
-    load(f0, 0);
-    load(f1, 1);
-    int step = 0;
-    for (; step + 1 < nc; step += 2) {
-        step_fn(f0, step);
-        step_fn(f1, step + 1);
+        __syncthreads();
     }
-    if (step < nc) step_fn(f0, step);
     if constexpr (DIR == 1) {
         if (d_init) {
 #pragma unroll
             for (int j = 0; j < NTW; ++j)
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt)
-                    *reinterpret_cast<float4 *>(d_init + bh * PN + (16 * pt + r16) * N + 16 * (NTW * w + j) + 4 * g4) =
+                    *reinterpret_cast<float4 *>(d_init + bh * PN + (16 * pt + r16) * N + 16 * (NTW * sw + j) + 4 * g4) =
                         make_float4(accN[j][pt][0], accN[j][pt][1], accN[j][pt][2], accN[j][pt][3]);
         }
     }
-}
-
-// The two walks are separate kernels so that each gets the registers it needs (the
-// reverse walk holds two copies of the state).
-template <int N>
-__global__ __launch_bounds__(kThreads) void k_bwd_chain_fwd(
-    const bf16_bits *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
-    const bf16_bits *__restrict__ B, const float *__restrict__ init_state,
-    bf16_bits *__restrict__ hinT, int L, int H, int G, int nc) {
-    __shared__ __align__(16) bf16_bits AT[HP * RS];    // [p][t] weighted x
-    __shared__ __align__(16) bf16_bits VT[N * RS];     // [n][t] B
-    __shared__ float wts[QB];
-    const int h = blockIdx.x, bi = blockIdx.y;
-    chain_walk<N, 0>(x, dt, A[h], B, init_state, hinT, nullptr, nullptr, bi, h, L, H, G, nc, AT,
-                     VT, wts);
-}
-
-template <int N>
-__global__ __launch_bounds__(kThreads, 2) void k_bwd_chain_rev(
-    const bf16_bits *__restrict__ dy, const float *__restrict__ dt, const float *__restrict__ A,
-    const bf16_bits *__restrict__ C, const float *__restrict__ d_final,
-    bf16_bits *__restrict__ ghT, bf16_bits *__restrict__ ghN, float *__restrict__ d_init, int L,
-    int H, int G, int nc) {
-    __shared__ __align__(16) bf16_bits AT[HP * RS];    // [p][t] weighted dy
-    __shared__ __align__(16) bf16_bits VT[N * RS];     // [n][t] C
-    __shared__ float wts[QB];
-    const int h = blockIdx.x, bi = blockIdx.y;
-    chain_walk<N, 1>(dy, dt, A[h], C, d_final, ghT, ghN, d_init, bi, h, L, H, G, nc, AT, VT, wts);
 }
 
 // ------------------------------------------------------------ in-chunk gradients
@@ -378,15 +395,14 @@ __global__ __launch_bounds__(kChunkThreads) void k_bwd_chunk_bf(
         const size_t bhc = (size_t(bi) * H + h) * nc + c;
         const size_t so = bhc * size_t(PN);
         // this head's states as MFMA A operands (rows owned by this wave)
+        // (Gh: rows p of block q, k = n; Gh^T and Hin^T: rows n of tile ntw, k = p)
         uint4 ghp[KN], ght[2], hnt[2];
 #pragma unroll
-        for (int kq = 0; kq < KN; ++kq)
-            ghp[kq] = *reinterpret_cast<const uint4 *>(ghN + so + (16 * q + r16) * N + 32 * kq + 8 * g4);
+        for (int kq = 0; kq < KN; ++kq) ghp[kq] = tile_operand(ghN + so, q * NT, 1, kq, r16, g4);
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp) {
-            const size_t o = so + (16 * ntw + r16) * HP + 32 * kp + 8 * g4;
-            ght[kp] = *reinterpret_cast<const uint4 *>(ghT + o);
-            hnt[kp] = *reinterpret_cast<const uint4 *>(hinT + o);
+            ght[kp] = tile_operand(ghT + so, ntw * 4, 1, kp, r16, g4);
+            hnt[kp] = tile_operand(hinT + so, ntw * 4, 1, kp, r16, g4);
         }
         const float dreg = dnext;
         const float Ah = A[h];
@@ -635,11 +651,11 @@ hipError_t launch_n(const ChunkScanBwdArgs &a, const ChunkScanBwdPlan &pl, hipSt
     const bf16_bits *x = static_cast<const bf16_bits *>(a.x), *B = static_cast<const bf16_bits *>(a.B);
     const bf16_bits *C = static_cast<const bf16_bits *>(a.C), *dy = static_cast<const bf16_bits *>(a.dy);
     hipError_t e;
-    hipLaunchKernelGGL((k_bwd_chain_fwd<N>), dim3(a.H, a.b), dim3(kThreads), 0, stream, x, a.dt,
-                       a.A, B, a.init_state, hinT, a.L, a.H, a.G, pl.nc);
+    hipLaunchKernelGGL((k_bwd_chain<N, 0>), dim3(a.H, a.b), dim3(kChainThreads), 0, stream, x,
+                       a.dt, a.A, B, a.init_state, hinT, nullptr, nullptr, a.L, a.H, a.G, pl.nc);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_bwd_chain_rev<N>), dim3(a.H, a.b), dim3(kThreads), 0, stream, dy, a.dt,
-                       a.A, C, a.d_final, ghT, ghN, a.d_init, a.L, a.H, a.G, pl.nc);
+    hipLaunchKernelGGL((k_bwd_chain<N, 1>), dim3(a.H, a.b), dim3(kChainThreads), 0, stream, dy,
+                       a.dt, a.A, C, a.d_final, ghT, ghN, a.d_init, a.L, a.H, a.G, pl.nc);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t lds = ChunkLds<N>::bytes;
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_bwd_chunk_bf<N>),
