@@ -21,6 +21,9 @@ Printed: one JSON line with the contract fields plus
                 SSD replaces) on the same layer shape (4 x 2048 tokens, 5120
                 channels) at N=16 and N=128, and how many times faster the SSD
                 chunked scan (N=128) is than each
+  backward      ssd_chunk_scan_bwd (all seven gradients, states recomputed) on the
+                L=2048 layer with upstream gradients for y and the final state:
+                tokens/s and algorithmic bytes / call time against 8 TB/s
 """
 import argparse
 import hashlib
@@ -192,6 +195,47 @@ def time_verify(steps, warmup, bd, inputs, torch):
     return dict(dims=d, alg_bytes=alg, call_ms_mean=mean_ms, gbs=alg / (mean_ms * 1e-3) / 1e9)
 
 
+def bwd_alg_bytes(d, io_bytes, init, final):
+    """Bytes the gradient call must move at least: x, dy, B, C, dt, A, D, the initial
+    state and d_final read; dx, ddt, dA, dB, dC, dD and d_init written."""
+    b, L, H, P, N, G = (d[k] for k in ("b", "L", "H", "P", "N", "G"))
+    xb, bc, st = b * L * H * P * io_bytes, b * L * G * N * io_bytes, b * H * P * N * 4
+    return (3 * xb + 4 * bc + 2 * b * L * H * 4 + (st if init else 0) + (st if final else 0) +
+            st + 4 * H * 4)
+
+
+def time_backward(name, steps, warmup, bd, inputs, torch):
+    """ssd_chunk_scan_bwd on a scan workload with upstream gradients for y and the final
+    state; inputs rotated like time_scan's."""
+    inp = inputs.make_workload(name)
+    dy, dfin = inputs.make_upstream_grads(inp, seed=77)
+    d = inp.dims
+    io_bytes = 2 if inp.io == "bf16" else 4
+    alg = bwd_alg_bytes(d, io_bytes, inp.init_state is not None, True)
+    nsets = max(2, math.ceil(3 * MALL_BYTES / alg))
+    sets = _copies(inp, nsets, bd)
+    for s in sets:
+        s["dy"], s["dfin"] = bd.to_device(dy), bd.to_device(dfin)
+        s["out"] = [torch.empty_like(s["x"]), torch.empty_like(s["dt"]), torch.empty_like(s["A"]),
+                    torch.empty_like(s["B"]), torch.empty_like(s["C"]), torch.empty_like(s["D"]),
+                    torch.empty((d["b"], d["H"], d["P"], d["N"]), dtype=torch.float32,
+                                device="cuda")]
+    n = bd.ssd_chunk_scan_bwd_workspace_bytes(d["b"], d["L"], d["H"], d["P"], d["N"], d["G"],
+                                              bd._io_code(sets[0]["x"]))
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        s = sets[i % nsets]
+        bd.ssd_chunk_scan_bwd(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"], s["init_state"],
+                              s["dy"], s["dfin"], *s["out"], ws, stream)
+
+    for i in range(warmup):
+        call(i)
+    mean_ms, _ = _timed(call, warmup, steps, stream, torch)
+    return dict(dims=d, alg_bytes=alg, call_ms_mean=mean_ms, workspace_bytes=n)
+
+
 def copy_bandwidth(torch, mib=1024, reps=10):
     """Read+write GB/s of a plain elementwise kernel over a buffer far larger than the
     caches: the practical HBM ceiling beside the 8 TB/s specification."""
@@ -315,6 +359,16 @@ def main():
                             "call_ms_mean": rs["call_ms_mean"],
                             "ssd_N128_speedup": ssd_tps / tps}
         out["selective_scan_comparison"] = cmp
+        rb = time_backward(args.workload, max(5, args.steps // 3), 2, bd, inputs, torch)
+        db = rb["dims"]
+        ab = rb["alg_bytes"] / (rb["call_ms_mean"] * 1e-3) / 1e9
+        out["backward"] = {"workload": args.workload,
+                           "tokens_per_s": db["b"] * db["L"] / (rb["call_ms_mean"] * 1e-3),
+                           "call_ms_mean": rb["call_ms_mean"], "alg_bytes": rb["alg_bytes"],
+                           "achieved_GBs": ab, "hbm_frac": ab / HBM_PEAK_GBS,
+                           "workspace_bytes": rb["workspace_bytes"],
+                           "kernels": "k_bwd_chain<N,0>, k_bwd_chain<N,1>, k_bwd_chunk_bf<N>, "
+                                      "k_bwd_reduce_bc, k_bwd_reduce_h"}
     if args.sweep:
         sw = {}
         for n in (16, 64, 128, 256):
