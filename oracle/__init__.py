@@ -18,14 +18,20 @@ Contents
     fp64 gradients of the scan (reverse-mode automatic differentiation through a
     plain torch transcription of the recurrence), pinned by finite differences of
     ``scan_f64``.
+``ring.verify_ring_f64`` / ``ring.ring_rollback`` / ``ring.softplus_f64``
+    multi-round verify on a ring of the most recent per-token states (rounds,
+    rollback, and the optional fused step activation softplus(dt + bias)), built on
+    ``verify_f64``; pinned by ``tests/test_oracle_ring_pins.py`` against the scan
+    oracle over the accepted prefix and against ``numpy.logaddexp``.
 ``forms``
     Two further fp64 NumPy formulations of the same map (the quadratic
     "masked attention" form over the semiseparable matrix, and the four-step
     chunked decomposition), used only to pin the recurrence in tests.
 
-Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
+Parity status: every function here is pinned by ``tests/test_oracle_*pins.py``
 (closed forms, a hand-computed worked example, an IIR-filter library routine,
-brute force on tiny inputs, invariants).  No function is "parity unpinned".
+brute force on tiny inputs, finite differences, invariants).  No function is
+"parity unpinned".
 """
 from __future__ import annotations
 
