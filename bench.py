@@ -21,6 +21,9 @@ Printed: one JSON line with the contract fields plus
                 SSD replaces) on the same layer shape (4 x 2048 tokens, 5120
                 channels) at N=16 and N=128, and how many times faster the SSD
                 chunked scan (N=128) is than each
+  decode_K1     the verify step with one token (a decode step), GB/s
+  verify_ring   one round of the multi-round verify on a ring of 8 states (K=4, every
+                draft accepted, fused softplus step), GB/s
   backward      ssd_chunk_scan_bwd (all seven gradients, states recomputed) on the
                 L=2048 layer with upstream gradients for y and the final state:
                 tokens/s and algorithmic bytes / call time against 8 TB/s
@@ -169,8 +172,8 @@ def _timed(call, first, steps, stream, torch):
     return start.elapsed_time(end) / steps, wall
 
 
-def time_verify(steps, warmup, bd, inputs, torch):
-    v = inputs.make_workload("verify_b32_K4")
+def time_verify(steps, warmup, bd, inputs, torch, K=None):
+    v = inputs.make_workload("verify_b32_K4", **({} if K is None else {"K": K}))
     d = v.dims
     io_bytes = 2 if v.io == "bf16" else 4
     alg = verify_alg_bytes(d, io_bytes)
@@ -234,6 +237,35 @@ def time_backward(name, steps, warmup, bd, inputs, torch):
         call(i)
     mean_ms, _ = _timed(call, warmup, steps, stream, torch)
     return dict(dims=d, alg_bytes=alg, call_ms_mean=mean_ms, workspace_bytes=n)
+
+
+def time_ring(steps, warmup, bd, inputs, torch, K=4, R=8):
+    """Verify rounds on a state ring at the verify workload's layer shape (b=32, H=32,
+    P=128, N=128, G=8, bf16 I/O), every draft accepted (K states written per round), with
+    the fused step activation."""
+    w = inputs.WORKLOADS["verify_b32_K4"]
+    b, H, P, N, G = w["b"], w["H"], w["P"], w["N"], w["G"]
+    ri = inputs.make_verify_ring_inputs(b, K, H, P, N, G, R, 1, io="bf16", biased=True, seed=5)
+    r = ri.rounds[0]
+    dev = bd.to_device
+    A, D, bias = dev(ri.A), dev(ri.D), dev(ri.dt_bias)
+    x, dt, B, C = dev(r["x"]), dev(r["dt"]), dev(r["B"]), dev(r["C"])
+    acc = torch.full((b,), K, dtype=torch.int32, device="cuda")
+    ring = torch.zeros((b, R, H, P, N), dtype=torch.float32, device="cuda")
+    meta = torch.empty((b, 2), dtype=torch.int32, device="cuda")
+    bd.ssd_verify_ring_init(ring, meta, dev(ri.init_state))
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        bd.ssd_verify_ring(ring, meta, x, dt, A, B, C, D, acc, y, dt_bias=bias, stream=stream)
+
+    for i in range(warmup):
+        call(i)
+    mean_ms, _ = _timed(call, warmup, steps, stream, torch)
+    st = b * H * P * N * 4
+    alg = (1 + K) * st + 2 * b * K * H * P * 2 + b * K * H * 4 + 2 * b * K * G * N * 2 + 16 * H + 12 * b
+    return dict(call_ms_mean=mean_ms, alg_bytes=alg, gbs=alg / (mean_ms * 1e-3) / 1e9, R=R, K=K)
 
 
 def copy_bandwidth(torch, mib=1024, reps=10):
@@ -349,6 +381,15 @@ def main():
         out["verify"] = {"workload": "verify_b32_K4", "GB_per_s": rv["gbs"],
                          "hbm_frac": rv["gbs"] / HBM_PEAK_GBS, "call_ms_mean": rv["call_ms_mean"],
                          "alg_bytes": rv["alg_bytes"]}
+        r1 = time_verify(max(10, args.steps), 3, bd, inputs, torch, K=1)
+        out["decode_K1"] = {"workload": "verify_b32_K4 with K=1", "GB_per_s": r1["gbs"],
+                            "hbm_frac": r1["gbs"] / HBM_PEAK_GBS,
+                            "call_ms_mean": r1["call_ms_mean"], "alg_bytes": r1["alg_bytes"]}
+        rr = time_ring(max(10, args.steps), 3, bd, inputs, torch)
+        out["verify_ring"] = {"workload": "verify_b32_K4 layer, ring of 8, all 4 drafts accepted, "
+                                          "fused softplus step",
+                              "GB_per_s": rr["gbs"], "hbm_frac": rr["gbs"] / HBM_PEAK_GBS,
+                              "call_ms_mean": rr["call_ms_mean"], "alg_bytes": rr["alg_bytes"]}
         cmp = {}
         ssd_tps = d["b"] * d["L"] / (r["call_ms_mean"] * 1e-3)   # both timed by HIP events
         for n in (16, 128):

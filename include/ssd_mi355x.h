@@ -12,8 +12,10 @@
  *                       back the state at the accepted position ("如何将 Llama 变成
  *                       Mamba？研究人员推出新工作并提高推理速度", «推测解码»).
  *
- * and, as a comparison kernel on the same data, ssd_selective_scan_fwd: the
- * selective scan with one channel per head and a diagonal A that SSD replaces.
+ * and, built on them: ssd_chunk_scan_bwd (the gradients of the chunked scan),
+ * ssd_verify_ring (verify rounds on a device-resident ring of recent states, with
+ * rollback) and, as a comparison kernel on the same data, ssd_selective_scan_fwd
+ * (the selective scan with one channel per head and a diagonal A that SSD replaces).
  *
  * Both compute, per batch row b and head h (group g = h / (H/G)):
  *
@@ -23,7 +25,8 @@
  * ("另辟蹊径--Mamba介绍", «The Recurrent Representation»: the output reads the
  * updated state; «What is a State Space Model?»: D is a skip term; Bi-Mamba page,
  * «Preliminary: Mamba Series»: in SSD, A is one scalar per head.)  dt is taken as
- * given: no softplus, bias or clamp is applied inside the library.
+ * given: no softplus, bias or clamp is applied inside the library, except that
+ * ssd_verify_ring can apply softplus(dt + bias) when a bias vector is passed.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -201,6 +204,55 @@ ssd_status_t ssd_selective_scan_fwd(const void *x, const float *dt, const float 
                                     const void *C, const float *D, const float *init_state,
                                     void *y, float *final_state, int b, int L, int Dch, int N,
                                     int G, ssd_dtype_t io, void *hip_stream);
+
+/*
+ * Multi-round verify on a ring of states.
+ *
+ * A verifier that runs round after round keeps a ring buffer of the most recent
+ * states and, when a draft is rejected, restores the state of the last accepted
+ * position ("Llama 3与Mamba混合架构：加速推理的蒸馏技术解析", «状态管理机制»;
+ * "如何将 Llama 变成 Mamba？...", «推测解码»).  Here the ring lives in device memory:
+ *
+ *   ring  [b, R, H, P, N] fp32   R states per batch row
+ *   meta  [b][2]          int32  (head, depth): slot head holds the current state,
+ *                                and the depth slots behind it (head - 1, ... mod R)
+ *                                the states of the depth positions before it
+ *
+ * so a whole decode loop (rounds and rollbacks) runs without reading anything back to
+ * the host between calls.
+ *
+ * ssd_verify_ring_init: slot 0 of every row <- init_state (NULL = zeros), head and
+ * depth <- 0.  ring 16-byte aligned; R >= 2.
+ *
+ * ssd_verify_ring: one round of K draft tokens from the head state of every row, by
+ * the recurrence at the top of this file (y for all K positions).  With a =
+ * accept_len[b], the states after tokens 1 .. a are stored in slots head + 1 ..
+ * head + a (mod R); then head <- (head + a) mod R and depth <- min(depth + a, R - 1).
+ * R must exceed K (the head slot is never overwritten in a round).  dt_bias [H] fp32,
+ * or NULL: when given, the step used is softplus(dt + dt_bias[h]) = ln(1 + e^(dt +
+ * dt_bias[h])), the discretisation step computed inside the kernel ("另辟蹊径--Mamba
+ * 介绍", «Hardware-aware Algorithm»); when NULL, dt is taken as given.  x, dt, B, C, D,
+ * A, y as for ssd_verify_step.  accept_len outside [0, K] is clamped and reported
+ * through err_flag (NULL allowed) as in ssd_verify_step.  Supported: K in [1, 16], N
+ * in {16, 32, 64, 128, 256}.  The round is two launches on hip_stream.
+ *
+ * ssd_verify_ring_rollback: head <- head - steps[b] (mod R), depth <- depth -
+ * steps[b]; steps [b] int32 in [0, depth] (values outside are clamped and reported
+ * through err_flag).  The states ahead of the new head stay in the ring but are no
+ * longer reachable.
+ *
+ * All pointers are device pointers; outputs (ring, meta, y, err_flag) must not overlap
+ * the inputs or each other.  Errors as for the other entry points.
+ */
+ssd_status_t ssd_verify_ring_init(float *ring, int32_t *meta, const float *init_state, int b,
+                                  int R, int H, int P, int N, void *hip_stream);
+ssd_status_t ssd_verify_ring(float *ring, int32_t *meta, const void *x, const float *dt,
+                             const float *dt_bias, const float *A, const void *B, const void *C,
+                             const float *D, const int32_t *accept_len, void *y,
+                             int32_t *err_flag, int b, int K, int R, int H, int P, int N, int G,
+                             ssd_dtype_t io, void *hip_stream);
+ssd_status_t ssd_verify_ring_rollback(int32_t *meta, const int32_t *steps, int32_t *err_flag,
+                                      int b, int R, void *hip_stream);
 
 /*
  * Workspace size in bytes that ssd_chunk_scan_bwd needs for these dimensions (0 for

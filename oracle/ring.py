@@ -84,14 +84,18 @@ def verify_ring_f64(ring, meta, x, dt, A, B, C, D, accept_len, dt_bias=None):
     return y, ring_out, meta_out
 
 
-def ring_rollback(meta, steps, R):
+def ring_rollback(meta, steps, R, clamp=False):
     """Move every row's head back by steps[b] slots (0 <= steps[b] <= depth).
-    Returns meta'; raises on a step count outside that range."""
+    Returns meta'.  A step count outside that range raises, or with ``clamp`` is
+    clamped into it (the device's documented behaviour); then (meta', flag) is
+    returned, flag telling whether any count was out of range."""
     meta = np.asarray(meta, dtype=np.int64)
     steps = np.asarray(steps, dtype=np.int64)
-    if np.any(steps < 0) or np.any(steps > meta[:, 1]):
+    bad = (steps < 0) | (steps > meta[:, 1])
+    if np.any(bad) and not clamp:
         raise ValueError("rollback outside [0, depth]")
+    n = np.clip(steps, 0, meta[:, 1])
     out = meta.copy()
-    out[:, 0] = (meta[:, 0] - steps) % R
-    out[:, 1] = meta[:, 1] - steps
-    return out
+    out[:, 0] = (meta[:, 0] - n) % R
+    out[:, 1] = meta[:, 1] - n
+    return (out, bool(np.any(bad))) if clamp else out

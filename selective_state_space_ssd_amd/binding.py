@@ -31,6 +31,7 @@ STATUS_NAMES = {
 EXPORTED = ("ssd_chunk_scan_workspace_bytes", "ssd_chunk_scan_workspace_init",
             "ssd_chunk_scan_fwd", "ssd_verify_step", "ssd_selective_scan_fwd",
             "ssd_chunk_scan_bwd_workspace_bytes", "ssd_chunk_scan_bwd",
+            "ssd_verify_ring_init", "ssd_verify_ring", "ssd_verify_ring_rollback",
             "ssd_status_string", "ssd_version")
 
 _lib = None
@@ -66,6 +67,12 @@ def lib() -> ctypes.CDLL:
         L.ssd_chunk_scan_bwd_workspace_bytes.restype = sz
         L.ssd_chunk_scan_bwd.argtypes = [vp] * 16 + [i32] * 6 + [i32, vp, sz, vp]
         L.ssd_chunk_scan_bwd.restype = i32
+        L.ssd_verify_ring_init.argtypes = [vp, vp, vp] + [i32] * 5 + [vp]
+        L.ssd_verify_ring_init.restype = i32
+        L.ssd_verify_ring.argtypes = [vp] * 12 + [i32] * 7 + [i32, vp]
+        L.ssd_verify_ring.restype = i32
+        L.ssd_verify_ring_rollback.argtypes = [vp, vp, vp, i32, i32, vp]
+        L.ssd_verify_ring_rollback.restype = i32
         L.ssd_status_string.argtypes = [i32]
         L.ssd_status_string.restype = ctypes.c_char_p
         L.ssd_version.argtypes = []
@@ -215,6 +222,47 @@ def ssd_chunk_scan_bwd(x, dt, A, B, C, D, init_state, dy, d_final, dx, ddt, dA, 
         _stream(stream))
     if st != 0:
         raise SSDError(st, "ssd_chunk_scan_bwd")
+
+
+def ssd_verify_ring_init(ring, meta, init_state=None, stream=None) -> None:
+    """Slot 0 of every row of ``ring`` [b,R,H,P,N] float32 <- init_state [b,H,P,N]
+    (None = zeros); ``meta`` [b,2] int32 <- (0, 0)."""
+    b, R, H, P, N = ring.shape
+    st = lib().ssd_verify_ring_init(_ptr(ring, "ring", torch.float32), _ptr(meta, "meta", torch.int32),
+                                    _ptr(init_state, "init_state", torch.float32), b, R, H, P, N,
+                                    _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_verify_ring_init")
+
+
+def ssd_verify_ring(ring, meta, x, dt, A, B, C, D, accept_len, y, dt_bias=None, err_flag=None,
+                    stream=None) -> None:
+    """Enqueue one verify round on the ring (see include/ssd_mi355x.h)."""
+    b, R = ring.shape[:2]
+    _, K, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    io = _io_code(x)
+    f32 = torch.float32
+    st = lib().ssd_verify_ring(
+        _ptr(ring, "ring", f32), _ptr(meta, "meta", torch.int32), _ptr(x, "x", x.dtype),
+        _ptr(dt, "dt", f32), _ptr(dt_bias, "dt_bias", f32), _ptr(A, "A", f32),
+        _ptr(B, "B", x.dtype), _ptr(C, "C", x.dtype), _ptr(D, "D", f32),
+        _ptr(accept_len, "accept_len", torch.int32), _ptr(y, "y", x.dtype),
+        _ptr(err_flag, "err_flag", torch.int32), b, K, R, H, P, N, G, io, _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_verify_ring")
+
+
+def ssd_verify_ring_rollback(meta, steps, err_flag=None, R=None, stream=None) -> None:
+    """Move every row's ring head back by steps[b] (int32 [b]) slots; R is the ring
+    length."""
+    b = meta.shape[0]
+    st = lib().ssd_verify_ring_rollback(_ptr(meta, "meta", torch.int32),
+                                        _ptr(steps, "steps", torch.int32),
+                                        _ptr(err_flag, "err_flag", torch.int32), b, R,
+                                        _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_verify_ring_rollback")
 
 
 # ------------------------------------------------------------ allocating wrappers

@@ -175,6 +175,84 @@ ssd_status_t ssd_verify_step(const float *state_in, const void *x, const float *
     return SSD_OK;
 }
 
+ssd_status_t ssd_verify_ring_init(float *ring, int32_t *meta, const float *init_state, int b,
+                                  int R, int H, int P, int N, void *hip_stream) {
+    if (b < 0 || R < 2 || H <= 0 || P <= 0 || N <= 0) return SSD_ERR_BAD_DIM;
+    if (b > 65535) return SSD_ERR_UNSUPPORTED;
+    if (b == 0) return SSD_OK;
+    if (!ring || !meta) return SSD_ERR_NULL_ARG;
+    if (!aligned(ring, 16) || !aligned(init_state, 4) || !aligned(meta, 4)) return SSD_ERR_ALIGN;
+    const size_t slot = size_t(H) * P * N;
+    const Range rr(ring, size_t(b) * R * slot * 4), ri(init_state, size_t(b) * slot * 4);
+    const Range rm(meta, size_t(b) * 8);
+    if (rr.overlaps(ri) || rr.overlaps(rm) || rm.overlaps(ri)) return SSD_ERR_ALIAS;
+    if (ssd::launch_ring_init(ring, meta, init_state, b, R, slot,
+                              static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+        return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
+ssd_status_t ssd_verify_ring(float *ring, int32_t *meta, const void *x, const float *dt,
+                             const float *dt_bias, const float *A, const void *B, const void *C,
+                             const float *D, const int32_t *accept_len, void *y,
+                             int32_t *err_flag, int b, int K, int R, int H, int P, int N, int G,
+                             ssd_dtype_t io, void *hip_stream) {
+    if (io != SSD_DTYPE_F32 && io != SSD_DTYPE_BF16) return SSD_ERR_UNSUPPORTED;
+    if (b < 0 || K <= 0 || R <= K || H <= 0 || P <= 0 || N <= 0 || G <= 0) return SSD_ERR_BAD_DIM;
+    if (H % G != 0) return SSD_ERR_GROUPS;
+    if (K > 16 || !ssd::verify_supported_n(N) || H > 65535 || b > 65535)
+        return SSD_ERR_UNSUPPORTED;
+    if (b == 0) return SSD_OK;
+    if (!ring || !meta || !x || !dt || !A || !B || !C || !D || !accept_len || !y)
+        return SSD_ERR_NULL_ARG;
+    const bool bf16 = io == SSD_DTYPE_BF16;
+    const size_t esz = bf16 ? 2 : 4;
+    if (!aligned(ring, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(x, esz) ||
+        !aligned(y, esz) || !aligned(dt, 4) || !aligned(dt_bias, 4) || !aligned(A, 4) ||
+        !aligned(D, 4) || !aligned(accept_len, 4) || !aligned(err_flag, 4) || !aligned(meta, 4))
+        return SSD_ERR_ALIGN;
+    const Range rring(ring, size_t(b) * R * H * P * N * 4), rmeta(meta, size_t(b) * 8);
+    const Range rx(x, size_t(b) * K * H * P * esz), ry(y, size_t(b) * K * H * P * esz);
+    const Range rB(B, size_t(b) * K * G * N * esz), rC(C, size_t(b) * K * G * N * esz);
+    const Range rdt(dt, size_t(b) * K * H * 4), rbias(dt_bias, size_t(H) * 4);
+    const Range rA(A, size_t(H) * 4), rD(D, size_t(H) * 4);
+    const Range racc(accept_len, size_t(b) * 4), rerr(err_flag, 4);
+    const Range ins[] = {rx, rB, rC, rdt, rbias, rA, rD, racc};
+    const Range outs[] = {rring, rmeta, ry, rerr};
+    for (int i = 0; i < 4; ++i) {
+        for (const Range &in : ins)
+            if (outs[i].overlaps(in)) return SSD_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (outs[i].overlaps(outs[j])) return SSD_ERR_ALIAS;
+    }
+    ssd::VerifyArgs a;
+    a.state_in = nullptr; a.x = x; a.dt = dt; a.A = A; a.B = B; a.C = C; a.D = D;
+    a.accept_len = accept_len; a.y = y; a.state_out = nullptr; a.states_all = nullptr;
+    a.err_flag = err_flag;
+    a.b = b; a.K = K; a.H = H; a.P = P; a.N = N; a.G = G;
+    a.bf16 = bf16;
+    a.ring = ring; a.meta = meta; a.R = R; a.dt_bias = dt_bias;
+    const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (ssd::launch_verify(a, stream) != hipSuccess) return SSD_ERR_HIP;
+    if (ssd::launch_ring_advance(meta, accept_len, b, K, R, stream) != hipSuccess)
+        return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
+ssd_status_t ssd_verify_ring_rollback(int32_t *meta, const int32_t *steps, int32_t *err_flag,
+                                      int b, int R, void *hip_stream) {
+    if (b < 0 || R < 2) return SSD_ERR_BAD_DIM;
+    if (b == 0) return SSD_OK;
+    if (!meta || !steps) return SSD_ERR_NULL_ARG;
+    if (!aligned(meta, 4) || !aligned(steps, 4) || !aligned(err_flag, 4)) return SSD_ERR_ALIGN;
+    const Range rm(meta, size_t(b) * 8), rs(steps, size_t(b) * 4), re(err_flag, 4);
+    if (rm.overlaps(rs) || rm.overlaps(re) || rs.overlaps(re)) return SSD_ERR_ALIAS;
+    if (ssd::launch_ring_rollback(meta, steps, err_flag, b, R,
+                                  static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+        return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
 ssd_status_t ssd_selective_scan_fwd(const void *x, const float *dt, const float *A, const void *B,
                                     const void *C, const float *D, const float *init_state,
                                     void *y, float *final_state, int b, int L, int Dch, int N,

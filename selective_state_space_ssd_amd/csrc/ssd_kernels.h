@@ -25,10 +25,22 @@ struct VerifyArgs {
     int32_t *err_flag;
     int b, K, H, P, N, G;
     bool bf16;
+    // multi-round mode: ring [b, R, H, P, N] fp32 and meta [b][2] = (head, depth);
+    // state_in / state_out / states_all unused when ring is set
+    float *ring = nullptr;
+    const int32_t *meta = nullptr;
+    int R = 0;
+    const float *dt_bias = nullptr;   // nullable: step = softplus(dt + dt_bias[h])
 };
 
 bool verify_supported_n(int N);
 hipError_t launch_verify(const VerifyArgs &a, hipStream_t stream);
+hipError_t launch_ring_init(float *ring, int32_t *meta, const float *init, int b, int R,
+                            size_t slot, hipStream_t stream);
+hipError_t launch_ring_advance(int32_t *meta, const int32_t *accept_len, int b, int K, int R,
+                               hipStream_t stream);
+hipError_t launch_ring_rollback(int32_t *meta, const int32_t *steps, int32_t *err_flag, int b,
+                                int R, hipStream_t stream);
 
 // selective scan, one channel per head, diagonal A (ssd_selective_scan.hip)
 struct SelectiveArgs {

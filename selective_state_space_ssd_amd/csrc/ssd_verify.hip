@@ -13,6 +13,8 @@
 // one load instruction of the wave covers whole 128-byte row segments; the
 // reduction y = C . h over N is an in-lane sum followed by DPP lane moves.  B and C
 // of the K tokens are shared by every row of a block and are staged once into LDS.
+#include <algorithm>
+
 #include "ssd_device.h"
 #include "ssd_kernels.h"
 
@@ -55,15 +57,25 @@ __device__ __forceinline__ float4 load4(const IO *p) {
     }
 }
 
+// Step activation fused into the kernel: softplus(v) = ln(1 + e^v), evaluated as
+// max(v, 0) + ln(1 + e^{-|v|}) so that it cannot overflow.
+__device__ __forceinline__ float softplus(float v) {
+    return fmaxf(v, 0.f) + log1pf(expf(-fabsf(v)));
+}
+
 // B and C of the K tokens (group g) are staged once per block into LDS as fp32
 // ([K][N] each).  KM >= K bounds the per-token registers (x and dt of every token).
-template <typename IO, int N, int KM>
+// RING: the state comes from slot meta[2 b] of the row's ring [R][H][P][N] and the
+// states after tokens 1 .. a go to the next a slots (mod R); state_out and states_all
+// are unused.  dt_bias (nullable): the step is softplus(dt + dt_bias[h]).
+template <typename IO, int N, int KM, bool RING>
 __global__ __launch_bounds__(256) void k_verify(
     const float *state_in, const IO *__restrict__ x, const float *__restrict__ dt,
     const float *__restrict__ A, const IO *__restrict__ B, const IO *__restrict__ C,
     const float *__restrict__ D, const int32_t *__restrict__ accept_len, IO *__restrict__ y,
     float *state_out, float *__restrict__ states_all, int32_t *err_flag, int K, int H, int P,
-    int G) {
+    int G, float *ring, const int32_t *__restrict__ meta, int R,
+    const float *__restrict__ dt_bias) {
     using S = VerifyShape<N>;
     extern __shared__ __align__(16) float sbc[];   // [K][N] B, then [K][N] C
     float *sB = sbc, *sC = sbc + K * N;
@@ -75,6 +87,18 @@ __global__ __launch_bounds__(256) void k_verify(
     const bool valid = p < P;
     const size_t bh = size_t(bi) * H + h;
     const size_t row = (bh * P + (valid ? p : 0)) * N;
+    // ring mode: the head slot of this row (reduced into [0, R) whatever meta holds,
+    // so no access leaves the ring; an out-of-range head is reported), and the ring
+    // of this (b) at head h
+    int head = 0;
+    if constexpr (RING) {
+        const int raw = meta[2 * bi];
+        head = ((raw % R) + R) % R;
+        if (head != raw && err_flag && blockIdx.x == 0 && h == 0 && threadIdx.x == 0) *err_flag = 1;
+    }
+    const size_t slot_stride = size_t(H) * P * N;
+    float *ring_bh = RING ? ring + size_t(bi) * R * slot_stride + size_t(h) * P * N : nullptr;
+    const float *src = RING ? ring_bh + size_t(head) * slot_stride : state_in + bh * P * N;
 
     // All global loads are issued up front, without branches around them (range-
     // checked buffer views read 0 past their end), in the order they are needed: B
@@ -127,7 +151,7 @@ __global__ __launch_bounds__(256) void k_verify(
     // the state streams through once: non-temporal loads and stores
     float4 s[S::J];
     {
-        const __amdgpu_buffer_rsrc_t sres = buffer_rsrc(state_in + bh * P * N, uint32_t(P) * N * 4u);
+        const __amdgpu_buffer_rsrc_t sres = buffer_rsrc(src, uint32_t(P) * N * 4u);
 #pragma unroll
         for (int j = 0; j < S::J; ++j) {
             const int n = j * 4 * S::LR + lr * 4;
@@ -157,7 +181,12 @@ __global__ __launch_bounds__(256) void k_verify(
         if (err_flag && blockIdx.x == 0 && h == 0 && threadIdx.x == 0) *err_flag = 1;
         a = a < 0 ? 0 : K;
     }
-    if (a == 0 && valid) {
+    if (dt_bias) {
+        const float bias = dt_bias[h];
+#pragma unroll
+        for (int k = 0; k < kMaxK; ++k) dtr[k] = softplus(dtr[k] + bias);
+    }
+    if (!RING && a == 0 && valid) {
 #pragma unroll
         for (int j = 0; j < S::J; ++j)
             __builtin_nontemporal_store(f32x4{s[j].x, s[j].y, s[j].z, s[j].w},
@@ -189,7 +218,16 @@ __global__ __launch_bounds__(256) void k_verify(
         part = row_sum<S::LR>(part);
         if (valid && lr == 0)
             y[xy0 + (uint32_t(k) * tok_stride + uint32_t(p))] = from_f32<IO>(part + Dh * xk);
-        if (valid) {
+        if (RING && valid && k < a) {
+            int slot = head + k + 1;
+            slot = slot >= R ? slot - R : slot;
+            float *dst = ring_bh + size_t(slot) * slot_stride + size_t(p) * N;
+#pragma unroll
+            for (int j = 0; j < S::J; ++j)
+                __builtin_nontemporal_store(f32x4{s[j].x, s[j].y, s[j].z, s[j].w},
+                                            reinterpret_cast<f32x4 *>(dst + j * 4 * S::LR + lr * 4));
+        }
+        if (!RING && valid) {
             if (states_all) {
                 float *dst = states_all + ((tk * H + h) * P + p) * N;
 #pragma unroll
@@ -212,10 +250,18 @@ static hipError_t launch_verify_nk(const VerifyArgs &a, hipStream_t stream) {
     using S = VerifyShape<N>;
     dim3 grid((a.P + S::RB - 1) / S::RB, a.H, a.b);
     const size_t lds = size_t(2) * a.K * N * sizeof(float);
-    hipLaunchKernelGGL((k_verify<IO, N, KM>), grid, dim3(256), lds, stream, a.state_in,
-                       static_cast<const IO *>(a.x), a.dt, a.A, static_cast<const IO *>(a.B),
-                       static_cast<const IO *>(a.C), a.D, a.accept_len, static_cast<IO *>(a.y),
-                       a.state_out, a.states_all, a.err_flag, a.K, a.H, a.P, a.G);
+    if (a.ring)
+        hipLaunchKernelGGL((k_verify<IO, N, KM, true>), grid, dim3(256), lds, stream, a.state_in,
+                           static_cast<const IO *>(a.x), a.dt, a.A, static_cast<const IO *>(a.B),
+                           static_cast<const IO *>(a.C), a.D, a.accept_len, static_cast<IO *>(a.y),
+                           a.state_out, a.states_all, a.err_flag, a.K, a.H, a.P, a.G, a.ring,
+                           a.meta, a.R, a.dt_bias);
+    else
+        hipLaunchKernelGGL((k_verify<IO, N, KM, false>), grid, dim3(256), lds, stream, a.state_in,
+                           static_cast<const IO *>(a.x), a.dt, a.A, static_cast<const IO *>(a.B),
+                           static_cast<const IO *>(a.C), a.D, a.accept_len, static_cast<IO *>(a.y),
+                           a.state_out, a.states_all, a.err_flag, a.K, a.H, a.P, a.G, nullptr,
+                           nullptr, 0, a.dt_bias);
     return hipGetLastError();
 }
 
@@ -237,6 +283,74 @@ static hipError_t launch_verify_io(const VerifyArgs &a, hipStream_t stream) {
         case 256: return launch_verify_n<IO, 256>(a, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+// ---------------------------------------------------------------- state ring
+// Slot 0 of every row <- init_state (or zeros); head and depth <- 0.
+__global__ __launch_bounds__(256) void k_ring_init(float *__restrict__ ring, int32_t *__restrict__ meta,
+                                                   const float *__restrict__ init, int R,
+                                                   size_t slot) {
+    const int bi = blockIdx.y;
+    for (size_t e = size_t(blockIdx.x) * 256 + threadIdx.x; e < slot; e += size_t(gridDim.x) * 256)
+        ring[size_t(bi) * R * slot + e] = init ? init[size_t(bi) * slot + e] : 0.f;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        meta[2 * bi] = 0;
+        meta[2 * bi + 1] = 0;
+    }
+}
+
+// After a round: head <- (head + a) mod R, depth <- min(depth + a, R - 1), with a the
+// accepted count clamped into [0, K] as the verify kernel clamped it.
+__global__ __launch_bounds__(256) void k_ring_advance(int32_t *__restrict__ meta,
+                                                      const int32_t *__restrict__ accept_len,
+                                                      int b, int K, int R) {
+    const int bi = blockIdx.x * 256 + threadIdx.x;
+    if (bi >= b) return;
+    int a = accept_len[bi];
+    a = a < 0 ? 0 : (a > K ? K : a);
+    const int head = ((meta[2 * bi] % R) + R) % R;
+    const int depth = min(max(meta[2 * bi + 1], 0), R - 1);
+    meta[2 * bi] = (head + a) % R;
+    meta[2 * bi + 1] = min(depth + a, R - 1);
+}
+
+// head <- head - n (mod R), depth <- depth - n; n outside [0, depth] is clamped into
+// it and reported through err_flag.
+__global__ __launch_bounds__(256) void k_ring_rollback(int32_t *__restrict__ meta,
+                                                       const int32_t *__restrict__ steps,
+                                                       int32_t *err_flag, int b, int R) {
+    const int bi = blockIdx.x * 256 + threadIdx.x;
+    if (bi >= b) return;
+    const int head = ((meta[2 * bi] % R) + R) % R;
+    const int depth = min(max(meta[2 * bi + 1], 0), R - 1);
+    int n = steps[bi];
+    if (n < 0 || n > depth) {
+        if (err_flag) *err_flag = 1;
+        n = n < 0 ? 0 : depth;
+    }
+    meta[2 * bi] = ((head - n) % R + R) % R;
+    meta[2 * bi + 1] = depth - n;
+}
+
+hipError_t launch_ring_init(float *ring, int32_t *meta, const float *init, int b, int R,
+                            size_t slot, hipStream_t stream) {
+    const unsigned gx = unsigned(std::min<size_t>((slot + 255) / 256, 1024));
+    hipLaunchKernelGGL(k_ring_init, dim3(gx, b), dim3(256), 0, stream, ring, meta, init, R, slot);
+    return hipGetLastError();
+}
+
+hipError_t launch_ring_advance(int32_t *meta, const int32_t *accept_len, int b, int K, int R,
+                               hipStream_t stream) {
+    hipLaunchKernelGGL(k_ring_advance, dim3((b + 255) / 256), dim3(256), 0, stream, meta,
+                       accept_len, b, K, R);
+    return hipGetLastError();
+}
+
+hipError_t launch_ring_rollback(int32_t *meta, const int32_t *steps, int32_t *err_flag, int b,
+                                int R, hipStream_t stream) {
+    hipLaunchKernelGGL(k_ring_rollback, dim3((b + 255) / 256), dim3(256), 0, stream, meta, steps,
+                       err_flag, b, R);
+    return hipGetLastError();
 }
 
 bool verify_supported_n(int N) {

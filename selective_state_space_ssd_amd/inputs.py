@@ -22,6 +22,11 @@ Recipe (the same for tests and for the benchmark):
 * accept_len ~ U{0, ..., K}
 * Upstream gradients of the chunked scan (its backward pass), from a generator of
   their own seed: dy ~ N(0, 1) stored like x, then d_final ~ N(0, 1) in float32.
+* Multi-round verify on a state ring: A, D, init_state as above, then (with a fused
+  step activation) dt_bias = softplus^-1(0.01) + N(0, 0.5^2) per head; then per
+  round x, dt, B, C, accept_len ~ U{0..K}, a rollback request ~ U{0..3} and whether
+  it is made (probability 0.3).  dt follows the recipe above without the activation,
+  and is the raw pre-activation value z ~ N(0, 1) with it.
 * Storage: dt, A, D and every state in float32.  x, B, C are float32 for the
   fp32 workload and bfloat16 (float64 -> float32 -> bfloat16, both roundings to
   nearest-even) for the bf16 workloads.
@@ -240,6 +245,44 @@ def make_upstream_grads(inp: ScanInputs, seed: int, final: bool = True):
     d_final = (_store(rng.standard_normal((d["b"], d["H"], d["P"], d["N"])), "f32")
                if final else None)
     return dy, d_final
+
+
+@dataclasses.dataclass
+class RingInputs:
+    A: Tensor
+    D: Tensor
+    init_state: Tensor
+    dt_bias: Optional[Tensor]
+    rounds: list          # per round: dict(x, dt, B, C, accept_len, rollback)
+    R: int
+    io: str
+
+
+def make_verify_ring_inputs(b, K, H, P, N, G, R, rounds, io="bf16", biased=False,
+                            seed=0) -> RingInputs:
+    """Draw a multi-round verify problem (see the module docstring for the recipe).
+    ``rollback`` of a round is None or int32 [b] step requests (which may exceed what
+    the ring can undo)."""
+    if H % G:
+        raise ValueError("H must be a multiple of G")
+    rng = np.random.default_rng(seed)
+    A = -np.exp(rng.uniform(0.0, math.log(16.0), H))
+    D = rng.standard_normal(H)
+    init = 0.1 * rng.standard_normal((b, H, P, N))
+    bias = _store(DT_BIAS + 0.5 * rng.standard_normal(H), "f32") if biased else None
+    out = []
+    for _ in range(rounds):
+        x = rng.standard_normal((b, K, H, P))
+        dt = rng.standard_normal((b, K, H)) if biased else _dt(rng, (b, K, H))
+        Bv = rng.standard_normal((b, K, G, N))
+        Cv = rng.standard_normal((b, K, G, N))
+        acc = rng.integers(0, K + 1, size=b).astype(np.int32)
+        steps = rng.integers(0, 4, size=b).astype(np.int32)
+        made = rng.uniform() < 0.3
+        out.append(dict(x=_store(x, io), dt=_store(dt, "f32"), B=_store(Bv, io), C=_store(Cv, io),
+                        accept_len=acc, rollback=steps if made else None))
+    return RingInputs(A=_store(A, "f32"), D=_store(D, "f32"), init_state=_store(init, "f32"),
+                      dt_bias=bias, rounds=out, R=R, io=io)
 
 
 def make_workload(name: str, **override):

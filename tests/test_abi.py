@@ -240,3 +240,50 @@ def test_bwd_workspace_and_alias_checks(lib):
     assert bwd_call(lib, {"ws": addr(1)}) == ALIAS                  # workspace on x
     assert bwd_call(lib, {"dinit": addr(16), "dfin": addr(16)}) == ALIAS
     assert bwd_call(lib, {"dD": addr(10)}) == ALIAS                 # dD on dA
+
+
+def ring_call(lib, over=None, dims=None, io=1):
+    p = dict(ring=addr(1), meta=addr(2), x=addr(3), dt=addr(4), bias=None, A=addr(5), B=addr(6),
+             C=addr(7), D=addr(8), acc=addr(9), y=addr(10), err=None)
+    p.update(over or {})
+    d = dict(b=2, K=4, R=6, H=4, P=16, N=32, G=2)
+    d.update(dims or {})
+    return lib.ssd_verify_ring(p["ring"], p["meta"], p["x"], p["dt"], p["bias"], p["A"], p["B"],
+                               p["C"], p["D"], p["acc"], p["y"], p["err"], d["b"], d["K"], d["R"],
+                               d["H"], d["P"], d["N"], d["G"], io, None)
+
+
+@pytest.mark.parametrize("name", ["ring", "meta", "x", "dt", "A", "B", "C", "D", "acc", "y"])
+def test_ring_null_required_pointer(lib, name):
+    assert ring_call(lib, {name: None}) == NULL
+
+
+@pytest.mark.parametrize("dims,code", [
+    (dict(b=-1), DIM), (dict(K=0), DIM), (dict(R=4), DIM), (dict(R=3), DIM), (dict(H=0), DIM),
+    (dict(G=3), GROUPS), (dict(K=17, R=20), UNSUP), (dict(N=48), UNSUP),
+])
+def test_ring_bad_dims(lib, dims, code):
+    assert ring_call(lib, dims=dims) == code
+
+
+def test_ring_alignment_and_alias(lib):
+    assert ring_call(lib, {"ring": addr(1, 8)}) == ALIGN
+    assert ring_call(lib, {"bias": addr(11, 2)}) == ALIGN
+    assert ring_call(lib, {"meta": addr(2, 2)}) == ALIGN
+    assert ring_call(lib, {"y": addr(3)}) == ALIAS                   # y on x
+    assert ring_call(lib, {"meta": addr(1, 16)}) == ALIAS            # meta inside the ring
+    assert ring_call(lib, {"ring": addr(5)}) == ALIAS                # ring on A
+    assert ring_call(lib, {"err": addr(9)}) == ALIAS                 # flag on accept_len
+    assert ring_call(lib, {"bias": addr(10)}) == ALIAS               # y on dt_bias
+
+
+def test_ring_init_and_rollback_checks(lib):
+    assert lib.ssd_verify_ring_init(addr(1), addr(2), None, 2, 1, 4, 16, 32, None) == DIM
+    assert lib.ssd_verify_ring_init(None, addr(2), None, 2, 4, 4, 16, 32, None) == NULL
+    assert lib.ssd_verify_ring_init(addr(1, 4), addr(2), None, 2, 4, 4, 16, 32, None) == ALIGN
+    assert lib.ssd_verify_ring_init(addr(1), addr(1, 64), None, 2, 4, 4, 16, 32, None) == ALIAS
+    assert lib.ssd_verify_ring_init(None, None, None, 0, 4, 4, 16, 32, None) == OK
+    assert lib.ssd_verify_ring_rollback(addr(1), addr(2), None, 2, 1, None) == DIM
+    assert lib.ssd_verify_ring_rollback(None, addr(2), None, 2, 4, None) == NULL
+    assert lib.ssd_verify_ring_rollback(addr(1), addr(1), None, 2, 4, None) == ALIAS
+    assert lib.ssd_verify_ring_rollback(addr(1, 2), addr(2), None, 2, 4, None) == ALIGN

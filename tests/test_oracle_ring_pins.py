@@ -135,11 +135,20 @@ def test_rejects_invalid_calls():
         ring.ring_rollback(meta, [1, 0], 4)
 
 
+def test_clamped_rollback():
+    meta = np.array([[3, 2], [0, 4], [1, 0]])
+    ok, flag = ring.ring_rollback(meta, [1, 4, 0], 5, clamp=True)
+    assert not flag and np.array_equal(ok, ring.ring_rollback(meta, [1, 4, 0], 5))
+    out, flag = ring.ring_rollback(meta, [5, -1, 2], 5, clamp=True)
+    assert flag
+    assert np.array_equal(out, [[1, 0], [0, 4], [1, 0]])   # back to the oldest state
+
+
 MUTANTS = {
     "slot_off_by_one": ("(head[bi] + k + 1) % R", "(head[bi] + k) % R"),
     "head_not_advanced": ("meta_out[bi, 0] = (head[bi] + a) % R", "meta_out[bi, 0] = head[bi] % R"),
     "depth_not_saturated": ("min(meta[bi, 1] + a, R - 1)", "meta[bi, 1] + a"),
-    "rollback_forward": ("(meta[:, 0] - steps) % R", "(meta[:, 0] + steps) % R"),
+    "rollback_forward": ("(meta[:, 0] - n) % R", "(meta[:, 0] + n) % R"),
     "softplus_no_log1p": ("np.log1p(np.exp(-np.abs(v)))", "np.exp(-np.abs(v))"),
 }
 
