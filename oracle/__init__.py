@@ -23,6 +23,11 @@ Contents
     rollback, and the optional fused step activation softplus(dt + bias)), built on
     ``verify_f64``; pinned by ``tests/test_oracle_ring_pins.py`` against the scan
     oracle over the accepted prefix and against ``numpy.logaddexp``.
+``cp.total_decay_f64`` / ``cp.combine_f64`` / ``cp.apply_entering_state_f64``
+    the per-device pieces of the sequence-parallel scan (total decay of a slice,
+    entering states folded from the slices' pairs, correction of a slice scanned
+    from zero); pinned by ``tests/test_oracle_cp_pins.py`` against the scan oracle of
+    the whole sequence.
 ``forms``
     Two further fp64 NumPy formulations of the same map (the quadratic
     "masked attention" form over the semiseparable matrix, and the four-step
