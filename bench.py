@@ -24,6 +24,11 @@ Printed: one JSON line with the contract fields plus
   decode_K1     the verify step with one token (a decode step), GB/s
   verify_ring   one round of the multi-round verify on a ring of 8 states (K=4, every
                 draft accepted, fused softplus step), GB/s
+  sequence_parallel
+                one device's share of the L=16k layer split into 8 slices: the slice's
+                scan from zero, its total decay, the combine of 8 pairs and the
+                correction by the entering state (the exchange between devices is not
+                measured: this build runs on one GPU)
   backward      ssd_chunk_scan_bwd (all seven gradients, states recomputed) on the
                 L=2048 layer with upstream gradients for y and the final state:
                 tokens/s and algorithmic bytes / call time against 8 TB/s
@@ -268,6 +273,43 @@ def time_ring(steps, warmup, bd, inputs, torch, K=4, R=8):
     return dict(call_ms_mean=mean_ms, alg_bytes=alg, gbs=alg / (mean_ms * 1e-3) / 1e9, R=R, K=K)
 
 
+def time_seqpar(steps, warmup, bd, inputs, torch, n=8):
+    """One device's share of the L=16k layer split into n slices (sequence parallel):
+    the slice's scan from a zero state, its total decay, the combine of n pairs and the
+    correction of the slice by its entering state, each timed with HIP events."""
+    inp = inputs.make_workload("mamba2_2p7b_L16k")
+    d = inp.dims
+    b, L, H, P, N = d["b"], d["L"], d["H"], d["P"], d["N"]
+    Ls = L // n
+    dev = bd.to_device
+    x, dt, A, B, C, D = (dev(getattr(inp, k)) for k in ("x", "dt", "A", "B", "C", "D"))
+    xs, dts, Bs, Cs = (t[:, :Ls].contiguous() for t in (x, dt, B, C))
+    ys = torch.empty_like(xs)
+    fs = torch.empty((b, H, P, N), dtype=torch.float32, device="cuda")
+    ws = bd.chunk_scan_workspace(xs, Bs, d["Q"])
+    alpha = torch.empty((n, b, H), dtype=torch.float32, device="cuda")
+    S = torch.randn((n, b, H, P, N), dtype=torch.float32, device="cuda")
+    h_in = torch.empty_like(S)
+    init = dev(inp.init_state)
+    stream = torch.cuda.current_stream()
+    calls = {
+        "scan_slice": lambda i: bd.ssd_chunk_scan_fwd(xs, dts, A, Bs, Cs, D, None, ys, fs, d["Q"],
+                                                      ws, stream),
+        "total_decay": lambda i: bd.ssd_seq_total_decay(dts, A, alpha[0], stream),
+        "combine": lambda i: bd.ssd_seq_combine(alpha, S, init, h_in, stream),
+        "apply_state": lambda i: bd.ssd_seq_apply_state(ys, fs, dts, A, Cs, h_in[1], stream),
+    }
+    out = {}
+    for k, call in calls.items():
+        for i in range(warmup):
+            call(i)
+        out[k + "_us"] = _timed(call, warmup, steps, stream, torch)[0] * 1e3
+    out["share_us"] = sum(out.values())
+    out["slice_tokens"] = b * Ls
+    out["exchange_bytes_per_device"] = b * H * (P * N + 1) * 4
+    return out
+
+
 def copy_bandwidth(torch, mib=1024, reps=10):
     """Read+write GB/s of a plain elementwise kernel over a buffer far larger than the
     caches: the practical HBM ceiling beside the 8 TB/s specification."""
@@ -400,6 +442,10 @@ def main():
                             "call_ms_mean": rs["call_ms_mean"],
                             "ssd_N128_speedup": ssd_tps / tps}
         out["selective_scan_comparison"] = cmp
+        sp = time_seqpar(max(10, args.steps), 3, bd, inputs, torch)
+        sp["workload"] = "mamba2_2p7b_L16k in 8 slices of 2048 tokens, one slice's share"
+        sp["monolithic_L16k_per_slice_us"] = r2["call_ms_mean"] * 1e3 / 8
+        out["sequence_parallel"] = sp
         rb = time_backward(args.workload, max(5, args.steps // 3), 2, bd, inputs, torch)
         db = rb["dims"]
         ab = rb["alg_bytes"] / (rb["call_ms_mean"] * 1e-3) / 1e9

@@ -14,7 +14,7 @@
  *
  * and, built on them: ssd_chunk_scan_bwd (the gradients of the chunked scan),
  * ssd_verify_ring (verify rounds on a device-resident ring of recent states, with
- * rollback) and, as a comparison kernel on the same data, ssd_selective_scan_fwd
+ * rollback), the per-device pieces of the sequence-parallel scan (ssd_seq_*) and, as a comparison kernel on the same data, ssd_selective_scan_fwd
  * (the selective scan with one channel per head and a diagonal A that SSD replaces).
  *
  * Both compute, per batch row b and head h (group g = h / (H/G)):
@@ -253,6 +253,41 @@ ssd_status_t ssd_verify_ring(float *ring, int32_t *meta, const void *x, const fl
                              ssd_dtype_t io, void *hip_stream);
 ssd_status_t ssd_verify_ring_rollback(int32_t *meta, const int32_t *steps, int32_t *err_flag,
                                       int b, int R, void *hip_stream);
+
+/*
+ * Sequence (context) parallelism: the per-device pieces.
+ *
+ * A long sequence is split into n slices, one per device (Mamba-2 article, «序列并行»):
+ * each device scans its slice from a zero state with ssd_chunk_scan_fwd; the devices
+ * exchange (alpha, S) = (total decay of the slice, its final state); each device folds
+ * its predecessors' pairs into the state h_in entering its slice and corrects its
+ * slice.  The pairs compose associatively because the state passing is linear (the
+ * scan over chunks of «SSD 算法：分块和形态传递», step 3, run over slices).  The
+ * exchange is a collective outside this library; on one device the three calls below
+ * and the per-slice scans reproduce the scan of the whole sequence.
+ *
+ * ssd_seq_total_decay: alpha[b, h] = exp(sum_t dt[b, t, h] * A[h]) over the slice;
+ *   dt [b, L, H], A [H], alpha [b, H], all fp32 (L = 0 gives 1).
+ * ssd_seq_combine: h_in[0] = init_state (NULL = zeros), h_in[j + 1] = alpha[j] h_in[j]
+ *   + S[j] for j < n; alpha [n, b, H], S and h_in [n, b, H, P, N], init_state
+ *   [b, H, P, N], fp32, states 16-byte aligned.
+ * ssd_seq_apply_state: with cum_t the sum of dt * A over the slice through token t,
+ *   y[b, t, h, :] += exp(cum_t) * sum_n C[b, t, g, n] h_in[b, h, :, n] in place, and
+ *   final_state (NULL = skip; the slice's zero-state final state on entry) +=
+ *   exp(cum_last) h_in.  y [b, L, H, P] and C [b, L, G, N] io; dt [b, L, H]; h_in
+ *   [b, H, P, N] fp32 (16-byte aligned, as C; y aligned to 4 elements).  bf16 I/O
+ *   rounds h_in to bf16 as the
+ *   matrix-core operand; fp32 I/O keeps fp32.  Supported: P and N multiples of 16,
+ *   N <= 256.  L = 0 leaves y alone and adds h_in to final_state.
+ * Outputs must not overlap inputs.  Errors as for the other entry points.
+ */
+ssd_status_t ssd_seq_total_decay(const float *dt, const float *A, float *alpha, int b, int L,
+                                 int H, void *hip_stream);
+ssd_status_t ssd_seq_combine(const float *alpha, const float *S, const float *init_state,
+                             float *h_in, int n, int b, int H, int P, int N, void *hip_stream);
+ssd_status_t ssd_seq_apply_state(void *y, float *final_state, const float *dt, const float *A,
+                                 const void *C, const float *h_in, int b, int L, int H, int P,
+                                 int N, int G, ssd_dtype_t io, void *hip_stream);
 
 /*
  * Workspace size in bytes that ssd_chunk_scan_bwd needs for these dimensions (0 for

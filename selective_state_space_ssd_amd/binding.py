@@ -32,6 +32,7 @@ EXPORTED = ("ssd_chunk_scan_workspace_bytes", "ssd_chunk_scan_workspace_init",
             "ssd_chunk_scan_fwd", "ssd_verify_step", "ssd_selective_scan_fwd",
             "ssd_chunk_scan_bwd_workspace_bytes", "ssd_chunk_scan_bwd",
             "ssd_verify_ring_init", "ssd_verify_ring", "ssd_verify_ring_rollback",
+            "ssd_seq_total_decay", "ssd_seq_combine", "ssd_seq_apply_state",
             "ssd_status_string", "ssd_version")
 
 _lib = None
@@ -73,6 +74,12 @@ def lib() -> ctypes.CDLL:
         L.ssd_verify_ring.restype = i32
         L.ssd_verify_ring_rollback.argtypes = [vp, vp, vp, i32, i32, vp]
         L.ssd_verify_ring_rollback.restype = i32
+        L.ssd_seq_total_decay.argtypes = [vp, vp, vp, i32, i32, i32, vp]
+        L.ssd_seq_total_decay.restype = i32
+        L.ssd_seq_combine.argtypes = [vp] * 4 + [i32] * 5 + [vp]
+        L.ssd_seq_combine.restype = i32
+        L.ssd_seq_apply_state.argtypes = [vp] * 6 + [i32] * 6 + [i32, vp]
+        L.ssd_seq_apply_state.restype = i32
         L.ssd_status_string.argtypes = [i32]
         L.ssd_status_string.restype = ctypes.c_char_p
         L.ssd_version.argtypes = []
@@ -263,6 +270,40 @@ def ssd_verify_ring_rollback(meta, steps, err_flag=None, R=None, stream=None) ->
                                         _stream(stream))
     if st != 0:
         raise SSDError(st, "ssd_verify_ring_rollback")
+
+
+def ssd_seq_total_decay(dt, A, alpha, stream=None) -> None:
+    """alpha[b,h] = exp(sum_t dt[b,t,h] A[h]) (all float32)."""
+    b, L, H = dt.shape
+    f32 = torch.float32
+    st = lib().ssd_seq_total_decay(_ptr(dt, "dt", f32), _ptr(A, "A", f32), _ptr(alpha, "alpha", f32),
+                                   b, L, H, _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_seq_total_decay")
+
+
+def ssd_seq_combine(alpha, S, init_state, h_in, stream=None) -> None:
+    """Entering states of n slices from alpha [n,b,H] and final states S [n,b,H,P,N]."""
+    n, b, H, P, N = S.shape
+    f32 = torch.float32
+    st = lib().ssd_seq_combine(_ptr(alpha, "alpha", f32), _ptr(S, "S", f32),
+                               _ptr(init_state, "init_state", f32), _ptr(h_in, "h_in", f32),
+                               n, b, H, P, N, _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_seq_combine")
+
+
+def ssd_seq_apply_state(y, final_state, dt, A, C, h_in, stream=None) -> None:
+    """Correct a slice scanned from zero by its entering state h_in (in place)."""
+    b, L, H, P = y.shape
+    G, N = C.shape[2], C.shape[3]
+    f32 = torch.float32
+    st = lib().ssd_seq_apply_state(_ptr(y, "y", y.dtype), _ptr(final_state, "final_state", f32),
+                                   _ptr(dt, "dt", f32), _ptr(A, "A", f32), _ptr(C, "C", y.dtype),
+                                   _ptr(h_in, "h_in", f32), b, L, H, P, N, G, _io_code(y),
+                                   _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_seq_apply_state")
 
 
 # ------------------------------------------------------------ allocating wrappers

@@ -253,6 +253,68 @@ ssd_status_t ssd_verify_ring_rollback(int32_t *meta, const int32_t *steps, int32
     return SSD_OK;
 }
 
+ssd_status_t ssd_seq_total_decay(const float *dt, const float *A, float *alpha, int b, int L,
+                                 int H, void *hip_stream) {
+    if (b < 0 || L < 0 || H <= 0) return SSD_ERR_BAD_DIM;
+    if (b > 65535) return SSD_ERR_UNSUPPORTED;
+    if (b == 0) return SSD_OK;
+    if (!A || !alpha || (L > 0 && !dt)) return SSD_ERR_NULL_ARG;
+    if (!aligned(dt, 4) || !aligned(A, 4) || !aligned(alpha, 4)) return SSD_ERR_ALIGN;
+    const Range ra(alpha, size_t(b) * H * 4);
+    if (ra.overlaps(Range(dt, size_t(b) * L * H * 4)) || ra.overlaps(Range(A, size_t(H) * 4)))
+        return SSD_ERR_ALIAS;
+    if (ssd::launch_seq_decay(dt, A, alpha, b, L, H, static_cast<hipStream_t>(hip_stream)) !=
+        hipSuccess)
+        return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
+ssd_status_t ssd_seq_combine(const float *alpha, const float *S, const float *init_state,
+                             float *h_in, int n, int b, int H, int P, int N, void *hip_stream) {
+    if (n < 0 || b < 0 || H <= 0 || P <= 0 || N <= 0) return SSD_ERR_BAD_DIM;
+    if ((size_t(P) * N) % 4 != 0 || H > 65535 || b > 65535) return SSD_ERR_UNSUPPORTED;
+    if (n == 0 || b == 0) return SSD_OK;
+    if (!alpha || !S || !h_in) return SSD_ERR_NULL_ARG;
+    if (!aligned(alpha, 4) || !aligned(S, 16) || !aligned(init_state, 16) || !aligned(h_in, 16))
+        return SSD_ERR_ALIGN;
+    const size_t st = size_t(b) * H * P * N * 4;
+    const Range rh(h_in, st * n);
+    if (rh.overlaps(Range(alpha, size_t(n) * b * H * 4)) || rh.overlaps(Range(S, st * n)) ||
+        rh.overlaps(Range(init_state, st)))
+        return SSD_ERR_ALIAS;
+    if (ssd::launch_seq_combine(alpha, S, init_state, h_in, n, b, H, P * N,
+                                static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+        return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
+ssd_status_t ssd_seq_apply_state(void *y, float *final_state, const float *dt, const float *A,
+                                 const void *C, const float *h_in, int b, int L, int H, int P,
+                                 int N, int G, ssd_dtype_t io, void *hip_stream) {
+    if (io != SSD_DTYPE_F32 && io != SSD_DTYPE_BF16) return SSD_ERR_UNSUPPORTED;
+    if (b < 0 || L < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0) return SSD_ERR_BAD_DIM;
+    if (H % G != 0) return SSD_ERR_GROUPS;
+    if (P % 16 != 0 || N % 16 != 0 || N > 256 || H > 65535 || b > 65535) return SSD_ERR_UNSUPPORTED;
+    if (b == 0) return SSD_OK;
+    if (!A || !h_in || (L > 0 && (!y || !dt || !C))) return SSD_ERR_NULL_ARG;
+    const bool bf16 = io == SSD_DTYPE_BF16;
+    const size_t esz = bf16 ? 2 : 4;
+    if (!aligned(y, 4 * esz) || !aligned(final_state, 4) || !aligned(dt, 4) || !aligned(A, 4) ||
+        !aligned(C, 16) || !aligned(h_in, 16))
+        return SSD_ERR_ALIGN;
+    const size_t st = size_t(b) * H * P * N * 4;
+    const Range ry(y, size_t(b) * L * H * P * esz), rf(final_state, st);
+    const Range ins[] = {Range(dt, size_t(b) * L * H * 4), Range(A, size_t(H) * 4),
+                         Range(C, size_t(b) * L * G * N * esz), Range(h_in, st)};
+    for (const Range &in : ins)
+        if (ry.overlaps(in) || rf.overlaps(in)) return SSD_ERR_ALIAS;
+    if (ry.overlaps(rf)) return SSD_ERR_ALIAS;
+    if (ssd::launch_seq_apply(y, final_state, dt, A, C, h_in, b, L, H, P, N, G, bf16,
+                              static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+        return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
 ssd_status_t ssd_selective_scan_fwd(const void *x, const float *dt, const float *A, const void *B,
                                     const void *C, const float *D, const float *init_state,
                                     void *y, float *final_state, int b, int L, int Dch, int N,

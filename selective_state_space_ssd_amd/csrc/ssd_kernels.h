@@ -171,6 +171,15 @@ hipError_t launch_chunk_scan_bwd_bf16(const ChunkScanBwdArgs &a, const ChunkScan
 hipError_t launch_bwd_reduce(const ChunkScanBwdArgs &a, const ChunkScanBwdPlan &plan,
                              hipStream_t stream);
 
+// sequence-parallel pieces (ssd_seqpar.hip)
+hipError_t launch_seq_decay(const float *dt, const float *A, float *alpha, int b, int L, int H,
+                            hipStream_t stream);
+hipError_t launch_seq_combine(const float *alpha, const float *S, const float *init, float *h_in,
+                              int n, int b, int H, int PN, hipStream_t stream);
+hipError_t launch_seq_apply(void *y, float *final_state, const float *dt, const float *A,
+                            const void *C, const float *h_in, int b, int L, int H, int P, int N,
+                            int G, bool bf16, hipStream_t stream);
+
 // final_state = init_state (or zeros) for an empty sequence.
 hipError_t launch_copy_state(const float *init_state, float *final_state, size_t count,
                              hipStream_t stream);

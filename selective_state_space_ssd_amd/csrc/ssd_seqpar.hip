@@ -1,0 +1,250 @@
+// ssd_seqpar.hip -- per-device pieces of the sequence-parallel (context-parallel) scan.
+//
+// A long sequence is split over devices (Mamba-2 article (msbhsh.com), «序列并行»):
+// each device scans its slice from a zero state (ssd_chunk_scan_fwd), the devices
+// exchange the pair (total decay of the slice, final state), every device folds its
+// predecessors' pairs into the state entering its slice, and corrects its outputs
+// by that state's contribution.  The pairs compose associatively because the state
+// passing is linear (Mamba-2 article, «SSD 算法：分块和形态传递», step 3, here over
+// slices instead of chunks).  With a_t = dt_t A_h and cum_t the sum of a over the
+// slice up to and including t:
+//   k_seq_decay   alpha = exp(cum_last) per (b, h)
+//   k_seq_combine h_in[0] = init, h_in[j+1] = alpha_j h_in[j] + S_j
+//   k_seq_apply   y_t += exp(cum_t) C_t . h_in   and   final += exp(cum_last) h_in
+// The exchange itself (an all-gather of b H (P N + 1) floats per device) is a
+// collective outside this library.
+#include "ssd_device.h"
+#include "ssd_kernels.h"
+#include "ssd_stage.h"
+
+namespace ssd {
+
+namespace {
+
+constexpr int kSeg = 256;   // tokens per workgroup of the correction
+
+// alpha[b, h] = exp(sum_t dt[b, t, h] A[h]): one wave per (head, batch), lanes over
+// tokens, summed in a fixed order.
+__global__ __launch_bounds__(64) void k_seq_decay(const float *__restrict__ dt,
+                                                  const float *__restrict__ A,
+                                                  float *__restrict__ alpha, int L, int H) {
+    const int h = blockIdx.x, bi = blockIdx.y, lane = threadIdx.x;
+    float s = 0.f;
+    for (int t = lane; t < L; t += 64) s += dt[(size_t(bi) * L + t) * H + h];
+    s = wave_sum(s);
+    if (lane == 0) alpha[size_t(bi) * H + h] = exp2f(s * A[h] * kLog2e);
+}
+
+// h_in[j] for the n slices, four state elements per thread.  The slices' states and
+// decays are loaded 8 at a time ahead of the dependent chain.
+__global__ __launch_bounds__(256) void k_seq_combine(const float *__restrict__ alpha,
+                                                     const float *__restrict__ S,
+                                                     const float *__restrict__ init,
+                                                     float *__restrict__ h_in, int n, int bH,
+                                                     int PN) {
+    constexpr int kBatch = 8;
+    const size_t bh = size_t(blockIdx.z) * gridDim.y + blockIdx.y;
+    const int e = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e >= PN) return;
+    float4 h = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (init) h = *reinterpret_cast<const float4 *>(init + bh * PN + e);
+    for (int j0 = 0; j0 < n; j0 += kBatch) {
+        float4 sv[kBatch];
+        float al[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int j = min(j0 + k, n - 1);
+            sv[k] = *reinterpret_cast<const float4 *>(S + (size_t(j) * bH + bh) * PN + e);
+            al[k] = alpha[size_t(j) * bH + bh];
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            if (j0 + k >= n) break;
+            *reinterpret_cast<float4 *>(h_in + (size_t(j0 + k) * bH + bh) * PN + e) = h;
+            h.x = al[k] * h.x + sv[k].x;
+            h.y = al[k] * h.y + sv[k].y;
+            h.z = al[k] * h.z + sv[k].z;
+            h.w = al[k] * h.w + sv[k].w;
+        }
+    }
+}
+
+// One workgroup (4 waves) per (256-token segment, head, batch).  The products are
+// Y^T[p][t] = sum_n h_in[p][n] C_t[n]: tiles with rows p and columns t, so each lane
+// updates 4 consecutive p of one token.
+// bf16 I/O: h_in rounded to bf16 as the MFMA operand (v_mfma_f32_16x16x32_bf16);
+// fp32 I/O: fp32 operands (v_mfma_f32_16x16x4f32).  kMaxKq = ceil(N / 32) (bf16).
+template <typename IO, int kMaxKq>
+__global__ __launch_bounds__(256) void k_seq_apply(
+    IO *__restrict__ y, float *__restrict__ final_state, const float *__restrict__ dt,
+    const float *__restrict__ A, const IO *__restrict__ C, const float *__restrict__ h_in, int L,
+    int H, int P, int N, int G) {
+    constexpr bool kBF = !std::is_same_v<IO, float>;
+    const int seg = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
+    const int g = h / (H / G);
+    const int t0 = seg * kSeg, slen = min(kSeg, L - t0);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
+    const size_t bh = size_t(bi) * H + h;
+    const float Al = A[h] * kLog2e;
+    __shared__ float ecum[kSeg];
+    __shared__ float tmp[8];
+
+    // sum of a over the tokens before the segment (log2 domain), fixed order
+    float pre = 0.f;
+    for (int t = tid; t < t0; t += 256) pre += dt[(size_t(bi) * L + t) * H + h];
+    pre = wave_sum(pre);
+    if (lane == 0) tmp[w] = pre;
+    __syncthreads();
+    pre = ((tmp[0] + tmp[1]) + (tmp[2] + tmp[3])) * Al;
+    const float d = tid < slen ? dt[(size_t(bi) * L + t0 + tid) * H + h] : 0.f;
+    const float cs = pre + block_inclusive_scan_256(d * Al, tmp + 4);
+    ecum[tid] = exp2f(cs);
+    __syncthreads();
+
+    const float *hin = h_in + bh * size_t(P) * N;
+    const int ptiles = P / 16;
+    const int ntb = (slen + 15) / 16;
+    if constexpr (kBF) {
+        // wave w takes token tiles w, w + 4, ... and every p tile (P <= 64 per pass), so
+        // each C row is read by one wave; h_in of the p tiles as MFMA A operands (bf16,
+        // k steps of 32; n >= N read 0)
+        for (int pb = 0; pb < ptiles; pb += 4) {
+            const int npt = min(4, ptiles - pb);
+            uint4 hq[4][kMaxKq];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int kq = 0; kq < kMaxKq; ++kq) {
+                    const int n0 = 32 * kq + 8 * g4;
+                    hq[j][kq] = make_uint4(0, 0, 0, 0);
+                    if (j < npt && n0 < N) {
+                        const float *hr = hin + (16 * (pb + j) + r16) * N + n0;
+                        const float4 h0 = *reinterpret_cast<const float4 *>(hr);
+                        const float4 h1 = *reinterpret_cast<const float4 *>(hr + 4);
+                        hq[j][kq] = make_uint4(pack_bf16x2(h0.x, h0.y), pack_bf16x2(h0.z, h0.w),
+                                               pack_bf16x2(h1.x, h1.y), pack_bf16x2(h1.z, h1.w));
+                    }
+                }
+            for (int tb = w; tb < ntb; tb += 4) {
+                const int t = 16 * tb + r16;
+                const bool tv = t < slen;
+                const bf16_bits *crow = C + ((size_t(bi) * L + t0 + (tv ? t : 0)) * G + g) * N;
+                uint4 cq[kMaxKq];
+                uint2 yv[4];
+                bf16_bits *yrow = y + ((size_t(bi) * L + t0 + (tv ? t : 0)) * H + h) * P;
+#pragma unroll
+                for (int kq = 0; kq < kMaxKq; ++kq) {
+                    const int n0 = 32 * kq + 8 * g4;
+                    cq[kq] = n0 < N ? *reinterpret_cast<const uint4 *>(crow + n0) : make_uint4(0, 0, 0, 0);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    yv[j] = (tv && j < npt)
+                                ? *reinterpret_cast<const uint2 *>(yrow + 16 * (pb + j) + 4 * g4)
+                                : make_uint2(0, 0);
+                const float e = ecum[t];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (j >= npt) break;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kq = 0; kq < kMaxKq; ++kq)
+                        acc = mfma_bf16(as_bf16x8(hq[j][kq]), as_bf16x8(cq[kq]), acc);
+                    if (tv) {   // 4 consecutive p of token t, one 8-byte store
+                        uint2 v = yv[j];
+                        v.x = pack_bf16x2(bf16_lo(v.x) + e * acc[0], bf16_hi(v.x) + e * acc[1]);
+                        v.y = pack_bf16x2(bf16_lo(v.y) + e * acc[2], bf16_hi(v.y) + e * acc[3]);
+                        *reinterpret_cast<uint2 *>(yrow + 16 * (pb + j) + 4 * g4) = v;
+                    }
+                }
+            }
+        }
+    } else {
+        for (int pt = w; pt < ptiles; pt += 4) {
+            const int p0 = 16 * pt + 4 * g4;
+            for (int tb = 0; tb < ntb; ++tb) {
+                const int t = 16 * tb + r16;
+                const bool tv = t < slen;
+                const IO *crow = C + ((size_t(bi) * L + t0 + (tv ? t : 0)) * G + g) * N;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int k0 = 0; k0 < N; k0 += 4)
+                    acc = mfma_f32(hin[(16 * pt + r16) * N + k0 + g4], to_f32<IO>(crow[k0 + g4]), acc);
+                if (tv) {   // 4 consecutive p of token t, one 16-byte access
+                    const float e = ecum[t];
+                    IO *yp = y + ((size_t(bi) * L + t0 + t) * H + h) * P + p0;
+                    float4 v = *reinterpret_cast<const float4 *>(yp);
+                    v.x += e * acc[0];
+                    v.y += e * acc[1];
+                    v.z += e * acc[2];
+                    v.w += e * acc[3];
+                    *reinterpret_cast<float4 *>(yp) = v;
+                }
+            }
+        }
+    }
+    if (final_state && t0 + slen == L) {   // the segment holding the last token
+        const float e = ecum[slen - 1];
+        float *fs = final_state + bh * size_t(P) * N;
+        for (int i = tid; i < P * N; i += 256) fs[i] += e * hin[i];
+    }
+}
+
+// final += h_in (a slice with no tokens: its decay is 1)
+__global__ __launch_bounds__(256) void k_seq_add(float *__restrict__ final_state,
+                                                 const float *__restrict__ h_in, size_t count) {
+    const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i < count) final_state[i] += h_in[i];
+}
+
+}  // namespace
+
+hipError_t launch_seq_decay(const float *dt, const float *A, float *alpha, int b, int L, int H,
+                            hipStream_t stream) {
+    hipLaunchKernelGGL(k_seq_decay, dim3(H, b), dim3(64), 0, stream, dt, A, alpha, L, H);
+    return hipGetLastError();
+}
+
+hipError_t launch_seq_combine(const float *alpha, const float *S, const float *init, float *h_in,
+                              int n, int b, int H, int PN, hipStream_t stream) {
+    hipLaunchKernelGGL(k_seq_combine, dim3((PN / 4 + 255) / 256, H, b), dim3(256), 0, stream,
+                       alpha, S, init, h_in, n, b * H, PN);
+    return hipGetLastError();
+}
+
+hipError_t launch_seq_apply(void *y, float *final_state, const float *dt, const float *A,
+                            const void *C, const float *h_in, int b, int L, int H, int P, int N,
+                            int G, bool bf16, hipStream_t stream) {
+    if (L == 0) {
+        if (!final_state) return hipSuccess;
+        const size_t count = size_t(b) * H * P * N;
+        hipLaunchKernelGGL(k_seq_add, dim3(unsigned((count + 255) / 256)), dim3(256), 0, stream,
+                           final_state, h_in, count);
+        return hipGetLastError();
+    }
+    const dim3 grid((L + kSeg - 1) / kSeg, H, b);
+    if (!bf16) {
+        hipLaunchKernelGGL((k_seq_apply<float, 1>), grid, dim3(256), 0, stream,
+                           static_cast<float *>(y), final_state, dt, A,
+                           static_cast<const float *>(C), h_in, L, H, P, N, G);
+        return hipGetLastError();
+    }
+    auto go = [&](auto kq) {
+        hipLaunchKernelGGL((k_seq_apply<bf16_bits, decltype(kq)::value>), grid, dim3(256), 0,
+                           stream, static_cast<bf16_bits *>(y), final_state, dt, A,
+                           static_cast<const bf16_bits *>(C), h_in, L, H, P, N, G);
+        return hipGetLastError();
+    };
+    switch ((N + 31) / 32) {
+        case 1: return go(std::integral_constant<int, 1>{});
+        case 2: return go(std::integral_constant<int, 2>{});
+        case 3: return go(std::integral_constant<int, 3>{});
+        case 4: return go(std::integral_constant<int, 4>{});
+        case 5: return go(std::integral_constant<int, 5>{});
+        case 6: return go(std::integral_constant<int, 6>{});
+        case 7: return go(std::integral_constant<int, 7>{});
+        case 8: return go(std::integral_constant<int, 8>{});
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace ssd

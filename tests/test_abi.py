@@ -287,3 +287,28 @@ def test_ring_init_and_rollback_checks(lib):
     assert lib.ssd_verify_ring_rollback(None, addr(2), None, 2, 4, None) == NULL
     assert lib.ssd_verify_ring_rollback(addr(1), addr(1), None, 2, 4, None) == ALIAS
     assert lib.ssd_verify_ring_rollback(addr(1, 2), addr(2), None, 2, 4, None) == ALIGN
+
+
+def test_seqpar_host_checks(lib):
+    # total decay
+    assert lib.ssd_seq_total_decay(addr(1), addr(2), addr(3), -1, 8, 4, None) == DIM
+    assert lib.ssd_seq_total_decay(None, addr(2), addr(3), 1, 8, 4, None) == NULL
+    assert lib.ssd_seq_total_decay(addr(1), addr(2), addr(1), 1, 8, 4, None) == ALIAS
+    assert lib.ssd_seq_total_decay(addr(1, 2), addr(2), addr(3), 1, 8, 4, None) == ALIGN
+    # combine
+    assert lib.ssd_seq_combine(addr(1), addr(2), None, addr(3), -1, 1, 4, 16, 16, None) == DIM
+    assert lib.ssd_seq_combine(addr(1), None, None, addr(3), 2, 1, 4, 16, 16, None) == NULL
+    assert lib.ssd_seq_combine(addr(1), addr(2, 8), None, addr(3), 2, 1, 4, 16, 16, None) == ALIGN
+    assert lib.ssd_seq_combine(addr(1), addr(2), None, addr(2), 2, 1, 4, 16, 16, None) == ALIAS
+    assert lib.ssd_seq_combine(None, None, None, None, 0, 1, 4, 16, 16, None) == OK
+    # apply
+    call = lambda y=addr(1), f=addr(2), dt=addr(3), A=addr(4), C=addr(5), h=addr(6), \
+        P=64, N=64, G=1, io=1: lib.ssd_seq_apply_state(y, f, dt, A, C, h, 1, 16, 4, P, N, G, io, None)
+    assert call(P=24) == UNSUP
+    assert call(N=512) == UNSUP
+    assert call(G=3) == GROUPS
+    assert call(io=5) == UNSUP
+    assert call(C=None) == NULL
+    assert call(C=addr(5, 8)) == ALIGN
+    assert call(y=addr(5)) == ALIAS                  # y on C
+    assert call(f=addr(6)) == ALIAS                  # final_state on h_in
