@@ -275,10 +275,9 @@ ssd_status_t ssd_verify_ring_rollback(int32_t *meta, const int32_t *steps, int32
  *   y[b, t, h, :] += exp(cum_t) * sum_n C[b, t, g, n] h_in[b, h, :, n] in place, and
  *   final_state (NULL = skip; the slice's zero-state final state on entry) +=
  *   exp(cum_last) h_in.  y [b, L, H, P] and C [b, L, G, N] io; dt [b, L, H]; h_in
- *   [b, H, P, N] fp32 (16-byte aligned, as C; y aligned to 4 elements).  bf16 I/O
- *   rounds h_in to bf16 as the
- *   matrix-core operand; fp32 I/O keeps fp32.  Supported: P and N multiples of 16,
- *   N <= 256.  L = 0 leaves y alone and adds h_in to final_state.
+ *   [b, H, P, N] fp32 (y, C and h_in 16-byte aligned).  bf16 I/O rounds h_in to
+ *   bf16 as the matrix-core operand; fp32 I/O keeps fp32.  Supported: P and N
+ *   multiples of 16, at most 256.  L = 0 leaves y alone and adds h_in to final_state.
  * Outputs must not overlap inputs.  Errors as for the other entry points.
  */
 ssd_status_t ssd_seq_total_decay(const float *dt, const float *A, float *alpha, int b, int L,

@@ -294,12 +294,13 @@ ssd_status_t ssd_seq_apply_state(void *y, float *final_state, const float *dt, c
     if (io != SSD_DTYPE_F32 && io != SSD_DTYPE_BF16) return SSD_ERR_UNSUPPORTED;
     if (b < 0 || L < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0) return SSD_ERR_BAD_DIM;
     if (H % G != 0) return SSD_ERR_GROUPS;
-    if (P % 16 != 0 || N % 16 != 0 || N > 256 || H > 65535 || b > 65535) return SSD_ERR_UNSUPPORTED;
+    if (P % 16 != 0 || P > 256 || N % 16 != 0 || N > 256 || H > 65535 || b > 65535)
+        return SSD_ERR_UNSUPPORTED;
     if (b == 0) return SSD_OK;
     if (!A || !h_in || (L > 0 && (!y || !dt || !C))) return SSD_ERR_NULL_ARG;
     const bool bf16 = io == SSD_DTYPE_BF16;
     const size_t esz = bf16 ? 2 : 4;
-    if (!aligned(y, 4 * esz) || !aligned(final_state, 4) || !aligned(dt, 4) || !aligned(A, 4) ||
+    if (!aligned(y, 16) || !aligned(final_state, 4) || !aligned(dt, 4) || !aligned(A, 4) ||
         !aligned(C, 16) || !aligned(h_in, 16))
         return SSD_ERR_ALIGN;
     const size_t st = size_t(b) * H * P * N * 4;

@@ -89,9 +89,20 @@ __global__ __launch_bounds__(256) void k_seq_apply(
     __shared__ float ecum[kSeg];
     __shared__ float tmp[8];
 
-    // sum of a over the tokens before the segment (log2 domain), fixed order
+    // sum of a over the tokens before the segment (log2 domain), fixed order; the
+    // loads of each batch of 8 are issued together
     float pre = 0.f;
-    for (int t = tid; t < t0; t += 256) pre += dt[(size_t(bi) * L + t) * H + h];
+    for (int base = 0; base < t0; base += 8 * 256) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int t = base + k * 256 + tid;
+            const float x = dt[(size_t(bi) * L + min(t, t0 - 1)) * H + h];
+            v[k] = t < t0 ? x : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) pre += v[k];
+    }
     pre = wave_sum(pre);
     if (lane == 0) tmp[w] = pre;
     __syncthreads();
@@ -105,43 +116,59 @@ __global__ __launch_bounds__(256) void k_seq_apply(
     const int ptiles = P / 16;
     const int ntb = (slen + 15) / 16;
     if constexpr (kBF) {
-        // wave w takes token tiles w, w + 4, ... and every p tile (P <= 64 per pass), so
-        // each C row is read by one wave; h_in of the p tiles as MFMA A operands (bf16,
-        // k steps of 32; n >= N read 0)
+        // the segment's y rows are staged in LDS with whole-row 16-byte accesses; wave
+        // w takes token tiles w, w + 4, ... and every p tile (4 per pass), so each C
+        // row is read by one wave; h_in of the p tiles as MFMA A operands (bf16, k
+        // steps of 32; n >= N read 0); results are added to the staged rows
+        extern __shared__ __align__(16) unsigned char ysm[];
+        bf16_bits *ys = reinterpret_cast<bf16_bits *>(ysm);   // [kSeg][P + 8]
+        const int YS = P + 8, vpr = P / 8;
+        bf16_bits *yseg = y + (size_t(bi) * L + t0) * size_t(H) * P + size_t(h) * P;
+        for (int base = 0; base < slen * vpr; base += 8 * 256) {   // 8 row pieces in flight
+            uint4 v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = min(base + k * 256 + tid, slen * vpr - 1);
+                const int t = i / vpr, c = i % vpr;
+                v[k] = *reinterpret_cast<const uint4 *>(yseg + size_t(t) * H * P + 8 * c);
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = base + k * 256 + tid;
+                if (i < slen * vpr)
+                    *reinterpret_cast<uint4 *>(ys + (i / vpr) * YS + 8 * (i % vpr)) = v[k];
+            }
+        }
+        __syncthreads();
         for (int pb = 0; pb < ptiles; pb += 4) {
             const int npt = min(4, ptiles - pb);
+            // loads without branches (clamped in-range addresses, values zeroed after),
+            // so they are all in flight at once
             uint4 hq[4][kMaxKq];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int kq = 0; kq < kMaxKq; ++kq) {
                     const int n0 = 32 * kq + 8 * g4;
-                    hq[j][kq] = make_uint4(0, 0, 0, 0);
-                    if (j < npt && n0 < N) {
-                        const float *hr = hin + (16 * (pb + j) + r16) * N + n0;
-                        const float4 h0 = *reinterpret_cast<const float4 *>(hr);
-                        const float4 h1 = *reinterpret_cast<const float4 *>(hr + 4);
-                        hq[j][kq] = make_uint4(pack_bf16x2(h0.x, h0.y), pack_bf16x2(h0.z, h0.w),
+                    const bool ok = j < npt && n0 < N;
+                    const float *hr = hin + (16 * (pb + min(j, npt - 1)) + r16) * N + min(n0, N - 8);
+                    const float4 h0 = *reinterpret_cast<const float4 *>(hr);
+                    const float4 h1 = *reinterpret_cast<const float4 *>(hr + 4);
+                    const uint4 v = make_uint4(pack_bf16x2(h0.x, h0.y), pack_bf16x2(h0.z, h0.w),
                                                pack_bf16x2(h1.x, h1.y), pack_bf16x2(h1.z, h1.w));
-                    }
+                    hq[j][kq] = ok ? v : make_uint4(0, 0, 0, 0);
                 }
             for (int tb = w; tb < ntb; tb += 4) {
                 const int t = 16 * tb + r16;
                 const bool tv = t < slen;
                 const bf16_bits *crow = C + ((size_t(bi) * L + t0 + (tv ? t : 0)) * G + g) * N;
                 uint4 cq[kMaxKq];
-                uint2 yv[4];
-                bf16_bits *yrow = y + ((size_t(bi) * L + t0 + (tv ? t : 0)) * H + h) * P;
 #pragma unroll
                 for (int kq = 0; kq < kMaxKq; ++kq) {
                     const int n0 = 32 * kq + 8 * g4;
-                    cq[kq] = n0 < N ? *reinterpret_cast<const uint4 *>(crow + n0) : make_uint4(0, 0, 0, 0);
+                    const uint4 v = *reinterpret_cast<const uint4 *>(crow + min(n0, N - 8));
+                    cq[kq] = n0 < N ? v : make_uint4(0, 0, 0, 0);
                 }
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    yv[j] = (tv && j < npt)
-                                ? *reinterpret_cast<const uint2 *>(yrow + 16 * (pb + j) + 4 * g4)
-                                : make_uint2(0, 0);
                 const float e = ecum[t];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -150,14 +177,21 @@ __global__ __launch_bounds__(256) void k_seq_apply(
 #pragma unroll
                     for (int kq = 0; kq < kMaxKq; ++kq)
                         acc = mfma_bf16(as_bf16x8(hq[j][kq]), as_bf16x8(cq[kq]), acc);
-                    if (tv) {   // 4 consecutive p of token t, one 8-byte store
-                        uint2 v = yv[j];
+                    if (tv) {   // 4 consecutive p of token t in the staged row
+                        uint2 *yp = reinterpret_cast<uint2 *>(ys + t * YS + 16 * (pb + j) + 4 * g4);
+                        uint2 v = *yp;
                         v.x = pack_bf16x2(bf16_lo(v.x) + e * acc[0], bf16_hi(v.x) + e * acc[1]);
                         v.y = pack_bf16x2(bf16_lo(v.y) + e * acc[2], bf16_hi(v.y) + e * acc[3]);
-                        *reinterpret_cast<uint2 *>(yrow + 16 * (pb + j) + 4 * g4) = v;
+                        *yp = v;
                     }
                 }
             }
+        }
+        __syncthreads();
+        for (int i = tid; i < slen * vpr; i += 256) {
+            const int t = i / vpr, c = i % vpr;
+            *reinterpret_cast<uint4 *>(yseg + size_t(t) * H * P + 8 * c) =
+                *reinterpret_cast<const uint4 *>(ys + t * YS + 8 * c);
         }
     } else {
         for (int pt = w; pt < ptiles; pt += 4) {
@@ -228,8 +262,15 @@ hipError_t launch_seq_apply(void *y, float *final_state, const float *dt, const 
                            static_cast<const float *>(C), h_in, L, H, P, N, G);
         return hipGetLastError();
     }
+    const size_t lds = size_t(kSeg) * (P + 8) * 2;   // staged y rows of one segment
     auto go = [&](auto kq) {
-        hipLaunchKernelGGL((k_seq_apply<bf16_bits, decltype(kq)::value>), grid, dim3(256), 0,
+        if (lds > 64 * 1024) {   // above the default dynamic LDS limit
+            const hipError_t e = hipFuncSetAttribute(
+                reinterpret_cast<const void *>(&k_seq_apply<bf16_bits, decltype(kq)::value>),
+                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL((k_seq_apply<bf16_bits, decltype(kq)::value>), grid, dim3(256), lds,
                            stream, static_cast<bf16_bits *>(y), final_state, dt, A,
                            static_cast<const bf16_bits *>(C), h_in, L, H, P, N, G);
         return hipGetLastError();
