@@ -89,16 +89,24 @@ struct ChainPf {
 // DIR 1: Gh_c for c = nc-1 .. 0 (as Gh^T and Gh tiles) from d_final, then d_init.
 // The reverse walk holds its state twice, as tiles with rows p (stored as Gh^T) and
 // with rows n (stored as Gh).
+template <int N>
+struct ChainLds {
+    bf16_bits AT[2][HP * RS];   // [p][t] weighted u, two buffers
+    bf16_bits VT[2][N * RS];    // [n][t] v, two buffers
+    float al_sh[2];
+};
+
 template <int N, int DIR>
-__global__ __launch_bounds__(kChainThreads, 4) void k_bwd_chain(
+__device__ __forceinline__ void chain_walk(
     const bf16_bits *__restrict__ u, const float *__restrict__ dt, const float *__restrict__ A,
     const bf16_bits *__restrict__ v, const float *__restrict__ s0, bf16_bits *__restrict__ dstT,
-    bf16_bits *__restrict__ ghN, float *__restrict__ d_init, int L, int H, int G, int nc) {
+    bf16_bits *__restrict__ ghN, float *__restrict__ d_init, int L, int H, int G, int nc,
+    ChainLds<N> &sm) {
     constexpr int NT = N / 16, NTW = NT / 4, NG = N / 8, PN = HP * N;
     constexpr int kVItems = (32 * NG + kThreads - 1) / kThreads;
-    __shared__ __align__(16) bf16_bits AT[2][HP * RS];   // [p][t] weighted u
-    __shared__ __align__(16) bf16_bits VT[2][N * RS];    // [n][t] v
-    __shared__ float al_sh[2];
+    auto &AT = sm.AT;
+    auto &VT = sm.VT;
+    auto &al_sh = sm.al_sh;
     const int h = blockIdx.x, bi = blockIdx.y;
     const int g = h / (H / G);
     const float Ah = A[h];
@@ -259,6 +267,22 @@ __global__ __launch_bounds__(kChainThreads, 4) void k_bwd_chain(
                         make_float4(accN[j][pt][0], accN[j][pt][1], accN[j][pt][2], accN[j][pt][3]);
         }
     }
+}
+
+// Both walks in one launch (blockIdx.z: 0 forward, 1 reverse), so that the two
+// independent chains of every (head, batch) run at the same time.
+template <int N>
+__global__ __launch_bounds__(kChainThreads, 4) void k_bwd_chain(
+    const bf16_bits *__restrict__ x, const bf16_bits *__restrict__ dy,
+    const float *__restrict__ dt, const float *__restrict__ A, const bf16_bits *__restrict__ B,
+    const bf16_bits *__restrict__ C, const float *__restrict__ init_state,
+    const float *__restrict__ d_final, bf16_bits *__restrict__ hinT, bf16_bits *__restrict__ ghT,
+    bf16_bits *__restrict__ ghN, float *__restrict__ d_init, int L, int H, int G, int nc) {
+    __shared__ __align__(16) ChainLds<N> sm;
+    if (blockIdx.z == 0)
+        chain_walk<N, 0>(x, dt, A, B, init_state, hinT, nullptr, nullptr, L, H, G, nc, sm);
+    else
+        chain_walk<N, 1>(dy, dt, A, C, d_final, ghT, ghN, d_init, L, H, G, nc, sm);
 }
 
 // ------------------------------------------------------------ in-chunk gradients
@@ -651,11 +675,9 @@ hipError_t launch_n(const ChunkScanBwdArgs &a, const ChunkScanBwdPlan &pl, hipSt
     const bf16_bits *x = static_cast<const bf16_bits *>(a.x), *B = static_cast<const bf16_bits *>(a.B);
     const bf16_bits *C = static_cast<const bf16_bits *>(a.C), *dy = static_cast<const bf16_bits *>(a.dy);
     hipError_t e;
-    hipLaunchKernelGGL((k_bwd_chain<N, 0>), dim3(a.H, a.b), dim3(kChainThreads), 0, stream, x,
-                       a.dt, a.A, B, a.init_state, hinT, nullptr, nullptr, a.L, a.H, a.G, pl.nc);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_bwd_chain<N, 1>), dim3(a.H, a.b), dim3(kChainThreads), 0, stream, dy,
-                       a.dt, a.A, C, a.d_final, ghT, ghN, a.d_init, a.L, a.H, a.G, pl.nc);
+    hipLaunchKernelGGL((k_bwd_chain<N>), dim3(a.H, a.b, 2), dim3(kChainThreads), 0, stream, x, dy,
+                       a.dt, a.A, B, C, a.init_state, a.d_final, hinT, ghT, ghN, a.d_init, a.L,
+                       a.H, a.G, pl.nc);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t lds = ChunkLds<N>::bytes;
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_bwd_chunk_bf<N>),
