@@ -14,6 +14,9 @@ Printed: one JSON line with the contract fields plus
                 bytes per call from the committed counter summary in profiles/, used
                 only while the kernel source still hashes to what was profiled
   cpu_baseline  the fp64 CPU oracle timed on this host's cores
+  cpu_oracle_extras
+                the verify, comparison-scan and gradient oracles timed on bounded
+                samples of their legs' workloads
   L16k          the long-context layer (L=16384, nonzero initial state)
   verify        the K=4 verify step (GB/s of algorithmic bytes)
   selective_scan_comparison
@@ -268,9 +271,15 @@ def time_ring(steps, warmup, bd, inputs, torch, K=4, R=8):
     for i in range(warmup):
         call(i)
     mean_ms, _ = _timed(call, warmup, steps, stream, torch)
-    st = b * H * P * N * 4
-    alg = (1 + K) * st + 2 * b * K * H * P * 2 + b * K * H * 4 + 2 * b * K * G * N * 2 + 16 * H + 12 * b
+    alg = ring_alg_bytes(b, H, P, N, G, K)
     return dict(call_ms_mean=mean_ms, alg_bytes=alg, gbs=alg / (mean_ms * 1e-3) / 1e9, R=R, K=K)
+
+
+def ring_alg_bytes(b, H, P, N, G, K):
+    """One ring round with every draft accepted: the head state read, K states written,
+    bf16 x and y, fp32 dt, bf16 B and C, fp32 A, D, dt_bias and the per-row scalars."""
+    st = b * H * P * N * 4
+    return (1 + K) * st + 2 * b * K * H * P * 2 + b * K * H * 4 + 2 * b * K * G * N * 2 + 16 * H + 12 * b
 
 
 def time_seqpar(steps, warmup, bd, inputs, torch, n=8):
@@ -344,6 +353,85 @@ def cpu_baseline(inp, max_units=None):
     return {"value": tokens / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{sample} of {units} (batch, head) units of the same workload, "
                       f"tokens scaled by {sample}/{units}; wall {wall:.2f} s"}
+
+
+def cpu_oracle_extras(inputs):
+    """The other oracles as they stand, on bounded samples of the extra legs'
+    workloads (one host thread each; a few seconds in all)."""
+    import numpy as np
+
+    import oracle
+    from oracle import backward, cp, ring
+    out = {}
+    # verify step: the whole verify workload through the fp64 verify oracle
+    v = inputs.make_workload("verify_b32_K4")
+    d = v.dims
+    args = [getattr(v, k).f64() for k in ("state", "x", "dt", "A", "B", "C", "D")]
+    t0 = time.perf_counter()
+    oracle.verify_f64(*args, v.accept_len, want_all=False)
+    wall = time.perf_counter() - t0
+    out["verify"] = {"value": verify_alg_bytes(d, 2) / wall / 1e9, "unit": "GB/s", "cores": 1,
+                     "kind": "oracle", "sample": f"the whole verify workload; wall {wall:.2f} s"}
+    # ring: one round of the ring leg's workload, every draft accepted
+    K, R = 4, 8
+    ri = inputs.make_verify_ring_inputs(d["b"], K, d["H"], d["P"], d["N"], d["G"], R, 1,
+                                        io="bf16", biased=True, seed=5)
+    rr = ri.rounds[0]
+    rg, meta = ring.ring_init_f64(ri.init_state.f64(), R)
+    acc = np.full(d["b"], K, dtype=np.int32)
+    t0 = time.perf_counter()
+    ring.verify_ring_f64(rg, meta, rr["x"].f64(), rr["dt"].f64(), ri.A.f64(), rr["B"].f64(),
+                         rr["C"].f64(), ri.D.f64(), acc, dt_bias=ri.dt_bias.f64())
+    wall = time.perf_counter() - t0
+    out["verify_ring"] = {"value": ring_alg_bytes(d["b"], d["H"], d["P"], d["N"], d["G"], K)
+                          / wall / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                          "sample": f"one whole round; wall {wall:.2f} s"}
+    # comparison scan: 64 of 5120 channels at N = 128
+    sel = inputs.make_workload("mamba1_L2k_N128")
+    ch = np.arange(64)
+    x, dt, A, D = (getattr(sel, k).f64() for k in ("x", "dt", "A", "D"))
+    t0 = time.perf_counter()
+    oracle.selective_scan_f64(x[:, :, ch], dt[:, :, ch], A[ch], sel.B.f64(), sel.C.f64(), D[ch])
+    wall = time.perf_counter() - t0
+    ds = sel.dims
+    out["selective_scan_N128"] = {
+        "value": ds["b"] * ds["L"] * len(ch) / ds["Dch"] / wall, "unit": "tokens/s", "cores": 1,
+        "kind": "oracle", "sample": f"{len(ch)} of {ds['Dch']} channels, tokens scaled by "
+                                    f"{len(ch)}/{ds['Dch']}; wall {wall:.2f} s"}
+    # sequence-parallel correction: 16 heads of batch row 0 over one 2048-token slice of
+    # the L16k layer (one group: C is shared by those heads)
+    l16 = inputs.make_workload("mamba2_2p7b_L16k")
+    d16 = l16.dims
+    Ls, nh = d16["L"] // 8, 16
+    rng = np.random.default_rng(3)
+    h_in = rng.standard_normal((1, nh, d16["P"], d16["N"]))
+    ys = rng.standard_normal((1, Ls, nh, d16["P"]))
+    t0 = time.perf_counter()
+    cp.apply_entering_state_f64(ys, None, l16.dt.f64()[:1, :Ls, :nh], l16.A.f64()[:nh],
+                                l16.C.f64()[:1, :Ls, :1], h_in)
+    wall = time.perf_counter() - t0
+    u16 = d16["b"] * d16["H"]
+    out["sequence_parallel_apply"] = {
+        "value": d16["b"] * Ls * nh / u16 / wall, "unit": "tokens/s", "cores": 1,
+        "kind": "oracle",
+        "sample": f"{nh} of {u16} (batch, head) units of one {Ls}-token slice, tokens scaled "
+                  f"by {nh}/{u16}; wall {wall:.2f} s"}
+    # backward: one head of one batch row of the L2k layer through the gradient oracle
+    inp = inputs.make_workload("mamba2_2p7b_L2k")
+    dy, dfin = inputs.make_upstream_grads(inp, seed=77)
+    db = inp.dims
+    sl = (slice(0, 1), slice(None), slice(0, 1))
+    t0 = time.perf_counter()
+    backward.scan_bwd_f64(inp.x.f64()[sl], inp.dt.f64()[:1, :, :1], inp.A.f64()[:1],
+                          inp.B.f64()[:1], inp.C.f64()[:1], inp.D.f64()[:1], None,
+                          dy.f64()[sl], dfin.f64()[:1, :1])
+    wall = time.perf_counter() - t0
+    units = db["b"] * db["H"]
+    out["backward"] = {"value": db["b"] * db["L"] / units / wall, "unit": "tokens/s",
+                       "cores": 1, "kind": "oracle",
+                       "sample": f"1 of {units} (batch, head) units, tokens scaled by 1/{units}; "
+                                 f"wall {wall:.2f} s"}
+    return out
 
 
 def main():
@@ -467,6 +555,8 @@ def main():
         out["dstate_sweep"] = sw
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(r["inp"])
+        if not args.no_extra:
+            out["cpu_oracle_extras"] = cpu_oracle_extras(inputs)
     print(json.dumps(out), flush=True)
 
 
