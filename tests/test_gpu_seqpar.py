@@ -52,6 +52,10 @@ SMALL = [
     (1, 513, 2, 32, 128, 1, "f32", True, [0, 1, 300, 513]),     # a one-token slice
     (2, 384, 4, 16, 32, 4, "f32", False, [0, 128, 256, 384]),
     (1, 300, 2, 64, 48, 2, "bf16", True, [0, 300, 300]),         # an empty last slice
+    (1, 400, 2, 128, 32, 1, "bf16", True, [0, 150, 400]),        # P > 64: two channel passes
+    (1, 600, 2, 64, 256, 2, "bf16", True, [0, 333, 600]),        # N = 256: state staged twice
+    (2, 300, 2, 16, 80, 1, "bf16", False, [0, 17, 300]),         # one channel tile, padded N,
+                                                                 # a slice of one token tile
 ]
 
 
