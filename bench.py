@@ -434,6 +434,11 @@ def cpu_oracle_extras(inputs):
     return out
 
 
+def _progress(msg):
+    """One line per finished leg on stderr (stdout carries only the JSON line)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -470,6 +475,7 @@ def main():
         del src, dst
 
     r = time_scan(args.workload, args.steps, args.warmup, bd, inputs, torch)
+    _progress(f"{args.workload} timed")
     d = r["dims"]
     tokens = d["b"] * d["L"]
     achieved = r["alg_bytes"] / (r["call_ms_mean"] * 1e-3) / 1e9
@@ -502,6 +508,7 @@ def main():
     }
     if not args.no_extra:
         r2 = time_scan("mamba2_2p7b_L16k", max(5, args.steps // 3), 2, bd, inputs, torch)
+        _progress("mamba2_2p7b_L16k timed")
         d2 = r2["dims"]
         a2 = r2["alg_bytes"] / (r2["call_ms_mean"] * 1e-3) / 1e9
         out["L16k"] = {"tokens_per_s": d2["b"] * d2["L"] / (r2["call_ms_mean"] * 1e-3),
@@ -516,6 +523,7 @@ def main():
                             "hbm_frac": r1["gbs"] / HBM_PEAK_GBS,
                             "call_ms_mean": r1["call_ms_mean"], "alg_bytes": r1["alg_bytes"]}
         rr = time_ring(max(10, args.steps), 3, bd, inputs, torch)
+        _progress("verify, decode and ring rounds timed")
         out["verify_ring"] = {"workload": "verify_b32_K4 layer, ring of 8, all 4 drafts accepted, "
                                           "fused softplus step",
                               "GB_per_s": rr["gbs"], "hbm_frac": rr["gbs"] / HBM_PEAK_GBS,
@@ -530,11 +538,14 @@ def main():
                             "call_ms_mean": rs["call_ms_mean"],
                             "ssd_N128_speedup": ssd_tps / tps}
         out["selective_scan_comparison"] = cmp
+        _progress("comparison scan timed")
         sp = time_seqpar(max(10, args.steps), 3, bd, inputs, torch)
+        _progress("sequence-parallel pieces timed")
         sp["workload"] = "mamba2_2p7b_L16k in 8 slices of 2048 tokens, one slice's share"
         sp["monolithic_L16k_per_slice_us"] = r2["call_ms_mean"] * 1e3 / 8
         out["sequence_parallel"] = sp
         rb = time_backward(args.workload, max(5, args.steps // 3), 2, bd, inputs, torch)
+        _progress("backward timed")
         db = rb["dims"]
         ab = rb["alg_bytes"] / (rb["call_ms_mean"] * 1e-3) / 1e9
         out["backward"] = {"workload": args.workload,
@@ -555,6 +566,7 @@ def main():
         out["dstate_sweep"] = sw
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(r["inp"])
+        _progress("oracle timed")
         if not args.no_extra:
             out["cpu_oracle_extras"] = cpu_oracle_extras(inputs)
     print(json.dumps(out), flush=True)

@@ -295,7 +295,7 @@ void k_ssd_fused(
         for (int k = 0; k < 4; ++k)
             xq[k] = __builtin_bit_cast(
                 uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                           xres, int((((xt0 + k) * H + hx) * P + xc0) * 2), 0, 0));
+                           xres, int((((xt0 + k) * H + hx) * P + xc0) * 2), 0, kBufNonTemporal));
     };
     auto load_dt = [&](int hx) {   // 0 past qlen; a head past the block reads unused data
         return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(dtres, int((tid * H + hx) * 4), 0, 0));
@@ -307,6 +307,12 @@ void k_ssd_fused(
     // loaded at the start of the head before the one they serve.  The first head's
     // loads are issued before B's, whose wait retires them.
     constexpr bool kPrefetchX = F::kWgPerCu == 1;
+    // A and D of the block's heads, lane j holding head h0 + j (HB <= 16), read per
+    // head with v_readlane: a scalar load per head would share its wait counter with
+    // the LDS reads and put a memory round trip in front of the first LDS wait of the
+    // cumsum and of the epilogue
+    const float a_lanes = lane < HB ? A[h0 + lane] : 0.f;
+    const float d_lanes = lane < HB ? D[h0 + lane] : 0.f;
     const float dt_first = load_dt(h0);
     float dt_pipe = kPrefetchX ? load_dt(h0 + 1) : 0.f;
     uint4 xq[4];       // x of the lane's 4 staging tokens, channels xc0 .. xc0+7
@@ -397,7 +403,7 @@ void k_ssd_fused(
         // ---- discretisation and in-chunk decay cumsum (inclusive, log2 domain),
         // computed by every wave for all tokens: 4 tokens per lane + a wave scan
         if constexpr (!kPrefetchX) load_x(xq, h);
-        const float Al2 = A[h] * kLog2e;
+        const float Al2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a_lanes), hh)) * kLog2e;
         float dq[4], aq[4];
         {
             const float4 d4 = *reinterpret_cast<const float4 *>(dtn + tq0);
@@ -446,9 +452,72 @@ void k_ssd_fused(
             for (int j = 0; j < 8; ++j)
                 *reinterpret_cast<uint2 *>(XwT + (xc0 + j) * F::QS + xp0) = cols[j];
         }
+        // ---- step 3, first half: wait for the previous chunk of this head to publish
+        // its state.  Thread 0 polls while the other waves finish staging, and the
+        // staging barrier hands the outcome to the workgroup; the state loads are then
+        // issued before the step 2 products, which cover their latency.
+        if (c > 0 && tid == 0) {
+            uint32_t *flag = flags + bh * nc + (c - 1);
+            uint32_t it = 0;
+            int ok = ws_ok;
+            while (ok && __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != ready) {
+                __builtin_amdgcn_s_sleep(2);
+                if (++it > kSpinLimit) {
+                    ok = 0;
+                    __hip_atomic_store(&hdr[kWsErrorWord], 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+            }
+            misc[1] = ok;
+        }
         __syncthreads();
 
         if (tid < Q) dtn[tid] = dt_next;
+        const float *hsrc = nullptr;   // state entering this chunk, fp32 [P][N]; null = zeros
+        bool coherent = false, poisoned = false;
+        if (c > 0) {
+            poisoned = __builtin_amdgcn_readfirstlane(misc[1]) == 0;
+            coherent = true;
+            hsrc = hbuf + (bh * 2 + ((c - 1) & 1)) * size_t(P) * N;
+        } else if (init_state) {
+            hsrc = init_state + bh * size_t(P) * N;
+        }
+        // one read of the entering state, in the accumulator layout: it feeds the
+        // update and the bf16 copy in LDS
+        float hp[F::PTW][F::NTW][4];
+        // offset of element (k, j, i) of the wave's tiles in a [P][N] state
+        auto off = [&](int k, int j, int i) {
+            return ((pt_base + PT_STEP * k) * 16 + 4 * g4 + i) * N + (nt_base + NT_STEP * j) * 16 + r16;
+        };
+#pragma unroll
+        for (int k = 0; k < F::PTW; ++k)
+#pragma unroll
+            for (int j = 0; j < F::NTW; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) hp[k][j][i] = 0.f;
+        if (s_active) {
+            if (coherent) {
+                const __amdgpu_buffer_rsrc_t ring = buffer_rsrc(hsrc, uint32_t(P * N * 4));
+#pragma unroll
+                for (int k = 0; k < F::PTW; ++k)
+#pragma unroll
+                    for (int j = 0; j < F::NTW; ++j) {
+                        const int tile = (pt_base + PT_STEP * k) * F::NTN + nt_base + NT_STEP * j;
+                        const f32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+                            ring, (tile * 64 + lane) * 16, 0, kBufDevice);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) hp[k][j][i] = v[i];
+                    }
+            } else if (hsrc) {
+#pragma unroll
+                for (int k = 0; k < F::PTW; ++k)
+#pragma unroll
+                    for (int j = 0; j < F::NTW; ++j)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) hp[k][j][i] = hsrc[off(k, j, i)];
+            }
+        }
         // ---- step 2: S_c = XwT^T B (x already carries dt and the decay to the chunk end)
         f32x4 accS[F::PTW][F::NTW];
 #pragma unroll
@@ -494,68 +563,10 @@ void k_ssd_fused(
             }
         }
 
-        // ---- step 3: chain with the previous chunk of this head
+        // ---- step 3, second half: H_c = exp(Acum_end) H_{c-1} + S_c
         const float alpha = exp2_dec(aend);
-        const float *hsrc = nullptr;   // state entering this chunk, fp32 [P][N]; null = zeros
-        bool coherent = false, poisoned = false;
-        if (c > 0) {
-            uint32_t *flag = flags + bh * nc + (c - 1);
-            if (tid == 0) {
-                uint32_t it = 0;
-                int ok = ws_ok;
-                while (ok && __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != ready) {
-                    __builtin_amdgcn_s_sleep(2);
-                    if (++it > kSpinLimit) {
-                        ok = 0;
-                        __hip_atomic_store(&hdr[kWsErrorWord], 1u, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-                        break;
-                    }
-                }
-                misc[1] = ok;
-            }
-            __syncthreads();
-            poisoned = __builtin_amdgcn_readfirstlane(misc[1]) == 0;
-            coherent = true;
-            hsrc = hbuf + (bh * 2 + ((c - 1) & 1)) * size_t(P) * N;
-        } else if (init_state) {
-            hsrc = init_state + bh * size_t(P) * N;
-        }
         const float nanv = __int_as_float(0x7fc00000);
         if (s_active) {
-            // one read of the entering state, in the accumulator layout: it feeds the
-            // update and the bf16 copy in LDS; then the update and all stores
-            float hp[F::PTW][F::NTW][4];
-            // offset of element (k, j, i) of the wave's tiles in a [P][N] state
-            auto off = [&](int k, int j, int i) {
-                return ((pt_base + PT_STEP * k) * 16 + 4 * g4 + i) * N + (nt_base + NT_STEP * j) * 16 + r16;
-            };
-#pragma unroll
-            for (int k = 0; k < F::PTW; ++k)
-#pragma unroll
-                for (int j = 0; j < F::NTW; ++j)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) hp[k][j][i] = 0.f;
-            if (coherent) {
-                const __amdgpu_buffer_rsrc_t ring = buffer_rsrc(hsrc, uint32_t(P * N * 4));
-#pragma unroll
-                for (int k = 0; k < F::PTW; ++k)
-#pragma unroll
-                    for (int j = 0; j < F::NTW; ++j) {
-                        const int tile = (pt_base + PT_STEP * k) * F::NTN + nt_base + NT_STEP * j;
-                        const f32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
-                            ring, (tile * 64 + lane) * 16, 0, kBufDevice);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) hp[k][j][i] = v[i];
-                    }
-            } else if (hsrc) {
-#pragma unroll
-                for (int k = 0; k < F::PTW; ++k)
-#pragma unroll
-                    for (int j = 0; j < F::NTW; ++j)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) hp[k][j][i] = hsrc[off(k, j, i)];
-            }
             if (poisoned) {
 #pragma unroll
                 for (int k = 0; k < F::PTW; ++k)
@@ -613,7 +624,7 @@ void k_ssd_fused(
         }
 
         // ---- steps 1 and 4 for this wave's output tiles
-        const float Dh = D[h];
+        const float Dh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d_lanes), hh));
         // step 4 (entering state through C, referenced to the chunk start) for all
         // of the wave's tile slots at once: each state fragment read from LDS feeds
         // every slot; the reads of k-step kk are in flight during the products of
