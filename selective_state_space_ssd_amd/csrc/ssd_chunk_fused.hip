@@ -798,15 +798,20 @@ void k_ssd_fused(
     }
 }
 
-// Heads per workgroup.  A workgroup computes the chunk's score tiles once (cost
-// about one head) and then runs its HB heads one after another, so a larger HB
-// amortises the score tiles but makes fewer, longer work items.  With `slots`
+// Heads per workgroup.  A workgroup computes the chunk's score tiles once and then runs
+// its HB heads one after another, so a larger HB amortises the item prologue (ticket,
+// B and C loads, score tiles) but makes fewer, longer work items.  With `slots`
 // workgroups resident at a time, the estimate in head-times is
-//   ceil(items / slots) * (1 + HB)  +  (chunks of one head in flight - 1) * link,
-// the second term being the fill of the chunk-to-chunk hand-off chain (one link
-// costs about 0.3 of a head).  HB ranges over the divisors of H / G up to 16
-// (a block never straddles two groups); ties go to the smaller HB.
-int heads_per_workgroup(int b, int H, int G, int nc, int slots) {
+//   ceil(items / slots) * (prologue + HB)  +  (chunks of one head in flight - 1) * link,
+// the second term being the fill of the chunk-to-chunk hand-off chain.  With one
+// workgroup per CU nothing covers the prologue: timestamps put it at about 1.15 head
+// times and a chain link at about 0.2.  With two per CU the other workgroup covers part
+// of the prologue, and 1.0 and 0.3 fit the measurements better.  HB ranges over the
+// divisors of H / G up to 16 (a block never straddles two groups); ties go to the
+// smaller HB.
+int heads_per_workgroup(int b, int H, int G, int nc, int slots, int wg_per_cu) {
+    const double prologue = wg_per_cu == 1 ? 1.15 : 1.0;
+    const double link = wg_per_cu == 1 ? 0.2 : 0.3;
     const int hpg = H / G;
     int best = 1;
     double best_t = 0.0;
@@ -816,7 +821,7 @@ int heads_per_workgroup(int b, int H, int G, int nc, int slots) {
         const double items = chains * nc;
         const double rounds = std::ceil(items / slots);
         const double inflight = std::min(double(nc), std::ceil(slots / chains));
-        const double t = rounds * (1.0 + hb) + (inflight - 1.0) * 0.3;
+        const double t = rounds * (prologue + hb) + (inflight - 1.0) * link;
         if (hb == 1 || t < best_t - 1e-9) {
             best = hb;
             best_t = t;
@@ -840,7 +845,8 @@ hipError_t launch_fused_qn(const ChunkScanArgs &a, const FusedPlan &fp, hipStrea
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    const int HB = heads_per_workgroup(a.b, a.H, a.G, fp.nc, std::max(1, cus) * F::kWgPerCu);
+    const int HB = heads_per_workgroup(a.b, a.H, a.G, fp.nc, std::max(1, cus) * F::kWgPerCu,
+                                       F::kWgPerCu);
     const int nchains = a.b * (a.H / HB);
     const unsigned items = unsigned(nchains) * unsigned(fp.nc);
     hipLaunchKernelGGL((k_ssd_fused<Q, N>), dim3(items), dim3(kFT), F::kLds, stream,
