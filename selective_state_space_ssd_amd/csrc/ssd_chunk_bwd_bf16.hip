@@ -35,6 +35,8 @@ namespace {
 constexpr int QB = 64;     // tokens per chunk
 constexpr int HP = 64;     // head dimension P of this path
 constexpr int RS = 80;     // LDS row stride (bf16) of rows of 64 elements
+constexpr int RSA = 72;    // the same for the chain walk's weighted-u rows (keeps two
+                           // two-head walk workgroups within one CU's LDS)
 
 __device__ __forceinline__ bf16x8 lds16(const bf16_bits *p) {
     return as_bf16x8(*reinterpret_cast<const uint4 *>(p));
@@ -70,10 +72,12 @@ __device__ __forceinline__ uint4 tile_operand(const bf16_bits *base, int t_base,
 }
 
 // Inputs of one chunk step held by a loader thread: the token pair (2 tpu, 2 tpu + 1)
-// of u (x or dy) at p group pgu, two token-pair items of v (B or C), and dt.
+// of u (x or dy) at p group pgu for each of the FH walked heads, two token-pair items
+// of v (B or C, shared by the heads of a group), and dt of each head.
+template <int FH>
 struct ChainPf {
-    uint4 ua, ub, va[2], vb[2];
-    float d;
+    uint4 ua[FH], ub[FH], va[2], vb[2];
+    float d[FH];
 };
 
 // One chain walk per workgroup of 8 waves with split roles, so that no wave waits on
@@ -85,31 +89,36 @@ struct ChainPf {
 //   state waves 4-7   hold the P x N state in MFMA accumulators, store it, and add the
 //                     staged chunk's contribution: state <- alpha state + U^T V.
 // One barrier per step hands a staged buffer from the loaders to the state waves.
-// DIR 0: Hin_c for c = 0 .. nc-1 (as Hin^T tiles), starting from init_state.
+// DIR 0: Hin_c for c = 0 .. nc-1 (as Hin^T tiles), starting from init_state, for FH
+//        heads of one group at once (they share B, so one staged V serves both).
 // DIR 1: Gh_c for c = nc-1 .. 0 (as Gh^T and Gh tiles) from d_final, then d_init.
 // The reverse walk holds its state twice, as tiles with rows p (stored as Gh^T) and
-// with rows n (stored as Gh).
-template <int N>
+// with rows n (stored as Gh); it walks one head.
+// With FH = 2 the LDS of a workgroup (76 KiB) stays under half of the CU's 160 KiB, so
+// two fit; the per-buffer decay factors live in the unused padding of the first AT row.
+template <int N, int FH>
 struct ChainLds {
-    bf16_bits AT[2][HP * RS];   // [p][t] weighted u, two buffers
-    bf16_bits VT[2][N * RS];    // [n][t] v, two buffers
-    float al_sh[2];
+    bf16_bits AT[2][FH][HP * RSA];  // [p][t] weighted u of each walked head, two buffers
+    bf16_bits VT[2][N * RS];        // [n][t] v, two buffers
 };
 
-template <int N, int DIR>
+template <int N, int DIR, int FH>
 __device__ __forceinline__ void chain_walk(
     const bf16_bits *__restrict__ u, const float *__restrict__ dt, const float *__restrict__ A,
     const bf16_bits *__restrict__ v, const float *__restrict__ s0, bf16_bits *__restrict__ dstT,
     bf16_bits *__restrict__ ghN, float *__restrict__ d_init, int L, int H, int G, int nc,
-    ChainLds<N> &sm) {
+    ChainLds<N, FH> &sm, int h, int bi) {
     constexpr int NT = N / 16, NTW = NT / 4, NG = N / 8, PN = HP * N;
     constexpr int kVItems = (32 * NG + kThreads - 1) / kThreads;
+    constexpr int WH = DIR == 0 ? FH : 1;   // heads this walk carries
+    static_assert(HP + 2 * (2 * FH) <= RSA, "decay factors must fit in the row padding");
     auto &AT = sm.AT;
     auto &VT = sm.VT;
-    auto &al_sh = sm.al_sh;
-    const int h = blockIdx.x, bi = blockIdx.y;
+    float *al_sh = reinterpret_cast<float *>(&sm.AT[0][0][HP]);   // [buf * FH + head]
     const int g = h / (H / G);
-    const float Ah = A[h];
+    float Ah[WH];
+#pragma unroll
+    for (int k = 0; k < WH; ++k) Ah[k] = A[h + k];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
     const size_t bh = size_t(bi) * H + h;
     auto chunk_of = [&](int step) { return DIR == 0 ? step : nc - 1 - step; };
@@ -117,7 +126,7 @@ __device__ __forceinline__ void chain_walk(
     if (w < 4) {
         // ------------------------------------------------ loader waves
         const int tpu = tid >> 3, pgu = tid & 7;
-        auto load = [&](ChainPf &f, int step) {
+        auto load = [&](ChainPf<WH> &f, int step) {
             const bool live = step < nc;
             const int t0 = live ? chunk_of(step) * QB : 0;
             const int qlen = live ? min(QB, L - t0) : 0;
@@ -125,9 +134,12 @@ __device__ __forceinline__ void chain_walk(
             const auto ur = buffer_rsrc(u + tok0 * H * HP, uint32_t(qlen) * uint32_t(H * HP) * 2u);
             const auto vr = buffer_rsrc(v + tok0 * G * N, uint32_t(qlen) * uint32_t(G * N) * 2u);
             const auto dr = buffer_rsrc(dt + tok0 * H, uint32_t(qlen) * uint32_t(H) * 4u);
-            const uint32_t uo = (uint32_t(2 * tpu) * H + h) * HP + 8 * pgu;
-            f.ua = ld128(ur, uo * 2u);
-            f.ub = ld128(ur, (uo + H * HP) * 2u);
+#pragma unroll
+            for (int k = 0; k < WH; ++k) {
+                const uint32_t uo = (uint32_t(2 * tpu) * H + h + k) * HP + 8 * pgu;
+                f.ua[k] = ld128(ur, uo * 2u);
+                f.ub[k] = ld128(ur, (uo + H * HP) * 2u);
+            }
 #pragma unroll
             for (int k = 0; k < kVItems; ++k) {
                 const int item = min(tid + k * kThreads, 32 * NG - 1);
@@ -136,24 +148,30 @@ __device__ __forceinline__ void chain_walk(
                 f.va[k] = ld128(vr, vo * 2u);
                 f.vb[k] = ld128(vr, (vo + G * N) * 2u);
             }
-            f.d = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(dr, int((lane * H + h) * 4), 0, 0));
+#pragma unroll
+            for (int k = 0; k < WH; ++k)
+                f.d[k] = __uint_as_float(
+                    __builtin_amdgcn_raw_buffer_load_b32(dr, int((lane * H + h + k) * 4), 0, 0));
         };
-        auto stage = [&](const ChainPf &f, int step) {
+        auto stage = [&](const ChainPf<WH> &f, int step) {
             const bool live = step < nc;
             const int qlen = live ? min(QB, L - chunk_of(step) * QB) : 1;
             const int buf = step & 1;
-            const float cs = wave_inclusive_scan(f.d * Ah * kLog2e);
-            const float aend = __shfl(cs, qlen - 1, 64);
-            const float wv = lane < qlen ? (DIR == 0 ? exp2f(aend - cs) * f.d : exp2f(cs)) : 0.f;
-            if (tid == 0) al_sh[buf] = exp2f(aend);
-            const float wa = __shfl(wv, 2 * tpu, 64), wb = __shfl(wv, 2 * tpu + 1, 64);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t ea = (&f.ua.x)[j >> 1], eb = (&f.ub.x)[j >> 1];
-                const float fa = (j & 1) ? bf16_hi(ea) : bf16_lo(ea);
-                const float fb = (j & 1) ? bf16_hi(eb) : bf16_lo(eb);
-                *reinterpret_cast<uint32_t *>(&AT[buf][(8 * pgu + j) * RS + 2 * tpu]) =
-                    pack_bf16x2(fa * wa, fb * wb);
+            for (int k = 0; k < WH; ++k) {
+                const float cs = wave_inclusive_scan(f.d[k] * Ah[k] * kLog2e);
+                const float aend = __shfl(cs, qlen - 1, 64);
+                const float wv = lane < qlen ? (DIR == 0 ? exp2f(aend - cs) * f.d[k] : exp2f(cs)) : 0.f;
+                if (tid == 0) al_sh[buf * FH + k] = exp2f(aend);
+                const float wa = __shfl(wv, 2 * tpu, 64), wb = __shfl(wv, 2 * tpu + 1, 64);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t ea = (&f.ua[k].x)[j >> 1], eb = (&f.ub[k].x)[j >> 1];
+                    const float fa = (j & 1) ? bf16_hi(ea) : bf16_lo(ea);
+                    const float fb = (j & 1) ? bf16_hi(eb) : bf16_lo(eb);
+                    *reinterpret_cast<uint32_t *>(&AT[buf][k][(8 * pgu + j) * RSA + 2 * tpu]) =
+                        pack_bf16x2(fa * wa, fb * wb);
+                }
             }
 #pragma unroll
             for (int k = 0; k < kVItems; ++k) {
@@ -170,7 +188,7 @@ __device__ __forceinline__ void chain_walk(
                 }
             }
         };
-        ChainPf f0, f1;
+        ChainPf<WH> f0, f1;
         load(f0, 0);
         load(f1, 1);
         stage(f0, 0);
@@ -192,13 +210,16 @@ __device__ __forceinline__ void chain_walk(
 
     // ---------------------------------------------------- state waves
     const int sw = w - 4;
-    f32x4 accP[NT];
+    f32x4 accP[WH][NT];
     f32x4 accN[DIR ? NTW : 1][4];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int k = 0; k < WH; ++k)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            accP[nt][i] = s0 ? s0[bh * PN + (16 * sw + 4 * g4 + i) * N + 16 * nt + r16] : 0.f;
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                accP[k][nt][i] =
+                    s0 ? s0[(bh + k) * PN + (16 * sw + 4 * g4 + i) * N + 16 * nt + r16] : 0.f;
     if constexpr (DIR == 1) {
 #pragma unroll
         for (int j = 0; j < NTW; ++j)
@@ -218,9 +239,12 @@ __device__ __forceinline__ void chain_walk(
         // store the state (entering chunk c forward, leaving chunk c in reverse)
         const size_t so = (bh * nc + c) * size_t(PN);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-            *reinterpret_cast<uint2 *>(dstT + so + tile_off(nt * 4 + sw, lane)) =
-                make_uint2(pack_bf16x2(accP[nt][0], accP[nt][1]), pack_bf16x2(accP[nt][2], accP[nt][3]));
+        for (int k = 0; k < WH; ++k)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                *reinterpret_cast<uint2 *>(dstT + so + size_t(k) * nc * PN + tile_off(nt * 4 + sw, lane)) =
+                    make_uint2(pack_bf16x2(accP[k][nt][0], accP[k][nt][1]),
+                               pack_bf16x2(accP[k][nt][2], accP[k][nt][3]));
         if constexpr (DIR == 1) {
 #pragma unroll
             for (int j = 0; j < NTW; ++j)
@@ -231,17 +255,23 @@ __device__ __forceinline__ void chain_walk(
                                    pack_bf16x2(accN[j][pt][2], accN[j][pt][3]));
         }
         // state <- al * state + (this chunk's contribution)
-        const float al = al_sh[buf];
-        const bf16_bits *at = AT[buf], *vt = VT[buf];
-        const bf16x8 a0 = lds16(at + (16 * sw + r16) * RS + 8 * g4);
-        const bf16x8 a1 = lds16(at + (16 * sw + r16) * RS + 32 + 8 * g4);
+        const bf16_bits *vt = VT[buf];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            f32x4 t = accP[nt] * al;
-            t = mfma_bf16(a0, lds16(vt + (16 * nt + r16) * RS + 8 * g4), t);
-            accP[nt] = mfma_bf16(a1, lds16(vt + (16 * nt + r16) * RS + 32 + 8 * g4), t);
+        for (int k = 0; k < WH; ++k) {
+            const float al = al_sh[buf * FH + k];
+            const bf16_bits *at = AT[buf][k];
+            const bf16x8 a0 = lds16(at + (16 * sw + r16) * RSA + 8 * g4);
+            const bf16x8 a1 = lds16(at + (16 * sw + r16) * RSA + 32 + 8 * g4);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                f32x4 t = accP[k][nt] * al;
+                t = mfma_bf16(a0, lds16(vt + (16 * nt + r16) * RS + 8 * g4), t);
+                accP[k][nt] = mfma_bf16(a1, lds16(vt + (16 * nt + r16) * RS + 32 + 8 * g4), t);
+            }
         }
         if constexpr (DIR == 1) {
+            const float al = al_sh[buf * FH];
+            const bf16_bits *at = AT[buf][0];
 #pragma unroll
             for (int j = 0; j < NTW; ++j) {
                 const int nt = NTW * sw + j;
@@ -250,8 +280,8 @@ __device__ __forceinline__ void chain_walk(
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) {
                     f32x4 t = accN[j][pt] * al;
-                    t = mfma_bf16(c0, lds16(at + (16 * pt + r16) * RS + 8 * g4), t);
-                    accN[j][pt] = mfma_bf16(c1, lds16(at + (16 * pt + r16) * RS + 32 + 8 * g4), t);
+                    t = mfma_bf16(c0, lds16(at + (16 * pt + r16) * RSA + 8 * g4), t);
+                    accN[j][pt] = mfma_bf16(c1, lds16(at + (16 * pt + r16) * RSA + 32 + 8 * g4), t);
                 }
             }
         }
@@ -269,20 +299,31 @@ __device__ __forceinline__ void chain_walk(
     }
 }
 
-// Both walks in one launch (blockIdx.z: 0 forward, 1 reverse), so that the two
-// independent chains of every (head, batch) run at the same time.
-template <int N>
+// Both walks in one launch, so that the independent chains of every (head, batch) run
+// at the same time: workgroups 0 .. nfwd-1 walk forward over FH heads of one group
+// each (batch row, then head pair), the following b H workgroups walk one head each in
+// reverse.  With FH = 2 and 76 KiB of LDS per workgroup, all b H (1 + 1/FH) workgroups
+// of the L=2048 layer (480) are resident at once on 256 CUs (two per CU), where one
+// head per forward walk (640) needed a second round.
+template <int N, int FH>
 __global__ __launch_bounds__(kChainThreads, 4) void k_bwd_chain(
     const bf16_bits *__restrict__ x, const bf16_bits *__restrict__ dy,
     const float *__restrict__ dt, const float *__restrict__ A, const bf16_bits *__restrict__ B,
     const bf16_bits *__restrict__ C, const float *__restrict__ init_state,
     const float *__restrict__ d_final, bf16_bits *__restrict__ hinT, bf16_bits *__restrict__ ghT,
-    bf16_bits *__restrict__ ghN, float *__restrict__ d_init, int L, int H, int G, int nc) {
-    __shared__ __align__(16) ChainLds<N> sm;
-    if (blockIdx.z == 0)
-        chain_walk<N, 0>(x, dt, A, B, init_state, hinT, nullptr, nullptr, L, H, G, nc, sm);
-    else
-        chain_walk<N, 1>(dy, dt, A, C, d_final, ghT, ghN, d_init, L, H, G, nc, sm);
+    bf16_bits *__restrict__ ghN, float *__restrict__ d_init, int L, int H, int G, int nc,
+    int nfwd) {
+    __shared__ __align__(16) ChainLds<N, FH> sm;
+    const int wg = blockIdx.x;
+    if (wg < nfwd) {
+        const int hp = H / FH;
+        chain_walk<N, 0, FH>(x, dt, A, B, init_state, hinT, nullptr, nullptr, L, H, G, nc, sm,
+                             FH * (wg % hp), wg / hp);
+    } else {
+        const int r = wg - nfwd;
+        chain_walk<N, 1, FH>(dy, dt, A, C, d_final, ghT, ghN, d_init, L, H, G, nc, sm, r % H,
+                             r / H);
+    }
 }
 
 // ------------------------------------------------------------ in-chunk gradients
@@ -675,9 +716,18 @@ hipError_t launch_n(const ChunkScanBwdArgs &a, const ChunkScanBwdPlan &pl, hipSt
     const bf16_bits *x = static_cast<const bf16_bits *>(a.x), *B = static_cast<const bf16_bits *>(a.B);
     const bf16_bits *C = static_cast<const bf16_bits *>(a.C), *dy = static_cast<const bf16_bits *>(a.dy);
     hipError_t e;
-    hipLaunchKernelGGL((k_bwd_chain<N>), dim3(a.H, a.b, 2), dim3(kChainThreads), 0, stream, x, dy,
-                       a.dt, a.A, B, C, a.init_state, a.d_final, hinT, ghT, ghN, a.d_init, a.L,
-                       a.H, a.G, pl.nc);
+    // two heads per forward walk whenever a group has an even number of heads
+    if ((a.H / a.G) % 2 == 0) {
+        const int nfwd = a.b * a.H / 2;
+        hipLaunchKernelGGL((k_bwd_chain<N, 2>), dim3(nfwd + a.b * a.H), dim3(kChainThreads), 0,
+                           stream, x, dy, a.dt, a.A, B, C, a.init_state, a.d_final, hinT, ghT, ghN,
+                           a.d_init, a.L, a.H, a.G, pl.nc, nfwd);
+    } else {
+        const int nfwd = a.b * a.H;
+        hipLaunchKernelGGL((k_bwd_chain<N, 1>), dim3(nfwd + a.b * a.H), dim3(kChainThreads), 0,
+                           stream, x, dy, a.dt, a.A, B, C, a.init_state, a.d_final, hinT, ghT, ghN,
+                           a.d_init, a.L, a.H, a.G, pl.nc, nfwd);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t lds = ChunkLds<N>::bytes;
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_bwd_chunk_bf<N>),
