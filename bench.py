@@ -18,7 +18,8 @@ Printed: one JSON line with the contract fields plus
                 the verify, comparison-scan and gradient oracles timed on bounded
                 samples of their legs' workloads
   L16k          the long-context layer (L=16384, nonzero initial state)
-  verify        the K=4 verify step (GB/s of algorithmic bytes)
+  verify        the K=4 verify step (GB/s of algorithmic bytes), beside an elementwise
+                kernel that reads and writes the same 64 MiB (inputs rotated alike)
   selective_scan_comparison
                 the one-channel-per-head selective scan (diagonal A, the recurrence
                 SSD replaces) on the same layer shape (4 x 2048 tokens, 5120
@@ -332,6 +333,27 @@ def copy_bandwidth(torch, mib=1024, reps=10):
     return 2 * (n * 4) / (ms * 1e-3) / 1e9
 
 
+def copy_bandwidth_rotated(torch, mib, steps):
+    """Read+write GB/s of the same elementwise kernel over `mib` MiB each way, the buffers
+    rotated like a leg's inputs so that none is served from the Infinity Cache: the
+    practical ceiling for a kernel that moves that many bytes in one launch."""
+    n = (mib << 20) // 4
+    nsets = max(2, math.ceil(3 * MALL_BYTES / (2 * n * 4)))
+    bufs = [(torch.ones(n, dtype=torch.float32, device="cuda"),
+             torch.empty(n, dtype=torch.float32, device="cuda")) for _ in range(nsets)]
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        src, dst = bufs[i % nsets]
+        torch.neg(src, out=dst)
+
+    for i in range(3):
+        call(i)
+    ms, _ = _timed(call, 3, steps, stream, torch)
+    del bufs
+    return 2 * (n * 4) / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(inp, max_units=None):
     """The fp64 oracle (as is) over (batch, head) units on a thread pool of host cores."""
     import concurrent.futures
@@ -515,9 +537,13 @@ def main():
                        "call_ms_mean": r2["call_ms_mean"], "achieved_GBs": a2,
                        "hbm_frac": a2 / HBM_PEAK_GBS}
         rv = time_verify(max(10, args.steps), 3, bd, inputs, torch)
+        # the verify step moves one 64 MiB state each way: the same-size copy is its
+        # practical ceiling
+        same = copy_bandwidth_rotated(torch, 64, max(10, args.steps))
         out["verify"] = {"workload": "verify_b32_K4", "GB_per_s": rv["gbs"],
                          "hbm_frac": rv["gbs"] / HBM_PEAK_GBS, "call_ms_mean": rv["call_ms_mean"],
-                         "alg_bytes": rv["alg_bytes"]}
+                         "alg_bytes": rv["alg_bytes"], "same_size_copy_GBs": same,
+                         "frac_of_same_size_copy": rv["gbs"] / same}
         r1 = time_verify(max(10, args.steps), 3, bd, inputs, torch, K=1)
         out["decode_K1"] = {"workload": "verify_b32_K4 with K=1", "GB_per_s": r1["gbs"],
                             "hbm_frac": r1["gbs"] / HBM_PEAK_GBS,
