@@ -579,7 +579,7 @@ def main():
                            "call_ms_mean": rb["call_ms_mean"], "alg_bytes": rb["alg_bytes"],
                            "achieved_GBs": ab, "hbm_frac": ab / HBM_PEAK_GBS,
                            "workspace_bytes": rb["workspace_bytes"],
-                           "kernels": "k_bwd_chain<N> (both walks), k_bwd_chunk_bf<N>, "
+                           "kernels": "k_bwd_chain<N, 2> (both walks), k_bwd_chunk_bf<N>, "
                                       "k_bwd_reduce_bc, k_bwd_reduce_h"}
     if args.sweep:
         sw = {}

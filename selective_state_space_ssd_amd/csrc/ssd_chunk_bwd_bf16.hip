@@ -6,8 +6,9 @@
 // reverse; intermediate states recomputed rather than stored, "另辟蹊径--Mamba介绍",
 // «Hardware-aware Algorithm»), organised for fewer HBM bytes:
 //
-//   k_bwd_chain    one workgroup per (head, batch) walks the 64-token chunks in
-//                  order (forward) or in reverse, keeping the P x N state in MFMA
+//   k_bwd_chain    one workgroup walks the 64-token chunks of one batch row in order
+//                  (forward, two heads of a group when the group has an even number
+//                  of heads) or in reverse (one head), keeping the P x N state in MFMA
 //                  accumulators: the forward walk writes the state entering each chunk,
 //                  Hin_c; the reverse walk writes the gradient of the state leaving it,
 //                  Gh_c, and finally d init_state.  Each chunk's contribution
