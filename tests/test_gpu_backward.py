@@ -53,9 +53,11 @@ def _assert(errs, tol):
 
 
 # Several 64-token chunks with ragged last ones, initial states, final-state gradients
-# or none, P in {32, 64}, N from 16 to 128, groups of 1, 2, 4 and 12 heads, both
+# or none, P in {32, 64}, N from 16 to 128, groups of 1, 2, 3, 4 and 12 heads, both
 # dtypes; bf16 with P = 64 and N in {64, 128} takes the bf16 matrix-core path (blocks
-# of up to 8 heads of a group per workgroup), the rest the fp32 path.
+# of up to 8 heads of a group per workgroup; forward state walks over two heads of a
+# group when the group has an even number of heads, one otherwise), the rest the fp32
+# path.
 SMALL = [
     # b,  L,  H,  P,   N, G,  io,    init, final
     (2, 300, 4, 64, 128, 2, "bf16", True, True),
@@ -67,6 +69,8 @@ SMALL = [
     (2, 517, 4, 64, 128, 1, "f32", True, True),
     (1, 190, 12, 64, 64, 1, "bf16", True, True),      # blocks of 6 heads
     (2, 129, 2, 64, 128, 2, "bf16", False, False),    # one head per group
+    (1, 200, 3, 64, 64, 1, "bf16", True, True),       # odd group: one head per forward walk
+    (2, 150, 6, 64, 128, 2, "bf16", True, False),     # odd groups of 3, two groups
 ]
 
 
