@@ -32,7 +32,8 @@
  * ---------------------------------------
  * - Every array pointer is a DEVICE pointer to row-major contiguous memory, owned
  *   by the caller.  The library never allocates or frees device memory and keeps
- *   no global state; calls are re-entrant and thread-safe.
+ *   no global state; calls are re-entrant and thread-safe, except that calls sharing
+ *   one chunk-scan workspace must not overlap in time.
  * - x, B, C and y have the I/O element type `io` (fp32 or bf16 bit patterns);
  *   dt, A, D and every state are fp32; accept_len is int32.
  * - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream) and
@@ -81,22 +82,51 @@ size_t ssd_chunk_scan_workspace_bytes(int b, int L, int H, int P, int N, int G, 
 /*
  * ssd_chunk_scan_workspace_init -- prepare a workspace once, before its first use
  * by ssd_chunk_scan_fwd (enqueued on hip_stream; workspace_bytes as allocated, at
- * least what the calls need, 16-byte aligned).
+ * least what the calls need, 16-byte aligned).  This call is required: without it
+ * the chunk-to-chunk hand-off of the bf16 single-pass kernel never reads as ready.
  *
- * The bf16 chunk scan hands each chunk's state to the next chunk through the
- * workspace: a work-item ticket and one ready flag per (batch, head, chunk).  This
- * call zeroes them (and writes a marker); every ssd_chunk_scan_fwd call that
- * completes leaves them zero again, so a prepared workspace serves any number of
- * later calls, of any shape that fits, one at a time (calls that overlap on one
- * workspace race).  A call that finds the workspace not prepared does not wait:
- * the outputs of every chunk after the first then hold NaN.  After a call that
+ * Step 3 of the chunked scan (the state passed from chunk to chunk, Mamba-2 article,
+ * «SSD 算法：分块和形态传递») runs as a hand-off between workgroups through the
+ * workspace: a 256-byte header (a work-item ticket and call number, an error word, a
+ * preparation marker) and one ready flag per (batch, head, chunk).  This call zeroes
+ * the workspace and writes the marker.  Each ssd_chunk_scan_fwd call takes a new
+ * call number, tags the flags it raises with it, and leaves the ticket at zero when it
+ * completes; flags of earlier calls therefore never read as ready, and one prepared
+ * workspace serves any number of later calls of any shape and I/O type that fits
+ * (the fp32 / other-P path keeps its buffers after the header).  Calls that share a
+ * workspace must run one at a time (same stream, or ordered by events): calls that
+ * overlap on one workspace race.  A call that finds the workspace not prepared does
+ * not wait: the outputs of every chunk after the first then hold NaN.  A call that
  * timed out waiting for a neighbouring chunk (the device broke its forward-progress
- * guarantee; the affected outputs are NaN), or that was aborted, prepare the
- * workspace again.  Returns SSD_ERR_NULL_ARG for a NULL workspace with
- * workspace_bytes > 0, SSD_ERR_ALIGN, or SSD_ERR_HIP.
+ * guarantee) completes with NaN in the affected outputs and sets the workspace's
+ * error word (read it with ssd_chunk_scan_workspace_error); the workspace stays
+ * usable.  After a call that was aborted mid-way, prepare the workspace again.
+ * Returns SSD_ERR_NULL_ARG for a NULL workspace with workspace_bytes > 0,
+ * SSD_ERR_ALIGN, or SSD_ERR_HIP.
  */
 ssd_status_t ssd_chunk_scan_workspace_init(void *workspace, size_t workspace_bytes,
                                            void *hip_stream);
+
+/*
+ * ssd_chunk_scan_workspace_error -- copy the time-out error word of a prepared
+ * chunk-scan workspace to err_out, and optionally clear it.
+ *
+ * The word is 0 while no chunk of any ssd_chunk_scan_fwd call on this workspace (since
+ * it was prepared or last cleared) gave up waiting for the state of the chunk before
+ * it; 1 once one did (its state and outputs were written as NaN).  A healthy device
+ * never sets it: the wait only ends this way if the device breaks its forward-progress
+ * guarantee.
+ *   workspace, workspace_bytes  the workspace (device, 16-byte aligned, at least the
+ *                               256-byte header)
+ *   err_out   device int32, written
+ *   clear     nonzero: reset the word to 0 after copying it
+ * Enqueued on hip_stream, ordered after the calls it should observe; allocates
+ * nothing.  Returns SSD_ERR_NULL_ARG, SSD_ERR_ALIGN (workspace 16 B, err_out 4 B),
+ * SSD_ERR_WORKSPACE (fewer than 256 bytes), SSD_ERR_ALIAS (err_out inside the header)
+ * or SSD_ERR_HIP.
+ */
+ssd_status_t ssd_chunk_scan_workspace_error(void *workspace, size_t workspace_bytes,
+                                            int32_t *err_out, int clear, void *hip_stream);
 
 /*
  * ssd_chunk_scan_fwd -- SSD chunked scan over a whole sequence.

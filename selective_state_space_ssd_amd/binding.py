@@ -29,7 +29,7 @@ STATUS_NAMES = {
 
 # Every symbol declared in include/ssd_mi355x.h
 EXPORTED = ("ssd_chunk_scan_workspace_bytes", "ssd_chunk_scan_workspace_init",
-            "ssd_chunk_scan_fwd", "ssd_verify_step", "ssd_selective_scan_fwd",
+            "ssd_chunk_scan_workspace_error", "ssd_chunk_scan_fwd", "ssd_verify_step", "ssd_selective_scan_fwd",
             "ssd_chunk_scan_bwd_workspace_bytes", "ssd_chunk_scan_bwd",
             "ssd_verify_ring_init", "ssd_verify_ring", "ssd_verify_ring_rollback",
             "ssd_seq_total_decay", "ssd_seq_combine", "ssd_seq_apply_state",
@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
         L.ssd_chunk_scan_workspace_bytes.restype = sz
         L.ssd_chunk_scan_workspace_init.argtypes = [vp, sz, vp]
         L.ssd_chunk_scan_workspace_init.restype = i32
+        L.ssd_chunk_scan_workspace_error.argtypes = [vp, sz, vp, i32, vp]
+        L.ssd_chunk_scan_workspace_error.restype = i32
         L.ssd_chunk_scan_fwd.argtypes = [vp] * 9 + [i32] * 7 + [i32, vp, sz, vp]
         L.ssd_chunk_scan_fwd.restype = i32
         L.ssd_verify_step.argtypes = [vp] * 12 + [i32] * 6 + [i32, vp]
@@ -136,6 +138,17 @@ def ssd_chunk_scan_workspace_init(workspace: torch.Tensor, stream=None) -> None:
                                              _stream(stream))
     if st != 0:
         raise SSDError(st, "ssd_chunk_scan_workspace_init")
+
+
+def ssd_chunk_scan_workspace_error(workspace: torch.Tensor, err_out: torch.Tensor, clear=False,
+                                   stream=None) -> None:
+    """Enqueue a copy of the workspace's time-out error word into ``err_out`` (an int32
+    GPU tensor of at least one element); ``clear`` resets the word afterwards."""
+    st = lib().ssd_chunk_scan_workspace_error(
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(err_out, "err_out", torch.int32), 1 if clear else 0, _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_chunk_scan_workspace_error")
 
 
 def ssd_chunk_scan_fwd(x, dt, A, B, C, D, init_state, y, final_state, Q, workspace,

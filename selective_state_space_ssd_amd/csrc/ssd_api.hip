@@ -61,6 +61,17 @@ ssd_status_t ssd_chunk_scan_workspace_init(void *workspace, size_t workspace_byt
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 
+ssd_status_t ssd_chunk_scan_workspace_error(void *workspace, size_t workspace_bytes,
+                                            int32_t *err_out, int clear, void *hip_stream) {
+    if (!workspace || !err_out) return SSD_ERR_NULL_ARG;
+    if (!aligned(workspace, 16) || !aligned(err_out, 4)) return SSD_ERR_ALIGN;
+    if (workspace_bytes < ssd::kWsHeaderBytes) return SSD_ERR_WORKSPACE;
+    if (Range(workspace, ssd::kWsHeaderBytes).overlaps(Range(err_out, 4))) return SSD_ERR_ALIAS;
+    const hipError_t e = ssd::launch_workspace_error(workspace, err_out, clear != 0,
+                                                     static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
 ssd_status_t ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, const void *B,
                                 const void *C, const float *D, const float *init_state, void *y,
                                 float *final_state, int b, int L, int H, int P, int N, int G,

@@ -33,6 +33,7 @@
 // Step 1, 2 and 4 contractions use v_mfma_f32_16x16x32_bf16 with fp32 accumulation;
 // the in-chunk decay cumsum is a wavefront scan.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 
 #include "ssd_device.h"
@@ -830,20 +831,44 @@ int heads_per_workgroup(int b, int H, int G, int nc, int slots, int wg_per_cu) {
     return best;
 }
 
+// Per-device values the launch needs, read from the runtime once per device and then
+// kept: the CU count, and whether the kernel's LDS limit has been raised.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+hipError_t device_cu_count(int dev, int *cus) {
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int c = g_cu_count[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *cus = c;
+            return hipSuccess;
+        }
+    }
+    const hipError_t e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess && dev >= 0 && dev < kMaxDevices && *cus > 0)
+        g_cu_count[dev].store(*cus, std::memory_order_relaxed);
+    return e;
+}
+
 template <int Q, int N>
 hipError_t launch_fused_qn(const ChunkScanArgs &a, const FusedPlan &fp, hipStream_t stream) {
     using F = Fz<Q, N>;
+    static std::atomic<bool> lds_set[kMaxDevices];
     char *ws = static_cast<char *>(a.workspace);
     uint32_t *hdr = reinterpret_cast<uint32_t *>(ws + fp.off_hdr);
     uint32_t *flags = reinterpret_cast<uint32_t *>(ws + fp.off_flags);
     float *hbuf = reinterpret_cast<float *>(ws + fp.off_hbuf);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_ssd_fused<Q, N>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, int(F::kLds));
-    if (e != hipSuccess) return e;
     int dev = 0, cus = 0;
-    e = hipGetDevice(&dev);
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const bool cached = dev >= 0 && dev < kMaxDevices;
+    if (!cached || !lds_set[dev].load(std::memory_order_acquire)) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_ssd_fused<Q, N>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(F::kLds));
+        if (e != hipSuccess) return e;
+        if (cached) lds_set[dev].store(true, std::memory_order_release);
+    }
+    e = device_cu_count(dev, &cus);
     if (e != hipSuccess) return e;
     const int HB = heads_per_workgroup(a.b, a.H, a.G, fp.nc, std::max(1, cus) * F::kWgPerCu,
                                        F::kWgPerCu);
@@ -905,6 +930,25 @@ __global__ void k_workspace_init(uint32_t *ws, size_t words) {
 }
 }  // namespace
 
+namespace {
+// One lane copies the header's time-out error word to the caller's word and, when
+// asked, clears it (device-scope accesses, as the scan's own writer uses).
+__global__ void k_workspace_error(uint32_t *hdr, int32_t *err_out, int clear) {
+    if (threadIdx.x != 0) return;
+    const uint32_t v =
+        __hip_atomic_load(&hdr[kWsErrorWord], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    err_out[0] = int32_t(v);
+    if (clear) __hip_atomic_store(&hdr[kWsErrorWord], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+}  // namespace
+
+hipError_t launch_workspace_error(void *workspace, int32_t *err_out, bool clear,
+                                  hipStream_t stream) {
+    hipLaunchKernelGGL(k_workspace_error, dim3(1), dim3(64), 0, stream,
+                       static_cast<uint32_t *>(workspace), err_out, clear ? 1 : 0);
+    return hipGetLastError();
+}
+
 hipError_t launch_workspace_init(void *workspace, size_t bytes, hipStream_t stream) {
     const size_t words = bytes / 4;
     if (words == 0) return hipSuccess;
@@ -927,7 +971,7 @@ FusedPlan plan_fused(int b, int L, int H, int P, int N, int G, int Q, bool bf16)
     const size_t items = size_t(b) * H * fp.nc;   // upper bound (one head per workgroup)
     if (items > 0x7fffffffu) return fp;
     fp.off_hdr = 0;
-    fp.off_flags = 256;
+    fp.off_flags = kWsHeaderBytes;
     fp.off_hbuf = fp.off_flags + align256(size_t(b) * H * fp.nc * 4);
     fp.total = fp.off_hbuf + align256(size_t(b) * H * 2 * size_t(P) * N * 4);
     fp.lds = lds;

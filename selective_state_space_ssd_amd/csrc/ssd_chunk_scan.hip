@@ -357,8 +357,11 @@ ChunkScanPlan plan_chunk_scan(int b, int L, int H, int P, int N, int G, int Q, b
     pl.nc = (L + Q - 1) / Q;
     const size_t io = bf16 ? 2 : 4;
     const size_t units = size_t(b) * H * pl.nc;
-    pl.off_states = 0;
-    pl.off_alpha = align256(units * size_t(P) * N * 4);
+    // the first kWsHeaderBytes hold the header of the single-pass kernel (ticket and
+    // call number, error word, preparation marker): a workspace prepared once keeps
+    // it whichever kernel a later call runs
+    pl.off_states = kWsHeaderBytes;
+    pl.off_alpha = pl.off_states + align256(units * size_t(P) * N * 4);
     pl.off_hprev = pl.off_alpha + align256(units * 4);
     pl.total = pl.off_hprev + align256(units * size_t(P) * N * io);
     if (bf16) {

@@ -96,8 +96,12 @@ ChunkScanPlan plan_chunk_scan(int b, int L, int H, int P, int N, int G, int Q, b
 // hand-off.  Header words: 0 = work-item count and 1 = call number (one 64-bit
 // word), 2 = time-out error word, 32 = magic word (its own cache line).
 // ssd_chunk_scan_workspace_init zeroes it and writes the magic word; every completed
-// call leaves the count at zero and advances the call number, which tags its flags.
+// call leaves the count at zero and advances the call number, and its ready flags
+// hold that call's tag (call number + 1), which no later call waits for.  The
+// three-kernel path keeps its buffers after the header, so a prepared workspace stays
+// prepared whichever path a call takes.
 constexpr uint32_t kWsMagic = 0x55d5ca11u;
+constexpr size_t kWsHeaderBytes = 256;   // reserved by both chunk-scan layouts
 constexpr int kWsErrorWord = 2;
 constexpr int kWsMagicWord = 32;
 struct FusedPlan {
@@ -185,5 +189,8 @@ hipError_t launch_copy_state(const float *init_state, float *final_state, size_t
                              hipStream_t stream);
 // Zero the workspace and write the magic word.
 hipError_t launch_workspace_init(void *workspace, size_t bytes, hipStream_t stream);
+// err_out[0] = the header's time-out error word; cleared afterwards when asked.
+hipError_t launch_workspace_error(void *workspace, int32_t *err_out, bool clear,
+                                  hipStream_t stream);
 
 }  // namespace ssd

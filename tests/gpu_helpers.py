@@ -1,5 +1,8 @@
 """Shared helpers of the GPU parity tests: run the HIP library through the binding,
 run the oracle on the same seeded inputs, and compare."""
+import concurrent.futures
+import os
+
 import numpy as np
 import torch
 
@@ -25,12 +28,25 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def run_scan(inp, device="cuda", workspace=None):
+def workspace_error(ws) -> int:
+    """The workspace's hand-off time-out word, read through the C ABI (0 = healthy)."""
+    err = torch.full((1,), -1, dtype=torch.int32, device=ws.device)
+    bd.ssd_chunk_scan_workspace_error(ws, err)
+    torch.cuda.synchronize()
+    return int(err.item())
+
+
+def run_scan(inp, device="cuda", workspace=None, check_error_word=True):
     dev = lambda a: bd.to_device(a, device)
     x, dt, A, B, C, D = (dev(getattr(inp, n)) for n in ("x", "dt", "A", "B", "C", "D"))
     init = dev(inp.init_state)
+    if workspace is None:
+        workspace = bd.chunk_scan_workspace(x, B, inp.Q)
     y, fs = bd.chunk_scan_fwd(x, dt, A, B, C, D, inp.Q, init_state=init, workspace=workspace)
     torch.cuda.synchronize()
+    if check_error_word and workspace.numel() >= 256:
+        # no chunk of a healthy call gives up waiting for its predecessor's state
+        assert workspace_error(workspace) == 0
     return y, fs
 
 
@@ -56,3 +72,41 @@ def scan_errors(inp, y, fs, units=None):
         ey = max(ey, slice_err(yg[bi, :, h], yo[bi, :, h], (0, 1)))
         ef = max(ef, slice_err(fg[bi, h], fo[bi, h], (0, 1)))
     return ey, ef
+
+
+def oracle_threads() -> int:
+    """Host threads for the oracle: the cores this process may use, at most 16 (a
+    GPU machine's share of its host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def scan_errors_all_units(inp, y, fs, threads=None):
+    """Slice errors of y and final_state against the oracle over EVERY (batch, head)
+    unit.  Each unit runs through the oracle on its own slice of the inputs (one batch
+    row, one head, its group's B and C), on a thread pool; returns (err_y, err_final,
+    units compared)."""
+    d = inp.dims
+    b, H, G = d["b"], d["H"], d["G"]
+    hpg = H // G
+    x, dt, A, B, C, D = (getattr(inp, n).f64() for n in ("x", "dt", "A", "B", "C", "D"))
+    init = None if inp.init_state is None else inp.init_state.f64()
+    yg, fg = to_f64(y), to_f64(fs)
+
+    def one(u):
+        bi, h = divmod(u, H)
+        g = h // hpg
+        sl = lambda a: np.ascontiguousarray(a)
+        yo, fo = oracle.scan_f64(sl(x[bi:bi + 1, :, h:h + 1]), sl(dt[bi:bi + 1, :, h:h + 1]),
+                                 A[h:h + 1], sl(B[bi:bi + 1, :, g:g + 1]),
+                                 sl(C[bi:bi + 1, :, g:g + 1]), D[h:h + 1],
+                                 None if init is None else sl(init[bi:bi + 1, h:h + 1]))
+        return (slice_err(yg[bi, :, h], yo[0, :, 0], (0, 1)),
+                slice_err(fg[bi, h], fo[0, 0], (0, 1)))
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=threads or oracle_threads()) as ex:
+        errs = list(ex.map(one, range(b * H)))
+    return max(e[0] for e in errs), max(e[1] for e in errs), len(errs)

@@ -52,7 +52,10 @@ def test_workspace_bytes(lib):
     # fp32 I/O: three-kernel path, fp32 chunk states + per-chunk decay + entering states
     n32 = bd.ssd_chunk_scan_workspace_bytes(b, L, H, P, N, G, Q, bd.SSD_DTYPE_F32)
     units = b * H * (L // Q)
-    assert units * P * N * 8 + units * 4 <= n32 < units * P * N * 8 + units * 4 + 3 * 256
+    # (after the same 256-byte header, which a prepared workspace keeps whichever path
+    # a call takes)
+    base = 256 + units * P * N * 8 + units * 4
+    assert base <= n32 < base + 3 * 256
     assert bd.ssd_chunk_scan_workspace_bytes(0, L, H, P, N, G, Q, 1) == 0
     assert bd.ssd_chunk_scan_workspace_bytes(b, 0, H, P, N, G, Q, 1) == 0
     with pytest.raises(bd.SSDError):
@@ -111,6 +114,29 @@ def test_workspace_init_checks(lib):
     assert lib.ssd_chunk_scan_workspace_init(None, 0, None) == OK          # nothing to do
     assert lib.ssd_chunk_scan_workspace_init(None, 4096, None) == NULL
     assert lib.ssd_chunk_scan_workspace_init(addr(9, 8), 4096, None) == ALIGN
+
+
+def test_workspace_error_checks(lib):
+    err = addr(11)
+    assert lib.ssd_chunk_scan_workspace_error(None, 4096, err, 0, None) == NULL
+    assert lib.ssd_chunk_scan_workspace_error(addr(9), 4096, None, 0, None) == NULL
+    assert lib.ssd_chunk_scan_workspace_error(addr(9, 8), 4096, err, 0, None) == ALIGN
+    assert lib.ssd_chunk_scan_workspace_error(addr(9), 4096, addr(11, 2), 0, None) == ALIGN
+    assert lib.ssd_chunk_scan_workspace_error(addr(9), 255, err, 1, None) == WS
+    assert lib.ssd_chunk_scan_workspace_error(addr(9), 0, err, 1, None) == WS
+    # err_out inside the 256-byte header
+    assert lib.ssd_chunk_scan_workspace_error(addr(9), 4096, addr(9, 8), 0, None) == ALIAS
+    assert lib.ssd_chunk_scan_workspace_error(addr(9), 4096, addr(9, 252), 1, None) == ALIAS
+
+
+def test_scan_q256_n256_p64_is_unsupported(lib):
+    # Q = 256 with N = 256 at P = 64 fits neither kernel's LDS (160 KiB per CU): the
+    # call is refused on the host, before anything is enqueued
+    dims = dict(b=1, L=600, H=2, P=64, N=256, G=1, Q=256)
+    assert scan_call(lib, dims=dims, io=1) == UNSUP
+    # Q = 128 is supported: the same call gets past that check and stops at the next
+    # one (a workspace too small), still before any launch
+    assert scan_call(lib, dims=dict(dims, Q=128), io=1, ws_bytes=1) == WS
 
 
 def test_scan_workspace_checks(lib):

@@ -3,7 +3,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import TOL, oracle_scan, run_scan, scan_errors, to_f64
+from gpu_helpers import (TOL, oracle_scan, run_scan, scan_errors, scan_errors_all_units,
+                         to_f64)
 from selective_state_space_ssd_amd import binding as bd
 from selective_state_space_ssd_amd import inputs
 
@@ -48,17 +49,67 @@ def test_small_cases_full_oracle(case):
     _check(inputs.make_scan_inputs(b, L, H, P, N, G, Q, io=io, init=init, seed=L + N + P))
 
 
+def fused_workspace_bytes(b, L, H, P, N, Q):
+    """Workspace of the single-pass bf16 kernel: the 256-byte header, one ready flag per
+    (batch, head, chunk) and a two-slot fp32 state ring per (batch, head), each part
+    rounded up to 256 bytes."""
+    up = lambda v: (v + 255) // 256 * 256
+    nc = (L + Q - 1) // Q
+    return 256 + up(b * H * nc * 4) + up(b * H * 2 * P * N * 4)
+
+
+# Every (Q, N) instantiation of the single-pass kernel that ssd_chunk_scan_fwd
+# dispatches (bf16 I/O, P = 64): three chunks with a ragged last one, a nonzero initial
+# state, two groups of two heads, two batch rows.
+FUSED_QN = [(q, n) for q in (64, 128, 256) for n in (16, 32, 64, 128, 256)
+            if (q, n) != (256, 256)]
+
+
+@pytest.mark.parametrize("qn", FUSED_QN, ids=lambda c: f"Q{c[0]}N{c[1]}")
+def test_every_fused_instantiation_full_oracle(qn):
+    Q, N = qn
+    b, L, H, P, G = 2, 2 * Q + Q // 2 + 7, 4, 64, 2
+    # the call takes the single-pass kernel: its workspace layout is the one asked for
+    assert bd.ssd_chunk_scan_workspace_bytes(b, L, H, P, N, G, Q, bd.SSD_DTYPE_BF16) == \
+        fused_workspace_bytes(b, L, H, P, N, Q)
+    _check(inputs.make_scan_inputs(b, L, H, P, N, G, Q, io="bf16", init=True, seed=1000 + Q + N))
+
+
 FULL = ["mamba2_2p7b_L2k", "mamba2_2p7b_L16k", "dstate_sweep_N16", "dstate_sweep_N64",
         "dstate_sweep_N128", "dstate_sweep_N256"]
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_workloads_sampled_heads(name):
+def test_full_size_workloads_every_unit(name):
+    """The full-size layers in the launch configuration the benchmark times, compared
+    with the oracle on every (batch, head) unit."""
     inp = inputs.make_workload(name)
-    d = inp.dims
-    nu = d["b"] * d["H"]
-    units = sorted({0, nu // 2 + 1, nu - 1})
-    _check(inp, units=units)
+    y, fs = run_scan(inp)
+    ey, ef, n = scan_errors_all_units(inp, y, fs)
+    tol = TOL[inp.io]
+    print(f"  {n} units: y err {ey:.3e}  final_state err {ef:.3e}  (tol {tol})", flush=True)
+    assert n == inp.dims["b"] * inp.dims["H"]
+    assert np.isfinite(ey) and np.isfinite(ef)
+    assert ey <= tol and ef <= tol
+
+
+def test_prepared_workspace_serves_both_paths():
+    """One workspace prepared once, used by a three-kernel call (fp32 I/O, then bf16
+    with P = 32) and then by single-pass bf16 P = 64 calls: the header stays intact, so
+    the single-pass calls hand their states over and match the oracle."""
+    cases = [(1, 300, 4, 64, 64, 1, 128, "f32"), (2, 700, 8, 64, 128, 2, 256, "bf16"),
+             (1, 517, 2, 32, 64, 1, 128, "bf16"), (2, 700, 8, 64, 128, 2, 256, "bf16")]
+    need = max(bd.ssd_chunk_scan_workspace_bytes(b, L, H, P, N, G, Q,
+                                                 bd.SSD_DTYPE_BF16 if io == "bf16" else
+                                                 bd.SSD_DTYPE_F32)
+               for b, L, H, P, N, G, Q, io in cases)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    bd.ssd_chunk_scan_workspace_init(ws)
+    for i, (b, L, H, P, N, G, Q, io) in enumerate(cases):
+        inp = inputs.make_scan_inputs(b, L, H, P, N, G, Q, io=io, init=True, seed=200 + i)
+        y, fs = run_scan(inp, workspace=ws)
+        ey, ef = scan_errors(inp, y, fs)
+        assert ey <= TOL[io] and ef <= TOL[io], (i, ey, ef)
 
 
 def test_run_to_run_bitwise_determinism():
@@ -156,7 +207,7 @@ def test_unprepared_workspace_gives_nan_not_garbage():
     inp = inputs.make_scan_inputs(1, 512, 4, 64, 128, 1, 256, io="bf16", init=False, seed=12)
     n = bd.ssd_chunk_scan_workspace_bytes(1, 512, 4, 64, 128, 1, 256, bd.SSD_DTYPE_BF16)
     ws = torch.zeros(n, dtype=torch.uint8, device="cuda")     # zero, but no marker
-    y, fs = run_scan(inp, workspace=ws)
+    y, fs = run_scan(inp, workspace=ws, check_error_word=False)
     yo = to_f64(y)
     ref, _ = oracle_scan(inp)
     first = yo[:, :256]
