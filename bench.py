@@ -10,14 +10,28 @@ rotate over several identical copies of the inputs whose total exceeds the cache
 
 Printed: one JSON line with the contract fields plus
   roofline      algorithmic bytes of one call / its mean duration (HIP events on the
-                launch stream around the timed calls), against 8 TB/s; "traffic" is the measured HBM
-                bytes per call from the committed counter summary in profiles/, used
-                only while the kernel source still hashes to what was profiled
-  cpu_baseline  the fp64 CPU oracle timed on this host's cores
+                launch stream around the K timed calls), against 8 TB/s; "traffic" is
+                the measured HBM bytes per call from the committed counter summary in
+                profiles/, used only while the kernel source still hashes to what was
+                profiled
+  call_stats_us median, 10th and 90th percentile of per-call durations, from a second
+                pass of at least 50 calls with an event before each (so the event
+                records stay out of the K timed steps)
+  device        CU count and maximum engine clock of the GPU (rocminfo)
+  scan_configs  the other chunk-scan configs of the workload list, each with its own
+                tokens/s, call statistics and roofline object: the long-context layer
+                (L=16384, nonzero initial state) and the state-size sweep (b=8, L=4096,
+                H=32, G=4, Q=128, N in {16, 64, 128, 256})
+  cpu_baseline  the fp64 CPU oracle as it stands, on a bounded sample of the headline
+                workload: one run on 1 thread and one on the host pool (the box's share,
+                at most 16 threads), with the CPU model and core counts; the pool run's
+                outputs are compared with the timed GPU call's (parity_vs_timed_call)
+  cpu_baseline_configs
+                the same on 16 units of every other chunk-scan config
+  parity_ok     every oracle comparison above within its tolerance
   cpu_oracle_extras
                 the verify, comparison-scan and gradient oracles timed on bounded
                 samples of their legs' workloads
-  L16k          the long-context layer (L=16384, nonzero initial state)
   verify        the K=4 verify step (GB/s of algorithmic bytes), beside an elementwise
                 kernel that reads and writes the same 64 MiB (inputs rotated alike)
   selective_scan_comparison
@@ -116,7 +130,7 @@ def _copies(inp, count, bd):
     return sets
 
 
-def time_scan(name, steps, warmup, bd, inputs, torch):
+def time_scan(name, steps, warmup, bd, inputs, torch, stats_calls=50):
     inp = inputs.make_workload(name)
     d = inp.dims
     io_bytes = 2 if inp.io == "bf16" else 4
@@ -138,8 +152,17 @@ def time_scan(name, steps, warmup, bd, inputs, torch):
     for i in range(warmup):
         call(i)
     mean_ms, wall = _timed(call, warmup, steps, stream, torch)
-    return dict(inp=inp, dims=d, alg_bytes=alg, flops=scan_alg_flops(d), wall_s=wall,
-                ms_per_step=wall * 1e3 / steps, call_ms_mean=mean_ms, nsets=nsets)
+    last = (warmup + steps - 1) % nsets          # the set the last timed call wrote
+    stats = _call_stats(call, warmup + steps, max(stats_calls, steps), stream, torch)
+    # outputs of one call for the oracle comparison: the stats pass ran after the timed
+    # calls, so run the last timed call's inputs once more into its own buffers
+    call(last)
+    err = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    bd.ssd_chunk_scan_workspace_error(ws, err)
+    torch.cuda.synchronize()
+    return dict(name=name, inp=inp, dims=d, alg_bytes=alg, flops=scan_alg_flops(d), wall_s=wall,
+                ms_per_step=wall * 1e3 / steps, call_ms_mean=mean_ms, nsets=nsets,
+                stats=stats, y=ys[last], final_state=fss[last], handoff_error=int(err.item()))
 
 
 def time_selective(name, steps, warmup, bd, inputs, torch):
@@ -181,6 +204,24 @@ def _timed(call, first, steps, stream, torch):
     return start.elapsed_time(end) / steps, wall
 
 
+def _call_stats(call, first, n, stream, torch):
+    """n more calls with a HIP event recorded on `stream` before each call and after the
+    last: per-call durations (event to event, so back-to-back launches) -> median, 10th
+    and 90th percentile in microseconds.  A separate pass from the K timed steps, so the
+    extra event records do not touch the headline timing."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(n):
+        call(first + i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    us = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n))
+    q = lambda f: us[min(n - 1, max(0, int(round(f * (n - 1)))))]
+    return {"calls": n, "median_us": q(0.5), "p10_us": q(0.1), "p90_us": q(0.9),
+            "min_us": us[0], "max_us": us[-1]}
+
+
 def time_verify(steps, warmup, bd, inputs, torch, K=None):
     v = inputs.make_workload("verify_b32_K4", **({} if K is None else {"K": K}))
     d = v.dims
@@ -204,7 +245,9 @@ def time_verify(steps, warmup, bd, inputs, torch, K=None):
     for i in range(warmup):
         call(i)
     mean_ms, _ = _timed(call, warmup, steps, stream, torch)
-    return dict(dims=d, alg_bytes=alg, call_ms_mean=mean_ms, gbs=alg / (mean_ms * 1e-3) / 1e9)
+    stats = _call_stats(call, warmup + steps, max(50, steps), stream, torch)
+    return dict(dims=d, alg_bytes=alg, call_ms_mean=mean_ms, gbs=alg / (mean_ms * 1e-3) / 1e9,
+                stats=stats)
 
 
 def bwd_alg_bytes(d, io_bytes, init, final):
@@ -354,27 +397,101 @@ def copy_bandwidth_rotated(torch, mib, steps):
     return 2 * (n * 4) / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(inp, max_units=None):
-    """The fp64 oracle (as is) over (batch, head) units on a thread pool of host cores."""
+def host_cpu():
+    """CPU model and the core counts the host reports (the box's share may be smaller
+    than os.cpu_count(): the oracle's pool uses the affinity count, at most 16)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cpus": affinity,
+            "pool_threads": max(1, min(16, affinity))}
+
+
+def _oracle_units(inp, units, threads):
+    """Run the fp64 oracle on the given (batch, head) units, each on its own slice of the
+    inputs (one batch row, one head, its group's B and C), on `threads` host threads.
+    Returns ({unit: (y [L, P], final_state [P, N])}, wall seconds)."""
     import concurrent.futures
+
+    import numpy as np
 
     import oracle
     d = inp.dims
-    units = d["b"] * d["H"]
-    sample = units if max_units is None else min(units, max_units)
-    threads = max(1, min(16, os.cpu_count() or 1, sample))
+    H, G = d["H"], d["G"]
+    hpg = H // G
     x, dt, A, B, C, D = (getattr(inp, k).f64() for k in ("x", "dt", "A", "B", "C", "D"))
     init = None if inp.init_state is None else inp.init_state.f64()
-    oracle.scan_f64(x[:, :8], dt[:, :8], A, B[:, :8], C[:, :8], D, init, bh_range=(0, 1))
+    sl = np.ascontiguousarray
+
+    def one(u):
+        bi, h = divmod(u, H)
+        g = h // hpg
+        y, fs = oracle.scan_f64(sl(x[bi:bi + 1, :, h:h + 1]), sl(dt[bi:bi + 1, :, h:h + 1]),
+                                A[h:h + 1], sl(B[bi:bi + 1, :, g:g + 1]),
+                                sl(C[bi:bi + 1, :, g:g + 1]), D[h:h + 1],
+                                None if init is None else sl(init[bi:bi + 1, h:h + 1]))
+        return u, (y[0, :, 0], fs[0, 0])
+
+    one(units[0])   # load the library, page in the inputs
     t0 = time.perf_counter()
     with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
-        list(ex.map(lambda u: oracle.scan_f64(x, dt, A, B, C, D, init, bh_range=(u, u + 1)),
-                    range(sample)))
-    wall = time.perf_counter() - t0
-    tokens = d["b"] * d["L"] * sample / units
-    return {"value": tokens / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{sample} of {units} (batch, head) units of the same workload, "
-                      f"tokens scaled by {sample}/{units}; wall {wall:.2f} s"}
+        res = dict(ex.map(one, units))
+    return res, time.perf_counter() - t0
+
+
+def _compare(res, y, fs, H, tol):
+    """Slice-normalised max errors of the GPU outputs against the oracle's, per unit."""
+    import numpy as np
+    yg = y.float().cpu().numpy().astype(np.float64)
+    fg = fs.cpu().numpy().astype(np.float64)
+    ey = ef = 0.0
+    for u, (yo, fo) in res.items():
+        bi, h = divmod(u, H)
+        ey = max(ey, float(np.max(np.abs(yg[bi, :, h] - yo)) / max(np.max(np.abs(yo)), 1e-30)))
+        ef = max(ef, float(np.max(np.abs(fg[bi, h] - fo)) / max(np.max(np.abs(fo)), 1e-30)))
+    ok = bool(np.isfinite(ey) and np.isfinite(ef) and ey <= tol and ef <= tol)
+    return {"units": len(res), "err_y": ey, "err_final_state": ef, "tol": tol, "ok": ok}
+
+
+def cpu_baseline(r, one_thread_units, all_units, host):
+    """The fp64 oracle as it stands, timed on the host cores on a bounded sample of the
+    workload: one run on 1 thread, one on the pool (up to 16 threads, the box's share).
+    The units of the pool run are also compared with the outputs of the timed GPU call
+    (slice-normalised max error, the tolerance the parity tests use)."""
+    inp, d = r["inp"], r["dims"]
+    units = d["b"] * d["H"]
+    tokens_per_unit = d["b"] * d["L"] / units
+    n1 = min(units, one_thread_units)
+    stride1 = max(1, units // n1)
+    u1 = list(range(0, units, stride1))[:n1]
+    _, w1 = _oracle_units(inp, u1, 1)
+    na = min(units, all_units)
+    stridea = max(1, units // na)
+    ua = list(range(0, units, stridea))[:na]
+    threads = host["pool_threads"]
+    resa, wa = _oracle_units(inp, ua, threads)
+    tol = 2e-2 if inp.io == "bf16" else 1e-4
+    return {"value": tokens_per_unit * len(ua) / wa, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(ua)} of {units} (batch, head) units of {d['b']}x{d['L']} tokens "
+                      f"on {threads} threads, tokens scaled by {len(ua)}/{units}; wall {wa:.2f} s",
+            "one_thread": {"value": tokens_per_unit * len(u1) / w1, "unit": "tokens/s",
+                           "cores": 1,
+                           "sample": f"{len(u1)} of {units} units, tokens scaled by "
+                                     f"{len(u1)}/{units}; wall {w1:.2f} s"},
+            "cpu_model": host["cpu_model"], "os_cpu_count": host["os_cpu_count"],
+            "affinity_cpus": host["affinity_cpus"],
+            "parity_vs_timed_call": _compare(resa, r["y"], r["final_state"], d["H"], tol)}
 
 
 def cpu_oracle_extras(inputs):
@@ -456,6 +573,52 @@ def cpu_oracle_extras(inputs):
     return out
 
 
+def device_info():
+    """CU count and maximum engine clock of the GPU agent, from rocminfo (run as a child
+    process before this process touches the GPU)."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return {}
+    info = {}
+    for agent in out.split("*******")[1:]:
+        if "gfx950" not in agent:
+            continue
+        for line in agent.splitlines():
+            key, _, val = line.strip().partition(":")
+            val = val.strip()
+            if key == "Compute Unit" and "compute_units" not in info:
+                info["compute_units"] = int(val.split()[0])
+            elif key == "Max Clock Freq. (MHz)" and "max_sclk_mhz" not in info:
+                info["max_sclk_mhz"] = int(val.split()[0])
+            elif key == "Marketing Name" and "name" not in info:
+                info["name"] = val
+        break
+    return info
+
+
+def scan_record(r, copy_gbs, traffic=None):
+    """One chunk-scan config: tokens/s, per-call statistics and its own roofline object
+    (algorithmic bytes of one call / the mean call time on the launch stream)."""
+    d = r["dims"]
+    achieved = r["alg_bytes"] / (r["call_ms_mean"] * 1e-3) / 1e9
+    tf = r["flops"] / (r["call_ms_mean"] * 1e-3) / 1e12
+    return {
+        "workload": r["name"],
+        "shape": {k: d[k] for k in ("b", "L", "H", "P", "N", "G", "Q")},
+        "tokens_per_s": d["b"] * d["L"] / (r["call_ms_mean"] * 1e-3),
+        "call_ms_mean": r["call_ms_mean"],
+        "call_stats_us": r["stats"],
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "alg_bytes_per_launch": r["alg_bytes"], "measured_copy_GBs": copy_gbs,
+                     "frac_of_measured_copy": achieved / copy_gbs,
+                     "mfma_tflops_alg": tf, "mfma_frac_alg": tf / BF16_PEAK_TFLOPS},
+        "handoff_error_word": r["handoff_error"],
+    }
+
+
 def _progress(msg):
     """One line per finished leg on stderr (stdout carries only the JSON line)."""
     print(f"bench: {msg}", file=sys.stderr, flush=True)
@@ -470,7 +633,6 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the L=16k and verify-step measurements")
-    ap.add_argument("--sweep", action="store_true", help="also time the dstate sweep")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="first run one elementwise kernel that reads and writes this many "
                          "MiB (a known-size reference for the HBM byte counters)")
@@ -479,6 +641,8 @@ def main():
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
+
+    dev_info = device_info()   # rocminfo, before this process touches the GPU
 
     import torch
 
@@ -500,7 +664,11 @@ def main():
     _progress(f"{args.workload} timed")
     d = r["dims"]
     tokens = d["b"] * d["L"]
-    achieved = r["alg_bytes"] / (r["call_ms_mean"] * 1e-3) / 1e9
+    copy_gbs = copy_bandwidth(torch)
+    head = scan_record(r, copy_gbs, measured_traffic())
+    roof = dict(head["roofline"])
+    roof["kernel"] = "ssd_chunk_scan_fwd = k_ssd_fused<256,128> (one launch per call)"
+    roof["call_ms_mean"] = r["call_ms_mean"]
     out = {
         "metric": METRIC,
         "value": tokens / (r["ms_per_step"] * 1e-3),
@@ -518,32 +686,44 @@ def main():
                    "nheads": d["H"], "headdim": d["P"], "dstate": d["N"], "ngroups": d["G"],
                    "chunk": d["Q"], "io": r["inp"].io, "state": "f32",
                    "input_copies_rotated": r["nsets"]},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "kernel": "ssd_chunk_scan_fwd = k_ssd_fused<256,128> (one launch per call)",
-                     "alg_bytes_per_launch": r["alg_bytes"],
-                     "call_ms_mean": r["call_ms_mean"],
-                     "measured_copy_GBs": copy_bandwidth(torch),
-                     "mfma_tflops_alg": r["flops"] / (r["call_ms_mean"] * 1e-3) / 1e12,
-                     "mfma_frac_alg": r["flops"] / (r["call_ms_mean"] * 1e-3) / 1e12 /
-                     BF16_PEAK_TFLOPS},
+        "roofline": roof,
+        "call_stats_us": r["stats"],
+        "handoff_error_word": r["handoff_error"],
+        "device": dev_info,
     }
+    scans = {args.workload: r}
     if not args.no_extra:
-        r2 = time_scan("mamba2_2p7b_L16k", max(5, args.steps // 3), 2, bd, inputs, torch)
-        _progress("mamba2_2p7b_L16k timed")
-        d2 = r2["dims"]
-        a2 = r2["alg_bytes"] / (r2["call_ms_mean"] * 1e-3) / 1e9
-        out["L16k"] = {"tokens_per_s": d2["b"] * d2["L"] / (r2["call_ms_mean"] * 1e-3),
-                       "call_ms_mean": r2["call_ms_mean"], "achieved_GBs": a2,
-                       "hbm_frac": a2 / HBM_PEAK_GBS}
+        # every chunk-scan config of the workload list: the long-context layer and the
+        # four state sizes of the sweep, each with its own roofline object
+        configs = {}
+        for name in ("mamba2_2p7b_L16k", "dstate_sweep_N16", "dstate_sweep_N64",
+                     "dstate_sweep_N128", "dstate_sweep_N256"):
+            if name == args.workload:
+                continue
+            rc = time_scan(name, max(5, args.steps // 2), 2, bd, inputs, torch)
+            scans[name] = rc
+            configs[name] = scan_record(rc, copy_gbs)
+            _progress(f"{name} timed")
+        out["scan_configs"] = configs
+        if "mamba2_2p7b_L16k" in configs:
+            c16 = configs["mamba2_2p7b_L16k"]
+            out["L16k"] = {"tokens_per_s": c16["tokens_per_s"],
+                           "call_ms_mean": c16["call_ms_mean"],
+                           "achieved_GBs": c16["roofline"]["achieved"],
+                           "hbm_frac": c16["roofline"]["frac"]}
+        r2 = scans.get("mamba2_2p7b_L16k")
         rv = time_verify(max(10, args.steps), 3, bd, inputs, torch)
         # the verify step moves one 64 MiB state each way: the same-size copy is its
         # practical ceiling
         same = copy_bandwidth_rotated(torch, 64, max(10, args.steps))
         out["verify"] = {"workload": "verify_b32_K4", "GB_per_s": rv["gbs"],
                          "hbm_frac": rv["gbs"] / HBM_PEAK_GBS, "call_ms_mean": rv["call_ms_mean"],
+                         "call_stats_us": rv["stats"],
                          "alg_bytes": rv["alg_bytes"], "same_size_copy_GBs": same,
-                         "frac_of_same_size_copy": rv["gbs"] / same}
+                         "frac_of_same_size_copy": rv["gbs"] / same,
+                         "roofline": {"bound": "hbm", "achieved": rv["gbs"],
+                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": rv["gbs"] / HBM_PEAK_GBS, "traffic": None}}
         r1 = time_verify(max(10, args.steps), 3, bd, inputs, torch, K=1)
         out["decode_K1"] = {"workload": "verify_b32_K4 with K=1", "GB_per_s": r1["gbs"],
                             "hbm_frac": r1["gbs"] / HBM_PEAK_GBS,
@@ -568,7 +748,8 @@ def main():
         sp = time_seqpar(max(10, args.steps), 3, bd, inputs, torch)
         _progress("sequence-parallel pieces timed")
         sp["workload"] = "mamba2_2p7b_L16k in 8 slices of 2048 tokens, one slice's share"
-        sp["monolithic_L16k_per_slice_us"] = r2["call_ms_mean"] * 1e3 / 8
+        if r2 is not None:
+            sp["monolithic_L16k_per_slice_us"] = r2["call_ms_mean"] * 1e3 / 8
         out["sequence_parallel"] = sp
         rb = time_backward(args.workload, max(5, args.steps // 3), 2, bd, inputs, torch)
         _progress("backward timed")
@@ -581,20 +762,26 @@ def main():
                            "workspace_bytes": rb["workspace_bytes"],
                            "kernels": "k_bwd_chain<N, 2> (both walks), k_bwd_chunk_bf<N>, "
                                       "k_bwd_reduce_bc, k_bwd_reduce_h"}
-    if args.sweep:
-        sw = {}
-        for n in (16, 64, 128, 256):
-            rs = time_scan(f"dstate_sweep_N{n}", max(5, args.steps // 3), 2, bd, inputs, torch)
-            ds = rs["dims"]
-            a = rs["alg_bytes"] / (rs["call_ms_mean"] * 1e-3) / 1e9
-            sw[f"N{n}"] = {"tokens_per_s": ds["b"] * ds["L"] / (rs["call_ms_mean"] * 1e-3),
-                           "call_ms_mean": rs["call_ms_mean"], "hbm_frac": a / HBM_PEAK_GBS}
-        out["dstate_sweep"] = sw
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(r["inp"])
-        _progress("oracle timed")
+        host = host_cpu()
+        out["cpu_baseline"] = cpu_baseline(r, 1 << 30, 1 << 30, host)
+        _progress("oracle timed on the headline workload")
         if not args.no_extra:
+            # the other chunk-scan configs: the oracle on 16 units each (pool threads),
+            # its outputs compared with the timed call's
+            per = {}
+            for name, rc in scans.items():
+                if name == args.workload:
+                    continue
+                cb = cpu_baseline(rc, 4, 16, host)
+                per[name] = {k: cb[k] for k in ("value", "unit", "cores", "sample",
+                                                "one_thread", "parity_vs_timed_call")}
+            out["cpu_baseline_configs"] = per
             out["cpu_oracle_extras"] = cpu_oracle_extras(inputs)
+            _progress("oracles timed on the other legs")
+        checks = [out["cpu_baseline"]["parity_vs_timed_call"]["ok"]] + [
+            v["parity_vs_timed_call"]["ok"] for v in out.get("cpu_baseline_configs", {}).values()]
+        out["parity_ok"] = all(checks)
     print(json.dumps(out), flush=True)
 
 
