@@ -169,6 +169,42 @@ ssd_status_t ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, 
                                 void *hip_stream);
 
 /*
+ * Bytes of the buffer ssd_chunk_scan_fwd_noalloc takes its workspace from (64 MiB, one
+ * per GPU).
+ */
+#define SSD_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+/*
+ * ssd_chunk_scan_fwd_noalloc -- ssd_chunk_scan_fwd for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.
+ *
+ * Same arguments (less the workspace), computation, results (bit for bit) and errors
+ * as ssd_chunk_scan_fwd.  The workspace is a buffer of SSD_NOALLOC_WORKSPACE_BYTES in
+ * the library's own device memory, one per GPU, which that GPU holds until the process
+ * ends.  The call allocates and frees nothing and calls no allocating routine.
+ * - A problem whose workspace (ssd_chunk_scan_workspace_bytes) exceeds that size is
+ *   refused with SSD_ERR_WORKSPACE before anything is enqueued.  For scale: the
+ *   2.7B-shaped layer (b 4, L 2048, H 80, P 64, N 128, bf16) needs 10.5 MB, and
+ *   b 8, L 4096, H 32, P 64, N 256, Q 128 (bf16) needs 34 MB.
+ * - The first call on a device prepares that device's buffer: it looks up the buffer's
+ *   address and enqueues a fill kernel on hip_stream ahead of the scan.  That first
+ *   call must not be made while hip_stream is being captured into a graph
+ *   (SSD_ERR_UNSUPPORTED, nothing enqueued); later calls may be captured.
+ * - Every call on a GPU shares that GPU's buffer, which keeps the last call's contents
+ *   (the hand-off protocol of ssd_chunk_scan_workspace_init leaves it ready for the
+ *   next call).  Calls on one GPU must therefore not overlap in time: issue them on one
+ *   stream, or order them with events.  Calls that overlap race.
+ * - A hand-off time-out (see ssd_chunk_scan_workspace_init) shows only as NaN outputs:
+ *   the buffer's error word is not exposed.
+ */
+ssd_status_t ssd_chunk_scan_fwd_noalloc(const void *x, const float *dt, const float *A,
+                                        const void *B, const void *C, const float *D,
+                                        const float *init_state, void *y, float *final_state,
+                                        int b, int L, int H, int P, int N, int G, int Q,
+                                        ssd_dtype_t io, void *hip_stream);
+
+/*
  * ssd_verify_step -- K draft tokens applied to an existing state.
  *
  * Mamba keeps only its current state, so a verifier that may reject part of the

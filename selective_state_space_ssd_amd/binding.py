@@ -29,7 +29,8 @@ STATUS_NAMES = {
 
 # Every symbol declared in include/ssd_mi355x.h
 EXPORTED = ("ssd_chunk_scan_workspace_bytes", "ssd_chunk_scan_workspace_init",
-            "ssd_chunk_scan_workspace_error", "ssd_chunk_scan_fwd", "ssd_verify_step", "ssd_selective_scan_fwd",
+            "ssd_chunk_scan_workspace_error", "ssd_chunk_scan_fwd",
+            "ssd_chunk_scan_fwd_noalloc", "ssd_verify_step", "ssd_selective_scan_fwd",
             "ssd_chunk_scan_bwd_workspace_bytes", "ssd_chunk_scan_bwd",
             "ssd_verify_ring_init", "ssd_verify_ring", "ssd_verify_ring_rollback",
             "ssd_seq_total_decay", "ssd_seq_combine", "ssd_seq_apply_state",
@@ -62,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.ssd_chunk_scan_workspace_error.restype = i32
         L.ssd_chunk_scan_fwd.argtypes = [vp] * 9 + [i32] * 7 + [i32, vp, sz, vp]
         L.ssd_chunk_scan_fwd.restype = i32
+        L.ssd_chunk_scan_fwd_noalloc.argtypes = [vp] * 9 + [i32] * 7 + [i32, vp]
+        L.ssd_chunk_scan_fwd_noalloc.restype = i32
         L.ssd_verify_step.argtypes = [vp] * 12 + [i32] * 6 + [i32, vp]
         L.ssd_verify_step.restype = i32
         L.ssd_selective_scan_fwd.argtypes = [vp] * 9 + [i32] * 5 + [i32, vp]
@@ -172,6 +175,26 @@ def ssd_chunk_scan_fwd(x, dt, A, B, C, D, init_state, y, final_state, Q, workspa
         workspace.element_size(), _stream(stream))
     if st != 0:
         raise SSDError(st, "ssd_chunk_scan_fwd")
+
+
+NOALLOC_WORKSPACE_BYTES = 64 << 20
+
+
+def ssd_chunk_scan_fwd_noalloc(x, dt, A, B, C, D, init_state, y, final_state, Q,
+                               stream=None) -> None:
+    """Enqueue the chunked scan with the library's own per-GPU workspace buffer (no
+    workspace argument, nothing allocated); arguments otherwise as ssd_chunk_scan_fwd."""
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    io = _io_code(x)
+    f32 = torch.float32
+    st = lib().ssd_chunk_scan_fwd_noalloc(
+        _ptr(x, "x", x.dtype), _ptr(dt, "dt", f32), _ptr(A, "A", f32), _ptr(B, "B", x.dtype),
+        _ptr(C, "C", x.dtype), _ptr(D, "D", f32), _ptr(init_state, "init_state", f32),
+        _ptr(y, "y", x.dtype), _ptr(final_state, "final_state", f32), b, L, H, P, N, G, Q, io,
+        _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_chunk_scan_fwd_noalloc")
 
 
 def ssd_verify_step(state_in, x, dt, A, B, C, D, accept_len, y, state_out, states_all=None,

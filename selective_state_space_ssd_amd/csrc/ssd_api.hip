@@ -3,10 +3,49 @@
 // before anything is enqueued; a failed check enqueues nothing.
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "ssd_kernels.h"
 #include "ssd_mi355x.h"
 
 namespace {
+
+// Workspace of ssd_chunk_scan_fwd_noalloc: a file-scope device array, one copy per GPU,
+// placed in device memory when the code object is loaded (nothing is allocated at run
+// time).  Host code uses the device address hipGetSymbolAddress returns for the
+// current device, never the array's name.
+constexpr size_t kNoallocBytes = SSD_NOALLOC_WORKSPACE_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoallocBytes];
+constexpr int kNoallocDevices = 64;
+std::mutex g_noalloc_mu;
+std::atomic<void *> g_noalloc_ptr[kNoallocDevices];
+
+// The current device's copy of `scratch`.  The first call on a device looks up its
+// address and prepares it (fill kernel on `stream`: zeroes, marker word); a stream
+// being captured cannot take that first preparation.
+ssd_status_t noalloc_workspace(hipStream_t stream, void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return SSD_ERR_HIP;
+    if (dev < 0 || dev >= kNoallocDevices) return SSD_ERR_UNSUPPORTED;
+    void *p = g_noalloc_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_noalloc_mu);
+        p = g_noalloc_ptr[dev].load(std::memory_order_acquire);
+        if (!p) {
+            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+            if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return SSD_ERR_HIP;
+            if (cs != hipStreamCaptureStatusNone) return SSD_ERR_UNSUPPORTED;
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+                return SSD_ERR_HIP;
+            if (ssd::launch_workspace_init(p, kNoallocBytes, stream) != hipSuccess)
+                return SSD_ERR_HIP;
+            g_noalloc_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return SSD_OK;
+}
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -72,68 +111,136 @@ ssd_status_t ssd_chunk_scan_workspace_error(void *workspace, size_t workspace_by
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 
-ssd_status_t ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, const void *B,
-                                const void *C, const float *D, const float *init_state, void *y,
-                                float *final_state, int b, int L, int H, int P, int N, int G,
-                                int Q, ssd_dtype_t io, void *workspace, size_t workspace_bytes,
-                                void *hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of a chunk-scan call, everything but the workspace; on SSD_OK the
+// plan of the path the call takes and the workspace it needs (0 for an empty problem).
+struct ScanPlan {
+    ssd::FusedPlan fplan;
+    ssd::ChunkScanPlan plan;
+    size_t ws_need = 0;
+    bool empty = false;
+};
+
+ssd_status_t check_scan(const void *x, const float *dt, const float *A, const void *B,
+                        const void *C, const float *D, const float *init_state, const void *y,
+                        const float *final_state, int b, int L, int H, int P, int N, int G,
+                        int Q, ssd_dtype_t io, ScanPlan *sp) {
     if (io != SSD_DTYPE_F32 && io != SSD_DTYPE_BF16) return SSD_ERR_UNSUPPORTED;
     if (b < 0 || L < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || Q <= 0) return SSD_ERR_BAD_DIM;
     if (H % G != 0) return SSD_ERR_GROUPS;
-    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     const size_t state_bytes = size_t(b) * H * P * N * sizeof(float);
-
     if (b == 0 || L == 0) {   // empty sequence: final state is the initial state
+        sp->empty = true;
         if (final_state && b > 0) {
             if (!aligned(final_state, 16) || (init_state && !aligned(init_state, 16)))
                 return SSD_ERR_ALIGN;
             if (init_state && Range(init_state, state_bytes).overlaps(Range(final_state, state_bytes)) &&
                 !Range(init_state, state_bytes).same(Range(final_state, state_bytes)))
                 return SSD_ERR_ALIAS;
-            if (ssd::launch_copy_state(init_state, final_state, state_bytes / 4, stream) != hipSuccess)
-                return SSD_ERR_HIP;
         }
         return SSD_OK;
     }
     if (!x || !dt || !A || !B || !C || !D || !y) return SSD_ERR_NULL_ARG;
-
     const bool bf16 = io == SSD_DTYPE_BF16;
-    const ssd::FusedPlan fplan = ssd::plan_fused(b, L, H, P, N, G, Q, bf16);
-    const ssd::ChunkScanPlan plan = ssd::plan_chunk_scan(b, L, H, P, N, G, Q, bf16);
-    if (!fplan.supported && !plan.supported) return SSD_ERR_UNSUPPORTED;
-    const size_t ws_need = fplan.supported ? fplan.total : plan.total;
-
+    sp->fplan = ssd::plan_fused(b, L, H, P, N, G, Q, bf16);
+    sp->plan = ssd::plan_chunk_scan(b, L, H, P, N, G, Q, bf16);
+    if (!sp->fplan.supported && !sp->plan.supported) return SSD_ERR_UNSUPPORTED;
+    sp->ws_need = sp->fplan.supported ? sp->fplan.total : sp->plan.total;
     if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) ||
-        !aligned(init_state, 16) || !aligned(final_state, 16) || !aligned(workspace, 16) ||
-        !aligned(dt, 4) || !aligned(A, 4) || !aligned(D, 4))
+        !aligned(init_state, 16) || !aligned(final_state, 16) || !aligned(dt, 4) ||
+        !aligned(A, 4) || !aligned(D, 4))
         return SSD_ERR_ALIGN;
-    if (!workspace || workspace_bytes < ws_need) return SSD_ERR_WORKSPACE;
-
     const size_t esz = bf16 ? 2 : 4;
     const Range rx(x, size_t(b) * L * H * P * esz), ry(y, size_t(b) * L * H * P * esz);
     const Range rB(B, size_t(b) * L * G * N * esz), rC(C, size_t(b) * L * G * N * esz);
     const Range rdt(dt, size_t(b) * L * H * 4), rA(A, size_t(H) * 4), rD(D, size_t(H) * 4);
     const Range rinit(init_state, state_bytes), rfin(final_state, state_bytes);
-    const Range rws(workspace, ws_need);
     const Range inputs[] = {rx, rB, rC, rdt, rA, rD, rinit};
     for (const Range &in : inputs) {
-        if (ry.overlaps(in) || rws.overlaps(in)) return SSD_ERR_ALIAS;
+        if (ry.overlaps(in)) return SSD_ERR_ALIAS;
         // final_state may replace init_state in place, but may not clobber other inputs
         if (&in != &inputs[6] && rfin.overlaps(in)) return SSD_ERR_ALIAS;
     }
     if (rfin.overlaps(rinit) && !rfin.same(rinit)) return SSD_ERR_ALIAS;
-    if (ry.overlaps(rfin) || ry.overlaps(rws) || rws.overlaps(rfin)) return SSD_ERR_ALIAS;
+    if (ry.overlaps(rfin)) return SSD_ERR_ALIAS;
+    return SSD_OK;
+}
 
+// Enqueue a checked call on `workspace` (checked by the caller too).
+ssd_status_t run_scan(const void *x, const float *dt, const float *A, const void *B,
+                      const void *C, const float *D, const float *init_state, void *y,
+                      float *final_state, int b, int L, int H, int P, int N, int G, int Q,
+                      ssd_dtype_t io, const ScanPlan &sp, void *workspace, hipStream_t stream) {
+    if (sp.empty) {
+        if (final_state && b > 0 &&
+            ssd::launch_copy_state(init_state, final_state, size_t(b) * H * P * N, stream) !=
+                hipSuccess)
+            return SSD_ERR_HIP;
+        return SSD_OK;
+    }
     ssd::ChunkScanArgs a;
     a.x = x; a.dt = dt; a.A = A; a.B = B; a.C = C; a.D = D;
     a.init_state = init_state; a.y = y; a.final_state = final_state;
     a.b = b; a.L = L; a.H = H; a.P = P; a.N = N; a.G = G; a.Q = Q;
-    a.bf16 = bf16;
+    a.bf16 = io == SSD_DTYPE_BF16;
     a.workspace = workspace;
-    const hipError_t e = fplan.supported ? ssd::launch_fused(a, fplan, stream)
-                                         : ssd::launch_chunk_scan(a, plan, stream);
-    if (e != hipSuccess) return SSD_ERR_HIP;
-    return SSD_OK;
+    const hipError_t e = sp.fplan.supported ? ssd::launch_fused(a, sp.fplan, stream)
+                                            : ssd::launch_chunk_scan(a, sp.plan, stream);
+    return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssd_status_t ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, const void *B,
+                                const void *C, const float *D, const float *init_state, void *y,
+                                float *final_state, int b, int L, int H, int P, int N, int G,
+                                int Q, ssd_dtype_t io, void *workspace, size_t workspace_bytes,
+                                void *hip_stream) {
+    ScanPlan sp;
+    ssd_status_t st = check_scan(x, dt, A, B, C, D, init_state, y, final_state, b, L, H, P, N,
+                                 G, Q, io, &sp);
+    if (st != SSD_OK) return st;
+    if (!sp.empty) {
+        if (!aligned(workspace, 16)) return SSD_ERR_ALIGN;
+        if (!workspace || workspace_bytes < sp.ws_need) return SSD_ERR_WORKSPACE;
+        const size_t esz = io == SSD_DTYPE_BF16 ? 2 : 4;
+        const size_t state_bytes = size_t(b) * H * P * N * sizeof(float);
+        const Range rws(workspace, sp.ws_need);
+        const Range others[] = {
+            Range(x, size_t(b) * L * H * P * esz), Range(y, size_t(b) * L * H * P * esz),
+            Range(B, size_t(b) * L * G * N * esz), Range(C, size_t(b) * L * G * N * esz),
+            Range(dt, size_t(b) * L * H * 4), Range(A, size_t(H) * 4), Range(D, size_t(H) * 4),
+            Range(init_state, state_bytes), Range(final_state, state_bytes)};
+        for (const Range &o : others)
+            if (rws.overlaps(o)) return SSD_ERR_ALIAS;
+    }
+    return run_scan(x, dt, A, B, C, D, init_state, y, final_state, b, L, H, P, N, G, Q, io, sp,
+                    workspace, static_cast<hipStream_t>(hip_stream));
+}
+
+ssd_status_t ssd_chunk_scan_fwd_noalloc(const void *x, const float *dt, const float *A,
+                                        const void *B, const void *C, const float *D,
+                                        const float *init_state, void *y, float *final_state,
+                                        int b, int L, int H, int P, int N, int G, int Q,
+                                        ssd_dtype_t io, void *hip_stream) {
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    ScanPlan sp;
+    ssd_status_t st = check_scan(x, dt, A, B, C, D, init_state, y, final_state, b, L, H, P, N,
+                                 G, Q, io, &sp);
+    if (st != SSD_OK) return st;
+    void *ws = nullptr;
+    if (!sp.empty) {
+        if (sp.ws_need > kNoallocBytes) return SSD_ERR_WORKSPACE;
+        st = noalloc_workspace(stream, &ws);
+        if (st != SSD_OK) return st;
+    }
+    return run_scan(x, dt, A, B, C, D, init_state, y, final_state, b, L, H, P, N, G, Q, io, sp,
+                    ws, stream);
 }
 
 ssd_status_t ssd_verify_step(const float *state_in, const void *x, const float *dt,

@@ -139,6 +139,31 @@ def test_scan_q256_n256_p64_is_unsupported(lib):
     assert scan_call(lib, dims=dict(dims, Q=128), io=1, ws_bytes=1) == WS
 
 
+def noalloc_call(lib, dims=None, io=1, over=None):
+    ptrs = dict(x=addr(1), dt=addr(2), A=addr(3), B=addr(4), C=addr(5), D=addr(6),
+                init=None, y=addr(7), final=addr(8))
+    ptrs.update(over or {})
+    d = dict(b=1, L=256, H=4, P=16, N=16, G=1, Q=64)
+    d.update(dims or {})
+    return lib.ssd_chunk_scan_fwd_noalloc(ptrs["x"], ptrs["dt"], ptrs["A"], ptrs["B"],
+                                          ptrs["C"], ptrs["D"], ptrs["init"], ptrs["y"],
+                                          ptrs["final"], d["b"], d["L"], d["H"], d["P"],
+                                          d["N"], d["G"], d["Q"], io, None)
+
+
+def test_noalloc_host_checks(lib):
+    # every case fails (or finishes) on the host before the buffer is looked up
+    assert bd.NOALLOC_WORKSPACE_BYTES == 64 << 20
+    big = dict(b=4, L=2048, H=80, P=64, N=128, G=1, Q=64)      # fp32: three-kernel path
+    need = bd.ssd_chunk_scan_workspace_bytes(*big.values(), bd.SSD_DTYPE_F32)
+    assert need > bd.NOALLOC_WORKSPACE_BYTES
+    assert noalloc_call(lib, dims=big, io=0) == WS
+    assert noalloc_call(lib, dims=dict(H=0)) == DIM
+    assert noalloc_call(lib, dims=dict(G=3)) == GROUPS
+    assert noalloc_call(lib, io=7) == UNSUP
+    assert noalloc_call(lib, dims=dict(b=0), over=dict(x=None, y=None)) == OK   # empty
+
+
 def test_scan_workspace_checks(lib):
     need = bd.ssd_chunk_scan_workspace_bytes(1, 256, 4, 16, 16, 1, 64, 1)
     assert scan_call(lib, ws_bytes=need - 1) == WS
