@@ -491,6 +491,18 @@ void k_ssd_fused(
         auto off = [&](int k, int j, int i) {
             return ((pt_base + PT_STEP * k) * 16 + 4 * g4 + i) * N + (nt_base + NT_STEP * j) * 16 + r16;
         };
+        // off(k, j, 0) - off(0, 0, 0), a constant (passed as the scalar offset of a
+        // buffer access)
+        auto tile_offset = [&](int k, int j) { return PT_STEP * k * 16 * N + NT_STEP * j * 16; };
+        // off(0, 0, 0) recomputed from an opaque copy of the thread index
+        auto lane_offset = [&]() {
+            int t = tid;
+            asm volatile("" : "+v"(t));
+            const int l = t & 63, ww = t >> 6;
+            const int ntb = F::kGrid22 ? 2 * (ww % 4) : F::NTN >= kFW ? ww : (ww % F::NTN);
+            const int ptb = F::kGrid22 ? 2 * (ww / 4) : F::NTN >= kFW ? 0 : (ww / F::NTN);
+            return (ptb * 16 + 4 * (l >> 4)) * N + ntb * 16 + (l & 15);
+        };
 #pragma unroll
         for (int k = 0; k < F::PTW; ++k)
 #pragma unroll
@@ -511,12 +523,19 @@ void k_ssd_fused(
                         for (int i = 0; i < 4; ++i) hp[k][j][i] = v[i];
                     }
             } else if (hsrc) {
+                // the initial state (first chunk only): offsets from an opaque copy of the
+                // thread index, so that they are computed here and not kept live (in 64-bit
+                // registers) through the whole head loop for this one-off read
+                const __amdgpu_buffer_rsrc_t src = buffer_rsrc(hsrc, uint32_t(P * N * 4));
+                const int lo = lane_offset();
 #pragma unroll
                 for (int k = 0; k < F::PTW; ++k)
 #pragma unroll
                     for (int j = 0; j < F::NTW; ++j)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) hp[k][j][i] = hsrc[off(k, j, i)];
+                        for (int i = 0; i < 4; ++i)
+                            hp[k][j][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                src, (lo + i * N) * 4, tile_offset(k, j) * 4, 0));
             }
         }
         // ---- step 2: S_c = XwT^T B (x already carries dt and the decay to the chunk end)
@@ -603,13 +622,18 @@ void k_ssd_fused(
                                                                kBufDevice);
                     }
             } else if (final_state) {
-                float *fdst = final_state + bh * size_t(P) * N;
+                // the final state (last chunk only), offsets as for the initial state
+                const __amdgpu_buffer_rsrc_t dst =
+                    buffer_rsrc(final_state + bh * size_t(P) * N, uint32_t(P * N * 4));
+                const int lo = lane_offset();
 #pragma unroll
                 for (int k = 0; k < F::PTW; ++k)
 #pragma unroll
                     for (int j = 0; j < F::NTW; ++j)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) fdst[off(k, j, i)] = hp[k][j][i];
+                        for (int i = 0; i < 4; ++i)
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hp[k][j][i]), dst,
+                                                                  (lo + i * N) * 4, tile_offset(k, j) * 4, 0);
             }
         }
         if (!last) wait_vm();   // this wave's state stores are complete and visible
