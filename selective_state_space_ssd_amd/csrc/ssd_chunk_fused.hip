@@ -220,8 +220,9 @@ void k_ssd_fused(
     bf16_bits *Hs = XN + Q * F::XS;                     // [P][HS] entering state, bf16
 
     const int tid = threadIdx.x, lane = tid & 63;
-    // wave index; held in a scalar register except in the Q = 256 kernels, whose
-    // register assignment only stays spill-free with it in a vector register
+    // wave index; held in a scalar register except in the Q = 256 kernels, whose scalar
+    // registers are short (they spill some into vector-register lanes, never to
+    // scratch; a scalar copy of the wave index adds to those spills)
     const int w = Q == 256 ? tid >> 6 : __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, g4 = lane >> 4;
 
