@@ -63,13 +63,15 @@ __device__ __forceinline__ int tile_off(int tile, int l) { return tile * 256 + 4
 // supplies as an MFMA operand at k step kk (32 values): rows 32 kk + 8 g4 .. + 7 of
 // column r16, taken from tiles t_base + (2 kk + g4 / 2) * t_stride as two 8-byte
 // pieces of lanes r16 + 32 (g4 & 1) and r16 + 32 (g4 & 1) + 16.
-__device__ __forceinline__ uint4 tile_operand(const bf16_bits *base, int t_base, int t_stride,
+__device__ __forceinline__ uint4 tile_operand(__amdgpu_buffer_rsrc_t st, int t_base, int t_stride,
                                               int kk, int r16, int g4) {
     const int tile = t_base + (2 * kk + (g4 >> 1)) * t_stride;
     const int l = r16 + 32 * (g4 & 1);
-    const uint2 lo = *reinterpret_cast<const uint2 *>(base + tile_off(tile, l));
-    const uint2 hi = *reinterpret_cast<const uint2 *>(base + tile_off(tile, l + 16));
-    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    const u32x2 lo = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_raw_buffer_load_b64(st, tile_off(tile, l) * 2, 0, 0));
+    const u32x2 hi = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_raw_buffer_load_b64(st, tile_off(tile, l + 16) * 2, 0, 0));
+    return make_uint4(lo[0], lo[1], hi[0], hi[1]);
 }
 
 // Inputs of one chunk step held by a loader thread: the token pair (2 tpu, 2 tpu + 1)
@@ -237,6 +239,13 @@ __device__ __forceinline__ void chain_walk(
     for (int step = 0; step < nc; ++step) {
         const int c = chunk_of(step);
         const int buf = step & 1;
+        // the lane's row and lane group, re-derived each step from an opaque copy of the
+        // lane index: otherwise the per-tile LDS addresses are hoisted out of the loop and
+        // spill, and each scratch reload waits (one in-order counter) for this step's
+        // state stores to complete
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int r16 = ln & 15, g4 = ln >> 4;
         // store the state (entering chunk c forward, leaving chunk c in reverse)
         const size_t so = (bh * nc + c) * size_t(PN);
 #pragma unroll
@@ -255,6 +264,9 @@ __device__ __forceinline__ void chain_walk(
                         make_uint2(pack_bf16x2(accN[j][pt][0], accN[j][pt][1]),
                                    pack_bf16x2(accN[j][pt][2], accN[j][pt][3]));
         }
+        // the stores above are issued before the update starts: otherwise the packed
+        // values stay live next to the update's operands and spill
+        __builtin_amdgcn_sched_barrier(0);
         // state <- al * state + (this chunk's contribution)
         const bf16_bits *vt = VT[buf];
 #pragma unroll
@@ -290,6 +302,11 @@ __device__ __forceinline__ void chain_walk(
     }
     if constexpr (DIR == 1) {
         if (d_init) {
+            // addresses computed here, from an opaque copy of the lane index, rather
+            // than kept (and spilled) through the walk
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const int r16 = ln & 15, g4 = ln >> 4;
 #pragma unroll
             for (int j = 0; j < NTW; ++j)
 #pragma unroll
@@ -400,15 +417,22 @@ __global__ __launch_bounds__(kChunkThreads) void k_bwd_chunk_bf(
     // one head's x (threads 0-255) or dy (threads 256-511): token pair tpu, p group pgu
     const bool is_dy = tid >= kThreads;
     const int tpu = (tid & 255) >> 3, pgu = tid & 7;
-    const bf16_bits *src_xy = is_dy ? dy : x;
+    // x, dy, dt, dx and ddt through buffer views of the chunk's qlen rows (32-bit
+    // offsets; rows past them read 0 and their stores are dropped)
+    const size_t tok0 = size_t(bi) * L + t0;
+    const __amdgpu_buffer_rsrc_t xyres =
+        buffer_rsrc((is_dy ? dy : x) + tok0 * H * HP, uint32_t(qlen) * uint32_t(H * HP) * 2u);
+    const __amdgpu_buffer_rsrc_t dtres = buffer_rsrc(dt + tok0 * H, uint32_t(qlen) * uint32_t(H) * 4u);
+    const __amdgpu_buffer_rsrc_t dxres = buffer_rsrc(dx + tok0 * H * HP, uint32_t(qlen) * uint32_t(H * HP) * 2u);
+    const __amdgpu_buffer_rsrc_t ddtres = buffer_rsrc(ddt + tok0 * H, uint32_t(qlen) * uint32_t(H) * 4u);
     uint4 ra, rb;
     float dnext;
     auto load_head = [&](int h) {
-        const int ta = 2 * tpu, tb = ta + 1;
-        const size_t o = ((size_t(bi) * L + t0 + ta) * H + h) * HP + 8 * pgu;
-        ra = ta < qlen ? *reinterpret_cast<const uint4 *>(src_xy + o) : zero4();
-        rb = tb < qlen ? *reinterpret_cast<const uint4 *>(src_xy + o + size_t(H) * HP) : zero4();
-        dnext = lane < qlen ? dt[(size_t(bi) * L + t0 + lane) * H + h] : 0.f;
+        const int ta = 2 * tpu;
+        const int o = ((ta * H + h) * HP + 8 * pgu) * 2;
+        ra = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xyres, o, 0, 0));
+        rb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xyres, o + H * HP * 2, 0, 0));
+        dnext = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(dtres, (lane * H + h) * 4, 0, 0));
     };
     load_head(h0);
 
@@ -456,19 +480,32 @@ __global__ __launch_bounds__(kChunkThreads) void k_bwd_chunk_bf(
         accC[k] = {0.f, 0.f, 0.f, 0.f};
     }
 
+    // a head's states as MFMA A operands (rows owned by this wave)
+    // (Gh: rows p of block q, k = n; Gh^T and Hin^T: rows n of tile ntw, k = p).  Gh,
+    // used first, is loaded one head ahead (issued once head hh's last use of those
+    // registers is done); Gh^T and Hin^T at the top of their head
+    uint4 ghp[KN], ght[2], hnt[2];
+    auto state_view = [&](const bf16_bits *base, int hs) {
+        const size_t so = ((size_t(bi) * H + h0 + hs) * nc + c) * size_t(PN);
+        return buffer_rsrc(base + so, uint32_t(PN) * 2u);
+    };
+    auto load_gh = [&](int hs) {
+        const __amdgpu_buffer_rsrc_t gn = state_view(ghN, hs);
+#pragma unroll
+        for (int kq = 0; kq < KN; ++kq) ghp[kq] = tile_operand(gn, q * NT, 1, kq, r16, g4);
+    };
+    load_gh(0);
+
     for (int hh = 0; hh < HB; ++hh) {
         const int h = h0 + hh;
         const size_t bhc = (size_t(bi) * H + h) * nc + c;
-        const size_t so = bhc * size_t(PN);
-        // this head's states as MFMA A operands (rows owned by this wave)
-        // (Gh: rows p of block q, k = n; Gh^T and Hin^T: rows n of tile ntw, k = p)
-        uint4 ghp[KN], ght[2], hnt[2];
+        {
+            const __amdgpu_buffer_rsrc_t gt = state_view(ghT, hh), ht = state_view(hinT, hh);
 #pragma unroll
-        for (int kq = 0; kq < KN; ++kq) ghp[kq] = tile_operand(ghN + so, q * NT, 1, kq, r16, g4);
-#pragma unroll
-        for (int kp = 0; kp < 2; ++kp) {
-            ght[kp] = tile_operand(ghT + so, ntw * 4, 1, kp, r16, g4);
-            hnt[kp] = tile_operand(hinT + so, ntw * 4, 1, kp, r16, g4);
+            for (int kp = 0; kp < 2; ++kp) {
+                ght[kp] = tile_operand(gt, ntw * 4, 1, kp, r16, g4);
+                hnt[kp] = tile_operand(ht, ntw * 4, 1, kp, r16, g4);
+            }
         }
         const float dreg = dnext;
         const float Ah = A[h];
@@ -573,13 +610,14 @@ __global__ __launch_bounds__(kChunkThreads) void k_bwd_chunk_bf(
                     o[i] = acc[i] + ws * U[i] + Dh * dyv[i];
                     vp += xv[i] * U[i];
                 }
-                if (s < qlen)
-                    *reinterpret_cast<uint2 *>(dx + ((size_t(bi) * L + t0 + s) * H + h) * HP + p0) =
-                        make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+                const u32x2 ov = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                __builtin_amdgcn_raw_buffer_store_b64(ov, dxres, ((s * H + h) * HP + p0) * 2, 0, 0);
                 vp = group4_sum(vp);
                 if (g4 == 0) vsp[q * QB + s] = vp;
             }
         }
+        // Gh of the next head: its registers are free from here on
+        if (hh + 1 < HB) load_gh(hh + 1);
 
         // ---- dC^T[n][t] += BT dS^T + e^{cum_t} V^T,  V^T[n][t] = Hin^T[n] . dy_t
         {
@@ -681,8 +719,8 @@ __global__ __launch_bounds__(kChunkThreads) void k_bwd_chunk_bf(
             if (t == qlen - 1) dc += dend;
             const float inc = wave_inclusive_scan(dc);
             const float da = __shfl(inc, 63, 64) - inc + dc;     // sum over tau >= t
-            if (valid)
-                ddt[(size_t(bi) * L + t0 + t) * H + h] = glw + exp2f(aend - cs) * v + Ah * da;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(glw + exp2f(aend - cs) * v + Ah * da),
+                                                  ddtres, (t * H + h) * 4, 0, 0);
             const float dA = wave_sum(valid ? dreg * da : 0.f);
             if (lane == 0) {
                 dAp[bhc] = dA;
