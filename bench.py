@@ -38,7 +38,10 @@ Printed: one JSON line with the contract fields plus
                 the one-channel-per-head selective scan (diagonal A, the recurrence
                 SSD replaces) on the same layer shape (4 x 2048 tokens, 5120
                 channels) at N=16 and N=128, and how many times faster the SSD
-                chunked scan (N=128) is than each
+                chunked scan (N=128) is than each, with the comparison kernel's own
+                roofline (state updates/s against the vector-ALU ceiling) and the
+                speed-up the SSD scan would keep over a comparison kernel at that
+                ceiling
   decode_K1     the verify step with one token (a decode step), GB/s
   verify_ring   one round of the multi-round verify on a ring of 8 states (K=4, every
                 draft accepted, fused softplus step), GB/s
@@ -67,6 +70,14 @@ METRIC = "SSD fwd tokens/s per layer at L=2k/16k; % MFMA/HBM roofline; verify-st
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20
+# Vector-ALU ceiling of the comparison scan, in state updates per second.  One update
+# of one state for one token needs one exponential (dt a, the decay factor) and four
+# plain vector operations (the product dt a, the product dt x B, the fused decay-and-add,
+# the fused C h accumulation).  On MI355X (256 CUs of 4 SIMDs at 2.4 GHz; 157.3 TFLOP/s
+# fp32 = 32 fused multiply-adds per SIMD per clock) a wave of 64 lanes issues a plain
+# fp32 operation in 2 clocks and a transcendental (quarter rate) in 8, so an update
+# costs at least (4 * 2 + 8) / 64 SIMD clocks: 4 updates per SIMD per clock.
+SEL_ALU_PEAK_UPDATES = 256 * 4 * 2.4e9 * 4.0
 
 
 KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_ssd_amd", "csrc", f)
@@ -740,9 +751,17 @@ def main():
             rs = time_selective(f"mamba1_L2k_N{n}", max(3, args.steps // 10), 1, bd, inputs, torch)
             ds = rs["dims"]
             tps = ds["b"] * ds["L"] / (rs["call_ms_mean"] * 1e-3)
+            ups = ds["b"] * ds["L"] * ds["Dch"] * ds["N"] / (rs["call_ms_mean"] * 1e-3)
             cmp[f"N{n}"] = {"workload": f"mamba1_L2k_N{n}", "tokens_per_s": tps,
                             "call_ms_mean": rs["call_ms_mean"],
-                            "ssd_N128_speedup": ssd_tps / tps}
+                            "ssd_N128_speedup": ssd_tps / tps,
+                            "roofline": {"bound": "alu", "achieved": ups / 1e12,
+                                         "peak": SEL_ALU_PEAK_UPDATES / 1e12,
+                                         "unit": "T state updates/s",
+                                         "frac": ups / SEL_ALU_PEAK_UPDATES, "traffic": None},
+                            "ssd_N128_speedup_vs_alu_floor":
+                                ssd_tps / (ds["b"] * ds["L"] * SEL_ALU_PEAK_UPDATES /
+                                           (ds["b"] * ds["L"] * ds["Dch"] * ds["N"]))}
         out["selective_scan_comparison"] = cmp
         _progress("comparison scan timed")
         sp = time_seqpar(max(10, args.steps), 3, bd, inputs, torch)

@@ -262,7 +262,7 @@ ssd_status_t ssd_verify_step(const float *state_in, const void *x, const float *
  *   final_state [b, Dch, N]  fp32   NULL, or the state after the last token (written;
  *                                   with L = 0 it is init_state, or zeros)
  * Supported: N in {16, 32, 64, 128, 256}; the channels of one group (Dch / G) must be
- * a multiple of 1024 / N (one workgroup's channels).  Outputs must not overlap
+ * a multiple of 32 (one workgroup's channels).  Outputs must not overlap
  * inputs or each other.  Errors as for the other entry points; nothing is enqueued
  * when a check fails.
  */

@@ -12,14 +12,17 @@
 // Series»).  Discretisation, scan and the product with C run in one kernel and the
 // per-token states never leave registers («Hardware-aware Algorithm»).
 //
-// Layout of the work: every lane holds SL consecutive states of one channel (2 for
-// N <= 32, else 4), so NL = N/SL lanes share a channel and a 256-thread block
-// covers DC = 256 SL/N channels of one batch.  The block walks the sequence in
-// tiles of T tokens: x, dt, B and C of a tile are staged in LDS (loaded into
-// registers while the previous tile is computed), the T steps run from LDS (each
-// step: SL exponentials, the state update, the partial C . h, a sum over the NL
-// lanes), and the tile's y is written back from LDS with coalesced stores.  Time
-// runs sequentially inside a lane; the parallelism is over (batch, channel, state).
+// Layout of the work: 8 lanes share a channel, each holding SL = N / 8 consecutive
+// states, so a 256-thread block covers DC = 32 channels of one batch row.  The block
+// walks the sequence in tiles of T tokens: x, dt, B and C of a tile are staged in LDS
+// once for all DC channels, in fp32 (loaded into registers while the previous tile is
+// computed, converted once at staging), the T steps run from LDS (each step: SL exponentials, the state
+// update, the partial C . h, a sum over the NL lanes), and the tile's y is written back
+// from LDS with coalesced stores.  Time runs sequentially inside a lane; the SL states
+// of a lane are independent chains, and the parallelism is over (batch, channel,
+// state).
+#include <type_traits>
+
 #include "ssd_device.h"
 #include "ssd_kernels.h"
 
@@ -29,31 +32,49 @@ namespace {
 
 constexpr int kSelThreads = 256;
 
-template <int N>
+template <typename IO, int N>
 struct SelShape {
-    static constexpr int SL = N <= 32 ? 2 : 4;        // states per lane
-    static constexpr int NL = N / SL;                 // lanes per channel
+    static constexpr int NL = 8;                      // lanes per channel
+    static constexpr int SL = N / NL;                 // states per lane
     static constexpr int CW = 64 / NL;                // channels per wave
     static constexpr int DC = 4 * CW;                 // channels per block
-    static constexpr int T = N >= 256 ? 32 : 64;      // tokens per tile
+    static constexpr int T = N <= 64 ? 64 : 32;       // tokens per tile (a multiple of 8)
     static_assert(N % 16 == 0 && N >= 16 && N <= 256, "N must be 16, 32, 64, 128 or 256");
+    static constexpr int VW = 16 / int(sizeof(IO));   // elements per 16-byte piece
     static constexpr size_t kLds = size_t(T) * DC * 4 * 3 + size_t(T) * N * 4 * 2;
 };
 
-// Sum over groups of NL consecutive lanes (NL a power of two, 4 .. 64); every lane
-// of a group ends with the group's sum.
+// Sum over groups of NL consecutive lanes (NL 4 or 8); every lane of a group ends
+// with the group's sum.
 template <int NL>
 __device__ __forceinline__ float group_sum(float v) {
-    constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
+    constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kRowHalfMirror = 0x141;
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kQuadSwap1, 0xF, 0xF, false));
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kQuadSwap2, 0xF, 0xF, false));
     if constexpr (NL >= 8)
         v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kRowHalfMirror, 0xF, 0xF, false));
-    if constexpr (NL >= 16)
-        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kRowMirror, 0xF, 0xF, false));
-    if constexpr (NL >= 32) v += __shfl_xor(v, 16, 64);
-    if constexpr (NL >= 64) v += __shfl_xor(v, 32, 64);
+    static_assert(NL == 4 || NL == 8, "groups of 4 or 8 lanes");
     return v;
+}
+
+// SL consecutive fp32 values of one staged row (16-byte LDS reads where SL allows)
+template <int SL>
+__device__ __forceinline__ void lds_row(const float *src, float (&out)[SL]) {
+    if constexpr (SL % 4 == 0) {
+#pragma unroll
+        for (int j = 0; j < SL; j += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(src + j);
+            out[j] = v.x;
+            out[j + 1] = v.y;
+            out[j + 2] = v.z;
+            out[j + 3] = v.w;
+        }
+    } else {
+        static_assert(SL == 2, "2 or a multiple of 4 states per lane");
+        const float2 v = *reinterpret_cast<const float2 *>(src);
+        out[0] = v.x;
+        out[1] = v.y;
+    }
 }
 
 template <typename IO, int N>
@@ -62,16 +83,16 @@ __global__ __launch_bounds__(kSelThreads) void k_selective_scan(
     const IO *__restrict__ B, const IO *__restrict__ C, const float *__restrict__ D,
     const float *__restrict__ init_state, IO *__restrict__ y, float *__restrict__ final_state,
     int L, int Dch, int G) {
-    using S = SelShape<N>;
-    constexpr int T = S::T, DC = S::DC, NL = S::NL;
+    using S = SelShape<IO, N>;
+    constexpr int T = S::T, DC = S::DC, NL = S::NL, SL = S::SL, VW = S::VW;
+    static_assert(NL == 8, "group_sum and the channel layout assume 8 lanes per channel");
     extern __shared__ __align__(16) float sm[];
-    float *xs = sm;                  // [T][DC] x
-    float *ds = xs + T * DC;         // [T][DC] dt
-    float *ys = ds + T * DC;         // [T][DC] y
-    float *bs = ys + T * DC;         // [T][N] B
-    float *cs = bs + T * N;          // [T][N] C
+    float *xs = sm;                                  // [T][DC] x
+    float *ds = xs + T * DC;                         // [T][DC] dt
+    float *ys = ds + T * DC;                         // [T][DC] y
+    float *bs = ys + T * DC;                         // [T][N] B
+    float *cs = bs + T * N;                          // [T][N] C
 
-    constexpr int SL = S::SL;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int bi = blockIdx.y, d0 = blockIdx.x * DC;
     const int g = d0 / (Dch / G);    // the block's channels share one group
@@ -89,42 +110,48 @@ __global__ __launch_bounds__(kSelThreads) void k_selective_scan(
     const float Dd = D[d];
     const bool writer = (lane % NL) == 0;
 
-    // tile loads, held in registers until the LDS is free: x and dt one element per
-    // slot (row t of the tile holds channels d0 .. d0+DC-1, contiguous in memory), B
-    // and C 16 bytes per slot (rows of N contiguous elements)
-    constexpr int NX = (T * DC + kSelThreads - 1) / kSelThreads;
-    constexpr int VW = 16 / int(sizeof(IO));
+    // tile loads through buffer views of the tile's rows (rows past the sequence read
+    // 0), held in registers until the LDS is free: x and dt one element per slot (row
+    // t holds channels d0 .. d0+DC-1, contiguous in memory), B and C 16 bytes per slot
+    constexpr int NX = T * DC / kSelThreads;
     constexpr int NV = (T * N / VW + kSelThreads - 1) / kSelThreads;
+    static_assert(T * DC % kSelThreads == 0, "whole x / dt slots per thread");
     IO xr[NX];
     float dr[NX];
     uint4 br[NV], cr[NV];
     auto load_tile = [&](int t0) {
         const int tl = min(T, L - t0);
+        const size_t row0 = size_t(bi) * L + t0;
+        const __amdgpu_buffer_rsrc_t xv = buffer_rsrc(x + row0 * Dch + d0, uint32_t(tl) * uint32_t(Dch) * sizeof(IO));
+        const __amdgpu_buffer_rsrc_t dv = buffer_rsrc(dt + row0 * Dch + d0, uint32_t(tl) * uint32_t(Dch) * 4u);
+        const __amdgpu_buffer_rsrc_t bv = buffer_rsrc(B + row0 * G * N + size_t(g) * N,
+                                                      uint32_t(tl) * uint32_t(G * N) * sizeof(IO));
+        const __amdgpu_buffer_rsrc_t cv = buffer_rsrc(C + row0 * G * N + size_t(g) * N,
+                                                      uint32_t(tl) * uint32_t(G * N) * sizeof(IO));
 #pragma unroll
         for (int k = 0; k < NX; ++k) {
             const int i = tid + k * kSelThreads, t = i / DC, c = i % DC;
-            const bool ok = i < T * DC && t < tl;
-            const size_t src = (size_t(bi) * L + t0 + (ok ? t : 0)) * Dch + d0 + c;
-            xr[k] = ok ? x[src] : IO(0);
-            dr[k] = ok ? dt[src] : 0.f;
+            const int off = t * Dch + c;
+            if constexpr (std::is_same_v<IO, float>)
+                xr[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xv, off * 4, 0, 0));
+            else
+                xr[k] = IO(__builtin_amdgcn_raw_buffer_load_b16(xv, off * 2, 0, 0));
+            dr[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(dv, off * 4, 0, 0));
         }
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
-            const int i = (tid + k * kSelThreads) * VW, t = i / N, n = i % N;
-            const bool ok = i < T * N && t < tl;
-            const size_t src = ((size_t(bi) * L + t0 + (ok ? t : 0)) * G + g) * N + n;
-            br[k] = ok ? *reinterpret_cast<const uint4 *>(B + src) : make_uint4(0, 0, 0, 0);
-            cr[k] = ok ? *reinterpret_cast<const uint4 *>(C + src) : make_uint4(0, 0, 0, 0);
+            const int i = min((tid + k * kSelThreads) * VW, T * N - VW), t = i / N, n = i % N;
+            const int off = (t * G * N + n) * int(sizeof(IO));
+            br[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bv, off, 0, 0));
+            cr[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(cv, off, 0, 0));
         }
     };
     auto store_tile = [&]() {
 #pragma unroll
         for (int k = 0; k < NX; ++k) {
             const int i = tid + k * kSelThreads;
-            if (i < T * DC) {
-                xs[i] = to_f32<IO>(xr[k]);
-                ds[i] = dr[k];
-            }
+            xs[i] = to_f32<IO>(xr[k]);
+            ds[i] = dr[k];
         }
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
@@ -136,11 +163,11 @@ __global__ __launch_bounds__(kSelThreads) void k_selective_scan(
                 } else {
                     const uint32_t *bw = &br[k].x, *cw = &cr[k].x;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        bs[i + 2 * q] = bf16_lo(bw[q]);
-                        bs[i + 2 * q + 1] = bf16_hi(bw[q]);
-                        cs[i + 2 * q] = bf16_lo(cw[q]);
-                        cs[i + 2 * q + 1] = bf16_hi(cw[q]);
+                    for (int q = 0; q < 4; q += 2) {
+                        *reinterpret_cast<float4 *>(bs + i + 2 * q) =
+                            make_float4(bf16_lo(bw[q]), bf16_hi(bw[q]), bf16_lo(bw[q + 1]), bf16_hi(bw[q + 1]));
+                        *reinterpret_cast<float4 *>(cs + i + 2 * q) =
+                            make_float4(bf16_lo(cw[q]), bf16_hi(cw[q]), bf16_lo(cw[q + 1]), bf16_hi(cw[q + 1]));
                     }
                 }
             }
@@ -153,51 +180,40 @@ __global__ __launch_bounds__(kSelThreads) void k_selective_scan(
         store_tile();
         __syncthreads();
         if (t0 + T < L) load_tile(t0 + T);   // in flight during this tile's steps
-        // ---- the tile's steps, in groups of U: the inputs of a group are read from
-        // LDS together (the y stores to LDS would otherwise order every step's reads
-        // after the previous step's store), then the steps run, then the y values go
-        // out together
-        constexpr int U = SL == 2 ? 8 : 4;
-        int t = 0;
-        for (; t + U <= tl; t += U) {
-            float xv[U], dv[U], bv[U][SL], cv[U][SL], yv[U];
+        // ---- the tile's steps (rows past the sequence hold x = dt = 0 and are not
+        // written back), in groups of U: the y values of a group go to LDS together
+        // after its steps, so that no step's LDS reads are ordered behind the previous
+        // step's y store
+        constexpr int U = SL <= 4 ? 8 : 32 / SL;   // the group's inputs fit the registers
+        for (int t = 0; t < tl; t += U) {
+            float yv[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                xv[u] = xs[(t + u) * DC + dl];
-                dv[u] = ds[(t + u) * DC + dl];
+                const int tu = t + u;   // tu < T: the tile's rows past tl read zeros
+                const float xv = xs[tu * DC + dl], dv = ds[tu * DC + dl];
+                float bv[SL], cv[SL];
+                lds_row<SL>(bs + tu * N + n0, bv);
+                lds_row<SL>(cs + tu * N + n0, cv);
+                const float uu = dv * xv;
+                // the partial C . h in up to four independent sums (shorter chains)
+                constexpr int NP = SL < 4 ? SL : 4;
+                float pp[NP];
+#pragma unroll
+                for (int j = 0; j < NP; ++j) pp[j] = 0.f;
 #pragma unroll
                 for (int j = 0; j < SL; ++j) {
-                    bv[u][j] = bs[(t + u) * N + n0 + j];
-                    cv[u][j] = cs[(t + u) * N + n0 + j];
+                    h[j] = __builtin_amdgcn_exp2f(dv * a2[j]) * h[j] + uu * bv[j];
+                    pp[j % NP] += cv[j] * h[j];
                 }
-            }
+                float part = pp[0];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const float uu = dv[u] * xv[u];
-                float part = 0.f;
-#pragma unroll
-                for (int j = 0; j < SL; ++j) {
-                    h[j] = __builtin_amdgcn_exp2f(dv[u] * a2[j]) * h[j] + uu * bv[u][j];
-                    part += cv[u][j] * h[j];
-                }
-                yv[u] = group_sum<NL>(part) + Dd * xv[u];
+                for (int j = 1; j < NP; ++j) part += pp[j];
+                yv[u] = group_sum<NL>(part) + Dd * xv;
             }
             if (writer) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) ys[(t + u) * DC + dl] = yv[u];
             }
-        }
-        for (; t < tl; ++t) {   // the last partial group
-            const float xv = xs[t * DC + dl], dv = ds[t * DC + dl];
-            const float uu = dv * xv;
-            float part = 0.f;
-#pragma unroll
-            for (int j = 0; j < SL; ++j) {
-                h[j] = __builtin_amdgcn_exp2f(dv * a2[j]) * h[j] + uu * bs[t * N + n0 + j];
-                part += cs[t * N + n0 + j] * h[j];
-            }
-            part = group_sum<NL>(part);
-            if (writer) ys[t * DC + dl] = part + Dd * xv;
         }
         __syncthreads();
         // ---- write the tile's y (the next tile's staging touches only xs, ds, bs, cs)
@@ -214,7 +230,7 @@ __global__ __launch_bounds__(kSelThreads) void k_selective_scan(
 
 template <typename IO, int N>
 hipError_t launch_sel_n(const SelectiveArgs &a, hipStream_t stream) {
-    using S = SelShape<N>;
+    using S = SelShape<IO, N>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_selective_scan<IO, N>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(S::kLds));
     if (e != hipSuccess) return e;
@@ -241,12 +257,12 @@ hipError_t launch_sel_io(const SelectiveArgs &a, hipStream_t stream) {
 }  // namespace
 
 int selective_channels_per_block(int N) {
-    switch (N) {
-        case 16: return SelShape<16>::DC;
-        case 32: return SelShape<32>::DC;
-        case 64: return SelShape<64>::DC;
-        case 128: return SelShape<128>::DC;
-        case 256: return SelShape<256>::DC;
+    switch (N) {   // the same for both I/O types
+        case 16: return SelShape<float, 16>::DC;
+        case 32: return SelShape<float, 32>::DC;
+        case 64: return SelShape<float, 64>::DC;
+        case 128: return SelShape<float, 128>::DC;
+        case 256: return SelShape<float, 256>::DC;
         default: return 0;
     }
 }
