@@ -110,3 +110,41 @@ def scan_errors_all_units(inp, y, fs, threads=None):
     with concurrent.futures.ThreadPoolExecutor(max_workers=threads or oracle_threads()) as ex:
         errs = list(ex.map(one, range(b * H)))
     return max(e[0] for e in errs), max(e[1] for e in errs), len(errs)
+
+
+def backward_row_oracle(args):
+    """Gradient oracle for one batch row of a named workload (every head, in blocks of
+    8 heads), for a process pool: the inputs are regenerated from the workload's seed
+    here rather than sent over.  Returns the row's dx, ddt, d_init, dB, dC and its
+    contributions to dA, dD."""
+    name, grad_seed, row, threads = args
+    from oracle import backward
+    from selective_state_space_ssd_amd import inputs
+
+    torch.set_num_threads(threads)
+    inp = inputs.make_workload(name)
+    dy, d_final = inputs.make_upstream_grads(inp, seed=grad_seed)
+    f = lambda t: None if t is None else t.f64()
+    x, dt, A, B, C, D = (f(getattr(inp, n)) for n in ("x", "dt", "A", "B", "C", "D"))
+    h0, dfin, dyf = f(inp.init_state), f(d_final), dy.f64()
+    H = inp.dims["H"]
+    r = slice(row, row + 1)
+    out = None
+    for h0_ in range(0, H, 8):
+        hs = slice(h0_, h0_ + 8)
+        part = backward.scan_bwd_f64(
+            x[r][:, :, hs], dt[r][:, :, hs], A[hs], B[r], C[r], D[hs],
+            None if h0 is None else h0[r][:, hs], dyf[r][:, :, hs],
+            None if dfin is None else dfin[r][:, hs])
+        if out is None:
+            out = {"dx": np.zeros(x[r].shape), "ddt": np.zeros(dt[r].shape),
+                   "d_init": np.zeros((1, H) + part[6].shape[2:]), "dB": np.zeros_like(part[3]),
+                   "dC": np.zeros_like(part[4]), "dA": np.zeros(H), "dD": np.zeros(H)}
+        out["dx"][:, :, hs] = part[0]
+        out["ddt"][:, :, hs] = part[1]
+        out["dA"][hs] = part[2]
+        out["dB"] += part[3]
+        out["dC"] += part[4]
+        out["dD"][hs] = part[5]
+        out["d_init"][:, hs] = part[6]
+    return out
