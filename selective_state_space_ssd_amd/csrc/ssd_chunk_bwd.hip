@@ -460,8 +460,7 @@ ChunkScanBwdPlan plan_chunk_scan_bwd(int b, int L, int H, int P, int N, int G, b
         const size_t part = size_t(b) * L * pl.nparts * N * 4;
         pl.off_hin = 0;
         pl.off_gh = align256b(st);
-        pl.off_ghn = pl.off_gh + align256b(st);
-        pl.off_dbp = pl.off_ghn + align256b(st);
+        pl.off_dbp = pl.off_gh + align256b(st);
         pl.off_dcp = pl.off_dbp + align256b(part);
         pl.off_dap = pl.off_dcp + align256b(part);
         pl.off_ddp = pl.off_dap + align256b(units * 4);

@@ -56,7 +56,7 @@ constexpr int kChainThreads = 512;   // 4 loader waves + 4 state waves
 // of the producing wave holding 4 consecutive bf16 at 4 l (tile element (4 (l / 16) +
 // i, l % 16) at 4 l + i), so every store writes 512 contiguous bytes.
 //   Hin^T, Gh^T: tile nt * 4 + pt holds rows p 16 pt .. (i), columns n 16 nt .. (l % 16)
-//   Gh:          tile pt * NT + nt holds rows n 16 nt .. (i), columns p 16 pt .. (l % 16)
+// (the chunk kernel reads Gh^T in both operand layouts from an LDS copy)
 __device__ __forceinline__ int tile_off(int tile, int l) { return tile * 256 + 4 * l; }
 
 // The 8 consecutive values (along the tile rows) that lane (r16, g4) of a consumer
@@ -94,9 +94,8 @@ struct ChainPf {
 // One barrier per step hands a staged buffer from the loaders to the state waves.
 // DIR 0: Hin_c for c = 0 .. nc-1 (as Hin^T tiles), starting from init_state, for FH
 //        heads of one group at once (they share B, so one staged V serves both).
-// DIR 1: Gh_c for c = nc-1 .. 0 (as Gh^T and Gh tiles) from d_final, then d_init.
-// The reverse walk holds its state twice, as tiles with rows p (stored as Gh^T) and
-// with rows n (stored as Gh); it walks one head.
+// DIR 1: Gh_c for c = nc-1 .. 0 (as Gh^T tiles) from d_final, then d_init; it walks
+// one head.
 // With FH = 2 the LDS of a workgroup (76 KiB) stays under half of the CU's 160 KiB, so
 // two fit; the per-buffer decay factors live in the unused padding of the first AT row.
 template <int N, int FH>
@@ -109,9 +108,9 @@ template <int N, int DIR, int FH>
 __device__ __forceinline__ void chain_walk(
     const bf16_bits *__restrict__ u, const float *__restrict__ dt, const float *__restrict__ A,
     const bf16_bits *__restrict__ v, const float *__restrict__ s0, bf16_bits *__restrict__ dstT,
-    bf16_bits *__restrict__ ghN, float *__restrict__ d_init, int L, int H, int G, int nc,
-    ChainLds<N, FH> &sm, int h, int bi) {
-    constexpr int NT = N / 16, NTW = NT / 4, NG = N / 8, PN = HP * N;
+    float *__restrict__ d_init, int L, int H, int G, int nc, ChainLds<N, FH> &sm, int h,
+    int bi) {
+    constexpr int NT = N / 16, NG = N / 8, PN = HP * N;
     constexpr int kVItems = (32 * NG + kThreads - 1) / kThreads;
     constexpr int WH = DIR == 0 ? FH : 1;   // heads this walk carries
     static_assert(HP + 2 * (2 * FH) <= RSA, "decay factors must fit in the row padding");
@@ -214,7 +213,6 @@ __device__ __forceinline__ void chain_walk(
     // ---------------------------------------------------- state waves
     const int sw = w - 4;
     f32x4 accP[WH][NT];
-    f32x4 accN[DIR ? NTW : 1][4];
 #pragma unroll
     for (int k = 0; k < WH; ++k)
 #pragma unroll
@@ -223,18 +221,6 @@ __device__ __forceinline__ void chain_walk(
             for (int i = 0; i < 4; ++i)
                 accP[k][nt][i] =
                     s0 ? s0[(bh + k) * PN + (16 * sw + 4 * g4 + i) * N + 16 * nt + r16] : 0.f;
-    if constexpr (DIR == 1) {
-#pragma unroll
-        for (int j = 0; j < NTW; ++j)
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
-                float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (s0)
-                    q = *reinterpret_cast<const float4 *>(
-                        s0 + bh * PN + (16 * pt + r16) * N + 16 * (NTW * sw + j) + 4 * g4);
-                accN[j][pt] = {q.x, q.y, q.z, q.w};
-            }
-    }
     __syncthreads();
     for (int step = 0; step < nc; ++step) {
         const int c = chunk_of(step);
@@ -255,15 +241,6 @@ __device__ __forceinline__ void chain_walk(
                 *reinterpret_cast<uint2 *>(dstT + so + size_t(k) * nc * PN + tile_off(nt * 4 + sw, lane)) =
                     make_uint2(pack_bf16x2(accP[k][nt][0], accP[k][nt][1]),
                                pack_bf16x2(accP[k][nt][2], accP[k][nt][3]));
-        if constexpr (DIR == 1) {
-#pragma unroll
-            for (int j = 0; j < NTW; ++j)
-#pragma unroll
-                for (int pt = 0; pt < 4; ++pt)
-                    *reinterpret_cast<uint2 *>(ghN + so + tile_off(pt * NT + NTW * sw + j, lane)) =
-                        make_uint2(pack_bf16x2(accN[j][pt][0], accN[j][pt][1]),
-                                   pack_bf16x2(accN[j][pt][2], accN[j][pt][3]));
-        }
         // the stores above are issued before the update starts: otherwise the packed
         // values stay live next to the update's operands and spill
         __builtin_amdgcn_sched_barrier(0);
@@ -282,22 +259,6 @@ __device__ __forceinline__ void chain_walk(
                 accP[k][nt] = mfma_bf16(a1, lds16(vt + (16 * nt + r16) * RS + 32 + 8 * g4), t);
             }
         }
-        if constexpr (DIR == 1) {
-            const float al = al_sh[buf * FH];
-            const bf16_bits *at = AT[buf][0];
-#pragma unroll
-            for (int j = 0; j < NTW; ++j) {
-                const int nt = NTW * sw + j;
-                const bf16x8 c0 = lds16(vt + (16 * nt + r16) * RS + 8 * g4);
-                const bf16x8 c1 = lds16(vt + (16 * nt + r16) * RS + 32 + 8 * g4);
-#pragma unroll
-                for (int pt = 0; pt < 4; ++pt) {
-                    f32x4 t = accN[j][pt] * al;
-                    t = mfma_bf16(c0, lds16(at + (16 * pt + r16) * RSA + 8 * g4), t);
-                    accN[j][pt] = mfma_bf16(c1, lds16(at + (16 * pt + r16) * RSA + 32 + 8 * g4), t);
-                }
-            }
-        }
         __syncthreads();
     }
     if constexpr (DIR == 1) {
@@ -308,11 +269,10 @@ __device__ __forceinline__ void chain_walk(
             asm volatile("" : "+v"(ln));
             const int r16 = ln & 15, g4 = ln >> 4;
 #pragma unroll
-            for (int j = 0; j < NTW; ++j)
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                for (int pt = 0; pt < 4; ++pt)
-                    *reinterpret_cast<float4 *>(d_init + bh * PN + (16 * pt + r16) * N + 16 * (NTW * sw + j) + 4 * g4) =
-                        make_float4(accN[j][pt][0], accN[j][pt][1], accN[j][pt][2], accN[j][pt][3]);
+                for (int i = 0; i < 4; ++i)
+                    d_init[bh * PN + (16 * sw + 4 * g4 + i) * N + 16 * nt + r16] = accP[0][nt][i];
         }
     }
 }
@@ -329,17 +289,16 @@ __global__ __launch_bounds__(kChainThreads, 4) void k_bwd_chain(
     const float *__restrict__ dt, const float *__restrict__ A, const bf16_bits *__restrict__ B,
     const bf16_bits *__restrict__ C, const float *__restrict__ init_state,
     const float *__restrict__ d_final, bf16_bits *__restrict__ hinT, bf16_bits *__restrict__ ghT,
-    bf16_bits *__restrict__ ghN, float *__restrict__ d_init, int L, int H, int G, int nc,
-    int nfwd) {
+    float *__restrict__ d_init, int L, int H, int G, int nc, int nfwd) {
     __shared__ __align__(16) ChainLds<N, FH> sm;
     const int wg = blockIdx.x;
     if (wg < nfwd) {
         const int hp = H / FH;
-        chain_walk<N, 0, FH>(x, dt, A, B, init_state, hinT, nullptr, nullptr, L, H, G, nc, sm,
+        chain_walk<N, 0, FH>(x, dt, A, B, init_state, hinT, nullptr, L, H, G, nc, sm,
                              FH * (wg % hp), wg / hp);
     } else {
         const int r = wg - nfwd;
-        chain_walk<N, 1, FH>(dy, dt, A, C, d_final, ghT, ghN, d_init, L, H, G, nc, sm, r % H,
+        chain_walk<N, 1, FH>(dy, dt, A, C, d_final, ghT, d_init, L, H, G, nc, sm, r % H,
                              r / H);
     }
 }
@@ -368,7 +327,8 @@ struct ChunkLds {
     static constexpr size_t off_MT = off_DYT + size_t(HP) * RS * 2;
     static constexpr size_t off_DS = off_MT + size_t(QB) * RS * 2;
     static constexpr size_t off_DST = off_DS + size_t(QB) * RS * 2;
-    static constexpr size_t bytes = off_DST + size_t(QB) * RS * 2;
+    static constexpr size_t off_GH = off_DST + size_t(QB) * RS * 2;   // Gh^T tiles of a head
+    static constexpr size_t bytes = off_GH + size_t(HP) * N * 2;
 };
 
 template <int N>
@@ -376,8 +336,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_bwd_chunk_bf(
     const bf16_bits *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
     const bf16_bits *__restrict__ B, const bf16_bits *__restrict__ C, const float *__restrict__ D,
     const bf16_bits *__restrict__ dy, const bf16_bits *__restrict__ hinT,
-    const bf16_bits *__restrict__ ghT, const bf16_bits *__restrict__ ghN,
-    bf16_bits *__restrict__ dx, float *__restrict__ ddt, float *__restrict__ dBp,
+    const bf16_bits *__restrict__ ghT, bf16_bits *__restrict__ dx, float *__restrict__ ddt, float *__restrict__ dBp,
     float *__restrict__ dCp, float *__restrict__ dAp, float *__restrict__ dDp, int L, int H,
     int G, int nc, int HB) {
     using Lay = ChunkLds<N>;
@@ -413,6 +372,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_bwd_chunk_bf(
     bf16_bits *MT = reinterpret_cast<bf16_bits *>(smem + Lay::off_MT);     // [s][t]
     bf16_bits *DS = reinterpret_cast<bf16_bits *>(smem + Lay::off_DS);     // [t][s]
     bf16_bits *DST = reinterpret_cast<bf16_bits *>(smem + Lay::off_DST);   // [s][t]
+    bf16_bits *GH = reinterpret_cast<bf16_bits *>(smem + Lay::off_GH);     // Gh^T tiles
 
     // one head's x (threads 0-255) or dy (threads 256-511): token pair tpu, p group pgu
     const bool is_dy = tid >= kThreads;
@@ -481,32 +441,62 @@ __global__ __launch_bounds__(kChunkThreads) void k_bwd_chunk_bf(
     }
 
     // a head's states as MFMA A operands (rows owned by this wave)
-    // (Gh: rows p of block q, k = n; Gh^T and Hin^T: rows n of tile ntw, k = p).  Gh,
-    // used first, is loaded one head ahead (issued once head hh's last use of those
-    // registers is done); Gh^T and Hin^T at the top of their head
+    // (Gh: rows p of block q, k = n; Gh^T and Hin^T: rows n of tile ntw, k = p).  Gh is
+    // stored once, as Gh^T tiles: a head's tiles are loaded one head ahead into
+    // registers (issued once the previous head's operands are built), copied to LDS at
+    // the top of the head, and both operand layouts are read from that copy.  Hin^T is
+    // read at the top of its head.
     uint4 ghp[KN], ght[2], hnt[2];
+    constexpr int GPT = HP * N * 2 / 16 / kChunkThreads;   // 16-byte pieces per thread
+    static_assert(GPT >= 1 && HP * N * 2 % (16 * kChunkThreads) == 0, "whole pieces");
+    uint4 ghq[GPT];
     auto state_view = [&](const bf16_bits *base, int hs) {
         const size_t so = ((size_t(bi) * H + h0 + hs) * nc + c) * size_t(PN);
         return buffer_rsrc(base + so, uint32_t(PN) * 2u);
     };
     auto load_gh = [&](int hs) {
-        const __amdgpu_buffer_rsrc_t gn = state_view(ghN, hs);
+        const __amdgpu_buffer_rsrc_t gt = state_view(ghT, hs);
 #pragma unroll
-        for (int kq = 0; kq < KN; ++kq) ghp[kq] = tile_operand(gn, q * NT, 1, kq, r16, g4);
+        for (int k = 0; k < GPT; ++k)
+            ghq[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   gt, (tid + k * kChunkThreads) * 16, 0, 0));
     };
     load_gh(0);
+    // 8 consecutive bf16 of the LDS copy at element stride 4: Gh[p][n0 .. n0+7] for the
+    // lane's row p = 16 q + r16, n0 = 32 kq + 8 g4 (tile (n0 / 16) * 4 + q, lane
+    // 16 (r16 / 4) + n0 % 16 + j, element r16 % 4)
+    auto gh_rows_p = [&](int kq) {
+        const int base = ((2 * kq + (g4 >> 1)) * 4 + q) * 256 + 4 * (16 * (r16 >> 2) + 8 * (g4 & 1)) +
+                         (r16 & 3);
+        uint32_t wv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            wv[j] = uint32_t(GH[base + 8 * j]) | (uint32_t(GH[base + 8 * j + 4]) << 16);
+        return make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    };
+    // Gh^T operand (rows n of tile ntw, k = p) from the LDS copy: the same two 8-byte
+    // pieces as tile_operand reads from memory
+    auto gh_rows_n = [&](int kp) {
+        const int tile = ntw * 4 + 2 * kp + (g4 >> 1);
+        const int l = r16 + 32 * (g4 & 1);
+        const uint2 lo = *reinterpret_cast<const uint2 *>(GH + tile_off(tile, l));
+        const uint2 hi = *reinterpret_cast<const uint2 *>(GH + tile_off(tile, l + 16));
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    };
 
     for (int hh = 0; hh < HB; ++hh) {
         const int h = h0 + hh;
         const size_t bhc = (size_t(bi) * H + h) * nc + c;
         {
-            const __amdgpu_buffer_rsrc_t gt = state_view(ghT, hh), ht = state_view(hinT, hh);
+            const __amdgpu_buffer_rsrc_t ht = state_view(hinT, hh);
 #pragma unroll
-            for (int kp = 0; kp < 2; ++kp) {
-                ght[kp] = tile_operand(gt, ntw * 4, 1, kp, r16, g4);
-                hnt[kp] = tile_operand(ht, ntw * 4, 1, kp, r16, g4);
-            }
+            for (int kp = 0; kp < 2; ++kp) hnt[kp] = tile_operand(ht, ntw * 4, 1, kp, r16, g4);
         }
+        // this head's Gh^T tiles to LDS (the previous head's reads of the copy ended
+        // before its last barrier)
+#pragma unroll
+        for (int k = 0; k < GPT; ++k)
+            *reinterpret_cast<uint4 *>(GH + (tid + k * kChunkThreads) * 8) = ghq[k];
         const float dreg = dnext;
         const float Ah = A[h];
         const float cs = wave_inclusive_scan(dreg * Ah * kLog2e);
@@ -534,6 +524,12 @@ __global__ __launch_bounds__(kChunkThreads) void k_bwd_chunk_bf(
         }
         if (hh + 1 < HB) load_head(h + 1);
         __syncthreads();
+        // both layouts of Gh from the LDS copy; then the next head's tiles can load
+#pragma unroll
+        for (int kq = 0; kq < KN; ++kq) ghp[kq] = gh_rows_p(kq);
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) ght[kp] = gh_rows_n(kp);
+        if (hh + 1 < HB) load_gh(hh + 1);
 
         // ---- scores on this wave's tiles: W = dy x^T, then M, dS and the sums
         {
@@ -616,8 +612,6 @@ __global__ __launch_bounds__(kChunkThreads) void k_bwd_chunk_bf(
                 if (g4 == 0) vsp[q * QB + s] = vp;
             }
         }
-        // Gh of the next head: its registers are free from here on
-        if (hh + 1 < HB) load_gh(hh + 1);
 
         // ---- dC^T[n][t] += BT dS^T + e^{cum_t} V^T,  V^T[n][t] = Hin^T[n] . dy_t
         {
@@ -747,7 +741,6 @@ hipError_t launch_n(const ChunkScanBwdArgs &a, const ChunkScanBwdPlan &pl, hipSt
     char *ws = static_cast<char *>(a.workspace);
     bf16_bits *hinT = reinterpret_cast<bf16_bits *>(ws + pl.off_hin);
     bf16_bits *ghT = reinterpret_cast<bf16_bits *>(ws + pl.off_gh);
-    bf16_bits *ghN = reinterpret_cast<bf16_bits *>(ws + pl.off_ghn);
     float *dBp = reinterpret_cast<float *>(ws + pl.off_dbp);
     float *dCp = reinterpret_cast<float *>(ws + pl.off_dcp);
     float *dAp = reinterpret_cast<float *>(ws + pl.off_dap);
@@ -759,12 +752,12 @@ hipError_t launch_n(const ChunkScanBwdArgs &a, const ChunkScanBwdPlan &pl, hipSt
     if ((a.H / a.G) % 2 == 0) {
         const int nfwd = a.b * a.H / 2;
         hipLaunchKernelGGL((k_bwd_chain<N, 2>), dim3(nfwd + a.b * a.H), dim3(kChainThreads), 0,
-                           stream, x, dy, a.dt, a.A, B, C, a.init_state, a.d_final, hinT, ghT, ghN,
+                           stream, x, dy, a.dt, a.A, B, C, a.init_state, a.d_final, hinT, ghT,
                            a.d_init, a.L, a.H, a.G, pl.nc, nfwd);
     } else {
         const int nfwd = a.b * a.H;
         hipLaunchKernelGGL((k_bwd_chain<N, 1>), dim3(nfwd + a.b * a.H), dim3(kChainThreads), 0,
-                           stream, x, dy, a.dt, a.A, B, C, a.init_state, a.d_final, hinT, ghT, ghN,
+                           stream, x, dy, a.dt, a.A, B, C, a.init_state, a.d_final, hinT, ghT,
                            a.d_init, a.L, a.H, a.G, pl.nc, nfwd);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -773,7 +766,7 @@ hipError_t launch_n(const ChunkScanBwdArgs &a, const ChunkScanBwdPlan &pl, hipSt
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_bwd_chunk_bf<N>), dim3(pl.nc, a.H / pl.hb, a.b), dim3(kChunkThreads), lds,
-                       stream, x, a.dt, a.A, B, C, a.D, dy, hinT, ghT, ghN,
+                       stream, x, a.dt, a.A, B, C, a.D, dy, hinT, ghT,
                        static_cast<bf16_bits *>(a.dx), a.ddt, dBp, dCp, dAp, dDp, a.L, a.H, a.G,
                        pl.nc, pl.hb);
     return hipGetLastError();

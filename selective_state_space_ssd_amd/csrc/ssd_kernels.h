@@ -152,7 +152,6 @@ struct ChunkScanBwdPlan {
     int nparts = 0;             // dB / dC partials per token: H (fp32 path) or H / hb
     size_t off_hin = 0;         // fp32 [b,H,nc,P,N] chunk states then Hin | bf16 Hin^T
     size_t off_gh = 0;          // fp32 [b,H,nc,P,N] adjoint sources then Gh | bf16 Gh^T
-    size_t off_ghn = 0;         // bf16 path: bf16 Gh [b,H,nc,P,N]
     size_t off_alpha = 0;       // fp32 path: fp32 [b,H,nc]
     size_t off_dbp = 0;         // fp32 [b, L, nparts, N]
     size_t off_dcp = 0;         // fp32 [b, L, nparts, N]
