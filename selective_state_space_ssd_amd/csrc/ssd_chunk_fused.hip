@@ -693,6 +693,11 @@ void k_ssd_fused(
                     }
             }
         }
+        // y of the wave's tiles, rounded and regrouped, stored together after the last
+        // tile: a store that cannot issue (the memory pipeline full of the next head's
+        // x loads) would otherwise hold up the products of the tiles after it
+        u32x4 yq[F::TPW][F::PT / 2];
+        uint32_t yoff[F::TPW];
 #pragma unroll
         for (int m = 0; m < F::TPW; ++m) {
             const int T = tile_of(m, w);
@@ -781,11 +786,11 @@ void k_ssd_fused(
                     }
                 }
             }
-            // epilogue: + D x, round to bf16, store y[t][p..p+3].  The stores go through
-            // a buffer resource that covers the chunk's qlen rows: rows past them are
-            // dropped by the range check, so no lane or wave branches around a store
-            // (and the compiler can count the stores in flight when it waits for the
-            // next head's x).  Streaming (non-temporal): y is not read again here.
+            // epilogue: + D x, round to bf16 (stored after the loop).  The stores go
+            // through a buffer resource that covers the chunk's qlen rows: rows past
+            // them are dropped by the range check, so no lane or wave branches around a
+            // store (and the compiler can count the stores in flight when it waits for
+            // the next head's x).  Streaming (non-temporal): y is not read again here.
             {
                 uint2 xd[F::PT];   // x[t][p0 .. p0+3]
                 const int tx = min(t, Q - 1);
@@ -813,13 +818,19 @@ void k_ssd_fused(
                 for (int pt = 0; pt < F::PT; pt += 2) {
                     const auto s0 = __builtin_amdgcn_permlane16_swap(v[pt][0], v[pt + 1][0], false, false);
                     const auto s1 = __builtin_amdgcn_permlane16_swap(v[pt][1], v[pt + 1][1], false, false);
-                    const u32x4 q = {s0[0], s1[0], s0[1], s1[1]};
-                    const int c0 = (pt + (g4 & 1)) * 16 + (g4 >> 1) * 8;
-                    __builtin_amdgcn_raw_buffer_store_b128(q, yres, int(row_off + 2u * c0), 0,
-                                                           kBufNonTemporal);
+                    yq[m][pt / 2] = u32x4{s0[0], s1[0], s0[1], s1[1]};
                 }
+                yoff[m] = row_off;
             }
         }
+#pragma unroll
+        for (int m = 0; m < F::TPW; ++m)
+#pragma unroll
+            for (int pt = 0; pt < F::PT; pt += 2) {
+                const int c0 = (pt + (g4 & 1)) * 16 + (g4 >> 1) * 8;
+                __builtin_amdgcn_raw_buffer_store_b128(yq[m][pt / 2], yres, int(yoff[m] + 2u * c0), 0,
+                                                       kBufNonTemporal);
+            }
         __syncthreads();
     }
 }
