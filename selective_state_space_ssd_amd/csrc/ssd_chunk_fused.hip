@@ -328,19 +328,18 @@ void k_ssd_fused(
     if (tid < Q) dtn[tid] = dt_first;
     __syncthreads();
 
-    // ---- G^T = B C^T tiles of this wave's output tiles, kept as MFMA B operands
-    // gfrag[m][S]: off-diagonal 32-token block S of tile slot m, bf16
-    // gdiag[m][.]: the diagonal block in fp32 (masked per head later)
-    constexpr int kSlots = (kFW / 2) * F::TPW;     // max off-diagonal blocks of a slot
+    // ---- G^T = B C^T tiles of this wave's output tiles, kept as MFMA B operands:
+    // gfrag[m][S] is 32-token block S of tile slot m in bf16, for S = 0 .. T / 2; the
+    // last of them is the diagonal block, causally masked (head independent)
+    constexpr int kSlots = (kFW / 2) * F::TPW;     // max blocks of a slot
     uint4 gfrag[F::TPW][kSlots];
-    float gdiag[F::TPW][8];
 #pragma unroll
     for (int m = 0; m < F::TPW; ++m) {
         const int T = tile_of(m, w);
         if (T >= F::NT) continue;
-        const int nsb = T / 2;   // off-diagonal blocks of this tile
+        const int nsb = T / 2, t = 16 * T + r16;
 #pragma unroll
-        for (int S = 0; S <= (kFW / 2) * (m + 1) - 1; ++S) {
+        for (int S = 0; S <= (kFW / 2) * (m + 1) - 1 && S < F::NSB; ++S) {
             if (S > nsb) break;
             f32x4 gt[2];
 #pragma unroll
@@ -352,39 +351,20 @@ void k_ssd_fused(
                     gt[half] = mfma_bf16(as_bf16x8(*reinterpret_cast<const uint4 *>(brow + 32 * kk)),
                                          as_bf16x8(cf[m][kk]), gt[half]);
             }
-            if (S < nsb) {
-                gfrag[m][S] = make_uint4(pack_bf16x2(gt[0][0], gt[0][1]),
-                                         pack_bf16x2(gt[0][2], gt[0][3]),
-                                         pack_bf16x2(gt[1][0], gt[1][1]),
-                                         pack_bf16x2(gt[1][2], gt[1][3]));
-            } else {
+            if (S == nsb) {   // keep s <= t only
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    gdiag[m][i] = gt[0][i];
-                    gdiag[m][4 + i] = gt[1][i];
-                }
+                for (int half = 0; half < 2; ++half)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (32 * S + 16 * half + 4 * g4 + i > t) gt[half][i] = 0.f;
             }
+            gfrag[m][S] = make_uint4(pack_bf16x2(gt[0][0], gt[0][1]),
+                                     pack_bf16x2(gt[0][2], gt[0][3]),
+                                     pack_bf16x2(gt[1][0], gt[1][1]),
+                                     pack_bf16x2(gt[1][2], gt[1][3]));
         }
     }
     __syncthreads();   // Bnat is overwritten by the first head's x
-
-    // causally masked diagonal score tile (head independent), bf16 B operand
-    uint4 gdmask[F::TPW];
-#pragma unroll
-    for (int m = 0; m < F::TPW; ++m) {
-        const int T = tile_of(m, w);
-        const int t = 16 * T + r16, nsb = T / 2;
-        float mv[8];
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int s = 32 * nsb + 16 * half + 4 * g4 + i;
-                mv[4 * half + i] = (T < F::NT && s <= t) ? gdiag[m][4 * half + i] : 0.f;
-            }
-        gdmask[m] = make_uint4(pack_bf16x2(mv[0], mv[1]), pack_bf16x2(mv[2], mv[3]),
-                               pack_bf16x2(mv[4], mv[5]), pack_bf16x2(mv[6], mv[7]));
-    }
 
     // state tiles of this wave (step 2 accumulators and the hand-off)
     const int nt_base = F::kGrid22 ? 2 * (w % 4) : F::NTN >= kFW ? w : (w % F::NTN);
@@ -696,6 +676,62 @@ void k_ssd_fused(
         // y of the wave's tiles, rounded and regrouped, stored together after the last
         // tile: a store that cannot issue (the memory pipeline full of the next head's
         // x loads) would otherwise hold up the products of the tiles after it
+        // step 1 in the usual case, for all tile slots at once: x decayed to the chunk
+        // end against the score tiles of every block up to the diagonal one, then each
+        // output column rescaled to its own token.  A slot's blocks are 0 .. T / 2, so
+        // the slots of a wave share their first blocks: each x fragment read from LDS
+        // feeds every slot that reaches its block.  The fragments of block S + kDepth - 1
+        // are read while block S is multiplied.
+        if (fast) {
+            int nsbm[F::TPW];
+            int nmax = -1;   // uniform over the wave
+#pragma unroll
+            for (int m = 0; m < F::TPW; ++m) {
+                nsbm[m] = slot_ok[m] ? tile_of(m, w) / 2 : -1;
+                nmax = max(nmax, nsbm[m]);
+            }
+            constexpr int DP = F::kDepth;
+            uint4 xf8[DP][F::PT];   // tokens 32S + 4g4 + 0..3 and 32S + 16 + 4g4 + 0..3
+#pragma unroll
+            for (int L = 0; L < DP - 1; ++L)
+#pragma unroll
+                for (int pt = 0; pt < F::PT; ++pt)
+                    xf8[L][pt] = *reinterpret_cast<const uint4 *>(
+                        XwT + (pt * 16 + r16) * F::QS + 32 * L + 8 * g4);
+#pragma unroll
+            for (int S = 0; S < F::NSB; ++S) {
+                if (S > nmax) break;
+                const int L = S + DP - 1;
+                if (L <= nmax) {
+#pragma unroll
+                    for (int pt = 0; pt < F::PT; ++pt)
+                        xf8[L % DP][pt] = *reinterpret_cast<const uint4 *>(
+                            XwT + (pt * 16 + r16) * F::QS + 32 * L + 8 * g4);
+                }
+                if (DP > 1) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int m = 0; m < F::TPW; ++m) {
+                    if (S > (kFW / 2) * (m + 1) - 1) continue;   // past any tile of slot m
+                    if (S <= nsbm[m]) {
+                        const uint4 gop = gfrag[m][S];
+#pragma unroll
+                        for (int pt = 0; pt < F::PT; ++pt)
+                            acc[m][pt] = mfma_bf16(as_bf16x8(xf8[S % DP][pt]), as_bf16x8(gop),
+                                                   acc[m][pt]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < F::TPW; ++m) {
+                const int t = 16 * tile_of(m, w) + r16;
+                const float u = slot_ok[m] && t < qlen ? __builtin_amdgcn_exp2f(acum[t] - aend) : 0.f;
+#pragma unroll
+                for (int pt = 0; pt < F::PT; ++pt) acc[m][pt] *= u;
+            }
+        }
+        // y of the wave's tiles, rounded and regrouped, stored together after the last
+        // tile: a store that cannot issue (the memory pipeline full of the next head's
+        // x loads) would otherwise hold up the products of the tiles after it
         u32x4 yq[F::TPW][F::PT / 2];
         uint32_t yoff[F::TPW];
 #pragma unroll
@@ -705,45 +741,10 @@ void k_ssd_fused(
             const int t = tl0 + r16;
             const bool tv = t < qlen;
             const int nsb = T / 2;
-            if (!slot_ok[m]) {
-                // nothing to compute; the epilogue still runs (its stores fall outside
-                // the chunk's rows and are dropped) so that every wave issues the same
-                // stores on every path
-            } else if (fast) {
-                const float at = acum[t];
-                // step 1, all blocks up to and including the diagonal one, against x
-                // decayed to the chunk end; then rescale column t to its own token.
-                // The x fragments of block S + kDepth - 1 are read while block S is
-                // multiplied.
-                constexpr int DP = F::kDepth;
-                uint4 xf8[DP][F::PT];   // tokens 32S + 4g4 + 0..3 and 32S + 16 + 4g4 + 0..3
-#pragma unroll
-                for (int L = 0; L < DP - 1; ++L)
-#pragma unroll
-                    for (int pt = 0; pt < F::PT; ++pt)
-                        xf8[L][pt] = *reinterpret_cast<const uint4 *>(
-                            XwT + (pt * 16 + r16) * F::QS + 32 * L + 8 * g4);
-#pragma unroll
-                for (int S = 0; S <= (kFW / 2) * (m + 1) - 1; ++S) {   // nsb's bound
-                    if (S > nsb) break;
-                    const int L = S + DP - 1;
-                    if (L <= nsb) {
-#pragma unroll
-                        for (int pt = 0; pt < F::PT; ++pt)
-                            xf8[L % DP][pt] = *reinterpret_cast<const uint4 *>(
-                                XwT + (pt * 16 + r16) * F::QS + 32 * L + 8 * g4);
-                    }
-                    if (DP > 1) __builtin_amdgcn_sched_barrier(0);
-                    const uint4 gop = S < nsb ? gfrag[m][S] : gdmask[m];
-#pragma unroll
-                    for (int pt = 0; pt < F::PT; ++pt)
-                        acc[m][pt] = mfma_bf16(as_bf16x8(xf8[S % DP][pt]),
-                                               as_bf16x8(gop), acc[m][pt]);
-                }
-                const float u = tv ? __builtin_amdgcn_exp2f(at - aend) : 0.f;
-#pragma unroll
-                for (int pt = 0; pt < F::PT; ++pt) acc[m][pt] *= u;
-            } else {
+            // a slot without rows computes nothing; the epilogue still runs (its stores
+            // fall outside the chunk's rows and are dropped) so that every wave issues
+            // the same stores on every path
+            if (slot_ok[m] && !fast) {
                 // exact fallback: entering state decays by 2^acum_t; every score tile
                 // (off-diagonal and the masked diagonal one) is multiplied element by
                 // element by dt_s 2^(acum_t - acum_s) and contracted with x as given
@@ -755,10 +756,10 @@ void k_ssd_fused(
                 // is picked from the register array with a static select chain
 #pragma unroll 1
                 for (int S = 0; S <= nsb; ++S) {
-                    uint4 gsrc = gdmask[m];   // block nsb is the diagonal one
+                    uint4 gsrc = gfrag[m][0];
 #pragma unroll
-                    for (int k = 0; k < kSlots; ++k)
-                        if (k == S && S < nsb) gsrc = gfrag[m][k];
+                    for (int k = 1; k < kSlots && k < F::NSB; ++k)
+                        if (k == S) gsrc = gfrag[m][k];
                     float mv[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
