@@ -323,14 +323,33 @@ ssd_status_t ssd_verify_ring_rollback(int32_t *meta, const int32_t *steps, int32
 /*
  * Sequence (context) parallelism: the per-device pieces.
  *
- * A long sequence is split into n slices, one per device (Mamba-2 article, «序列并行»):
- * each device scans its slice from a zero state with ssd_chunk_scan_fwd; the devices
- * exchange (alpha, S) = (total decay of the slice, its final state); each device folds
- * its predecessors' pairs into the state h_in entering its slice and corrects its
- * slice.  The pairs compose associatively because the state passing is linear (the
- * scan over chunks of «SSD 算法：分块和形态传递», step 3, run over slices).  The
- * exchange is a collective outside this library; on one device the three calls below
- * and the per-slice scans reproduce the scan of the whole sequence.
+ * A long sequence is split into n slices, one per device (Mamba-2 article, «序列并行»).
+ * The devices exchange (alpha, S) = (total decay of the slice, the state it leaves from
+ * a zero start), and each device folds its predecessors' pairs into the state h_in
+ * entering its slice.  The pairs compose associatively because the state passing is
+ * linear (the scan over chunks of «SSD 算法：分块和形态传递», step 3, run over slices).
+ * Two orders of work give the same outputs:
+ *   states first: ssd_seq_slice_state gives the pair without computing any output;
+ *     after the exchange, ssd_seq_combine gives h_in and ssd_chunk_scan_fwd with
+ *     init_state = h_in gives the slice's y and final state in one pass;
+ *   outputs first: ssd_chunk_scan_fwd from a zero state gives y and S,
+ *     ssd_seq_total_decay gives alpha, and after the exchange and ssd_seq_combine,
+ *     ssd_seq_apply_state adds h_in's contribution to y and the final state.
+ * The exchange is a collective outside this library; on one device these calls and
+ * the per-slice scans reproduce the scan of the whole sequence.
+ *
+ * ssd_seq_slice_state: state[b, h] = the final state of the recurrence at the top of
+ *   this file run over the slice from a zero state (what ssd_chunk_scan_fwd returns as
+ *   final_state with init_state NULL), alpha[b, h] = the total decay of the slice
+ *   (the product of the decays of its chunks, exp(sum_t dt A) up to rounding).  It
+ *   computes the chunk states of step 2 and folds them with the scan of step 3; no
+ *   output y is formed.  x [b, L, H, P] and B [b, L, G, N] io, 16-byte aligned; dt
+ *   [b, L, H], A [H]; state [b, H, P, N] (16-byte aligned) and alpha [b, H] fp32.  The
+ *   caller passes a workspace of ssd_seq_slice_state_workspace_bytes (16-byte
+ *   aligned; 0 bytes when L = 0; (size_t)-1 means dimensions this build does not
+ *   run), which holds the chunk states between the two
+ *   launches and may be reused once the call has completed.  Supported: P in {16, 32,
+ *   64, 128}, N a multiple of 16 up to 256.  L = 0 gives a zero state and alpha = 1.
  *
  * ssd_seq_total_decay: alpha[b, h] = exp(sum_t dt[b, t, h] * A[h]) over the slice;
  *   dt [b, L, H], A [H], alpha [b, H], all fp32 (L = 0 gives 1).
@@ -346,6 +365,12 @@ ssd_status_t ssd_verify_ring_rollback(int32_t *meta, const int32_t *steps, int32
  *   multiples of 16, at most 256.  L = 0 leaves y alone and adds h_in to final_state.
  * Outputs must not overlap inputs.  Errors as for the other entry points.
  */
+size_t ssd_seq_slice_state_workspace_bytes(int b, int L, int H, int P, int N, int G,
+                                           ssd_dtype_t io);
+ssd_status_t ssd_seq_slice_state(const void *x, const float *dt, const float *A, const void *B,
+                                 float *state, float *alpha, int b, int L, int H, int P, int N,
+                                 int G, ssd_dtype_t io, void *workspace, size_t workspace_bytes,
+                                 void *hip_stream);
 ssd_status_t ssd_seq_total_decay(const float *dt, const float *A, float *alpha, int b, int L,
                                  int H, void *hip_stream);
 ssd_status_t ssd_seq_combine(const float *alpha, const float *S, const float *init_state,

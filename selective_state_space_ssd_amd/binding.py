@@ -33,6 +33,7 @@ EXPORTED = ("ssd_chunk_scan_workspace_bytes", "ssd_chunk_scan_workspace_init",
             "ssd_chunk_scan_fwd_noalloc", "ssd_verify_step", "ssd_selective_scan_fwd",
             "ssd_chunk_scan_bwd_workspace_bytes", "ssd_chunk_scan_bwd",
             "ssd_verify_ring_init", "ssd_verify_ring", "ssd_verify_ring_rollback",
+            "ssd_seq_slice_state_workspace_bytes", "ssd_seq_slice_state",
             "ssd_seq_total_decay", "ssd_seq_combine", "ssd_seq_apply_state",
             "ssd_status_string", "ssd_version")
 
@@ -79,6 +80,10 @@ def lib() -> ctypes.CDLL:
         L.ssd_verify_ring.restype = i32
         L.ssd_verify_ring_rollback.argtypes = [vp, vp, vp, i32, i32, vp]
         L.ssd_verify_ring_rollback.restype = i32
+        L.ssd_seq_slice_state_workspace_bytes.argtypes = [i32] * 6 + [i32]
+        L.ssd_seq_slice_state_workspace_bytes.restype = sz
+        L.ssd_seq_slice_state.argtypes = [vp] * 6 + [i32] * 6 + [i32, vp, sz, vp]
+        L.ssd_seq_slice_state.restype = i32
         L.ssd_seq_total_decay.argtypes = [vp, vp, vp, i32, i32, i32, vp]
         L.ssd_seq_total_decay.restype = i32
         L.ssd_seq_combine.argtypes = [vp] * 4 + [i32] * 5 + [vp]
@@ -308,6 +313,29 @@ def ssd_verify_ring_rollback(meta, steps, err_flag=None, R=None, stream=None) ->
         raise SSDError(st, "ssd_verify_ring_rollback")
 
 
+def ssd_seq_slice_state_workspace_bytes(b, L, H, P, N, G, io) -> int:
+    n = lib().ssd_seq_slice_state_workspace_bytes(b, L, H, P, N, G, io)
+    if n == ctypes.c_size_t(-1).value:
+        raise SSDError(4, "ssd_seq_slice_state_workspace_bytes")
+    return n
+
+
+def ssd_seq_slice_state(x, dt, A, B, state, alpha, workspace, stream=None) -> None:
+    """state [b,H,P,N] and alpha [b,H] (float32) of the slice x, dt, B from a zero state;
+    workspace: a uint8 GPU tensor of ssd_seq_slice_state_workspace_bytes (or None when 0)."""
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    f32 = torch.float32
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    st = lib().ssd_seq_slice_state(_ptr(x, "x", x.dtype), _ptr(dt, "dt", f32), _ptr(A, "A", f32),
+                                   _ptr(B, "B", x.dtype), _ptr(state, "state", f32),
+                                   _ptr(alpha, "alpha", f32), b, L, H, P, N, G, _io_code(x),
+                                   _ptr(workspace, "workspace", torch.uint8), ws_bytes,
+                                   _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_seq_slice_state")
+
+
 def ssd_seq_total_decay(dt, A, alpha, stream=None) -> None:
     """alpha[b,h] = exp(sum_t dt[b,t,h] A[h]) (all float32)."""
     b, L, H = dt.shape
@@ -351,6 +379,18 @@ def chunk_scan_workspace(x, B, Q, stream=None) -> torch.Tensor:
     ws = torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
     ssd_chunk_scan_workspace_init(ws, stream)
     return ws
+
+
+def seq_slice_state(x, dt, A, B, stream=None):
+    """Allocate the outputs and the workspace; returns (state, alpha) of the slice."""
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    n = ssd_seq_slice_state_workspace_bytes(b, L, H, P, N, G, _io_code(x))
+    ws = torch.empty(n, dtype=torch.uint8, device=x.device) if n else None
+    state = torch.empty((b, H, P, N), dtype=torch.float32, device=x.device)
+    alpha = torch.empty((b, H), dtype=torch.float32, device=x.device)
+    ssd_seq_slice_state(x, dt, A, B, state, alpha, ws, stream)
+    return state, alpha
 
 
 def chunk_scan_fwd(x, dt, A, B, C, D, Q, init_state=None, workspace=None, stream=None):

@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 SOURCES = ["ssd_api.hip", "ssd_verify.hip", "ssd_chunk_scan.hip", "ssd_chunk_fused.hip",
            "ssd_selective_scan.hip", "ssd_chunk_bwd.hip",
-           "ssd_chunk_bwd_bf16.hip", "ssd_seqpar.hip"]
+           "ssd_chunk_bwd_bf16.hip", "ssd_seqpar.hip", "ssd_slice_state.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

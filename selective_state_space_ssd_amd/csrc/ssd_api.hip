@@ -387,6 +387,44 @@ ssd_status_t ssd_seq_total_decay(const float *dt, const float *A, float *alpha, 
     return SSD_OK;
 }
 
+size_t ssd_seq_slice_state_workspace_bytes(int b, int L, int H, int P, int N, int G,
+                                           ssd_dtype_t io) {
+    if (io != SSD_DTYPE_F32 && io != SSD_DTYPE_BF16) return size_t(-1);
+    if (b < 0 || L < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0) return size_t(-1);
+    const ssd::SliceStatePlan pl = ssd::plan_slice_state(b, L, H, P, N, G, io == SSD_DTYPE_BF16);
+    return pl.supported ? pl.total : size_t(-1);
+}
+
+ssd_status_t ssd_seq_slice_state(const void *x, const float *dt, const float *A, const void *B,
+                                 float *state, float *alpha, int b, int L, int H, int P, int N,
+                                 int G, ssd_dtype_t io, void *workspace, size_t workspace_bytes,
+                                 void *hip_stream) {
+    if (io != SSD_DTYPE_F32 && io != SSD_DTYPE_BF16) return SSD_ERR_UNSUPPORTED;
+    if (b < 0 || L < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0) return SSD_ERR_BAD_DIM;
+    if (H % G != 0) return SSD_ERR_GROUPS;
+    const bool bf16 = io == SSD_DTYPE_BF16;
+    const ssd::SliceStatePlan pl = ssd::plan_slice_state(b, L, H, P, N, G, bf16);
+    if (!pl.supported) return SSD_ERR_UNSUPPORTED;
+    if (b == 0) return SSD_OK;
+    if (!A || !state || !alpha || (L > 0 && (!x || !dt || !B))) return SSD_ERR_NULL_ARG;
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(state, 16) || !aligned(dt, 4) ||
+        !aligned(A, 4) || !aligned(alpha, 4) || !aligned(workspace, 16))
+        return SSD_ERR_ALIGN;
+    if (pl.total > 0 && (!workspace || workspace_bytes < pl.total)) return SSD_ERR_WORKSPACE;
+    const size_t esz = bf16 ? 2 : 4;
+    const Range rs(state, size_t(b) * H * P * N * 4), ra(alpha, size_t(b) * H * 4),
+        rw(workspace, pl.total);
+    const Range ins[] = {Range(x, size_t(b) * L * H * P * esz), Range(dt, size_t(b) * L * H * 4),
+                         Range(A, size_t(H) * 4), Range(B, size_t(b) * L * G * N * esz)};
+    for (const Range &in : ins)
+        if (rs.overlaps(in) || ra.overlaps(in) || rw.overlaps(in)) return SSD_ERR_ALIAS;
+    if (rs.overlaps(ra) || rs.overlaps(rw) || ra.overlaps(rw)) return SSD_ERR_ALIAS;
+    if (ssd::launch_slice_state(x, dt, A, B, state, alpha, workspace, b, L, H, P, N, G, bf16, pl,
+                                static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+        return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
 ssd_status_t ssd_seq_combine(const float *alpha, const float *S, const float *init_state,
                              float *h_in, int n, int b, int H, int P, int N, void *hip_stream) {
     if (n < 0 || b < 0 || H <= 0 || P <= 0 || N <= 0) return SSD_ERR_BAD_DIM;

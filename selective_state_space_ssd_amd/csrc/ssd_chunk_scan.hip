@@ -24,6 +24,8 @@
 // the transposed score tile (B C^T, rows s, cols t) whose accumulator layout is
 // directly the B operand of the next MFMA, so the masked scores never leave
 // registers.
+#include <type_traits>
+
 #include "ssd_device.h"
 #include "ssd_kernels.h"
 #include "ssd_stage.h"
@@ -89,32 +91,53 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(
 }
 
 // ---------------------------------------------------------------- step 3 kernel
+// The scan over the chunk states, four state elements per thread: H_{-1} = init_state
+// (zeros if null), hprev[c] = H_{c-1} (not written when hprev is null), H_c = alpha_c
+// H_{c-1} + S_c, final_state = H_{nc-1} (when not null), and alpha_total = the product
+// of the chunk decays (when not null).  The states and decays of 8 chunks are loaded
+// ahead of the dependent chain.
 template <typename IO>
 __global__ __launch_bounds__(kThreads) void k_state_pass(
     const float *__restrict__ S, const float *__restrict__ alpha,
-    const float *init_state, IO *__restrict__ hprev, float *final_state, int H, int PN,
-    int nc) {
+    const float *init_state, IO *__restrict__ hprev, float *final_state, float *alpha_total,
+    int H, int PN, int nc) {
+    constexpr int kBatch = 8;
     const size_t bh = size_t(blockIdx.z) * H + blockIdx.y;
     const int e = (blockIdx.x * kThreads + threadIdx.x) * 4;
     if (e >= PN) return;
     float4 hc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (init_state) hc = *reinterpret_cast<const float4 *>(init_state + bh * PN + e);
-    for (int c = 0; c < nc; ++c) {
-        const size_t off = (bh * nc + c) * size_t(PN) + e;
-        const float4 s = *reinterpret_cast<const float4 *>(S + off);
-        const float al = alpha[bh * nc + c];
-        if constexpr (std::is_same_v<IO, float>) {
-            *reinterpret_cast<float4 *>(hprev + off) = hc;
-        } else {
-            *reinterpret_cast<uint2 *>(hprev + off) =
-                make_uint2(pack_bf16x2(hc.x, hc.y), pack_bf16x2(hc.z, hc.w));
+    float at = 1.f;
+    for (int c0 = 0; c0 < nc; c0 += kBatch) {
+        float4 sv[kBatch];
+        float al[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int c = min(c0 + k, nc - 1);
+            sv[k] = *reinterpret_cast<const float4 *>(S + (bh * nc + c) * size_t(PN) + e);
+            al[k] = alpha[bh * nc + c];
         }
-        hc.x = al * hc.x + s.x;
-        hc.y = al * hc.y + s.y;
-        hc.z = al * hc.z + s.z;
-        hc.w = al * hc.w + s.w;
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            if (c0 + k >= nc) break;
+            if (hprev) {
+                const size_t off = (bh * nc + c0 + k) * size_t(PN) + e;
+                if constexpr (std::is_same_v<IO, float>) {
+                    *reinterpret_cast<float4 *>(hprev + off) = hc;
+                } else {
+                    *reinterpret_cast<uint2 *>(hprev + off) =
+                        make_uint2(pack_bf16x2(hc.x, hc.y), pack_bf16x2(hc.z, hc.w));
+                }
+            }
+            hc.x = al[k] * hc.x + sv[k].x;
+            hc.y = al[k] * hc.y + sv[k].y;
+            hc.z = al[k] * hc.z + sv[k].z;
+            hc.w = al[k] * hc.w + sv[k].w;
+            at *= al[k];
+        }
     }
     if (final_state) *reinterpret_cast<float4 *>(final_state + bh * PN + e) = hc;
+    if (alpha_total && e == 0) alpha_total[bh] = at;
 }
 
 // ------------------------------------------------------------- steps 1 + 4 kernel
@@ -330,7 +353,7 @@ hipError_t launch_p(const ChunkScanArgs &a, const ChunkScanPlan &pl, hipStream_t
     const int PN = P * a.N;
     const dim3 gpass((PN / 4 + kThreads - 1) / kThreads, a.H, a.b);
     hipLaunchKernelGGL((k_state_pass<IO>), gpass, dim3(kThreads), 0, stream, S, alpha,
-                       a.init_state, hprev, a.final_state, a.H, PN, pl.nc);
+                       a.init_state, hprev, a.final_state, nullptr, a.H, PN, pl.nc);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
     hipLaunchKernelGGL((k_chunk_out<IO, P>), grid, dim3(kThreads), pl.lds_out, stream, x, a.dt,
@@ -382,6 +405,51 @@ hipError_t launch_chunk_scan(const ChunkScanArgs &a, const ChunkScanPlan &pl,
                              hipStream_t stream) {
     if (a.bf16) return launch_io<bf16_bits>(a, pl, stream);
     return launch_io<float>(a, pl, stream);
+}
+
+size_t chunk_states_lds(int P, int N, int Q, bool bf16) {
+    return bf16 ? lds_state_bytes<bf16_bits>(P, N, Q) : lds_state_bytes<float>(P, N, Q);
+}
+
+hipError_t launch_chunk_states(const void *x, const float *dt, const float *A, const void *B,
+                               float *S, float *alpha, int b, int L, int H, int P, int N, int G,
+                               int Q, bool bf16, hipStream_t stream) {
+    const int nc = (L + Q - 1) / Q;
+    if (nc == 0 || b == 0) return hipSuccess;
+    const size_t lds = chunk_states_lds(P, N, Q, bf16);
+    const dim3 grid(nc, H, b);
+    hipError_t e = hipErrorInvalidValue;
+    auto go = [&](auto io_tag, auto p_tag) {
+        using IO = decltype(io_tag);
+        constexpr int PP = decltype(p_tag)::value;
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_chunk_state<IO, PP>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+        if (e != hipSuccess) return;
+        hipLaunchKernelGGL((k_chunk_state<IO, PP>), grid, dim3(kThreads), lds, stream,
+                           static_cast<const IO *>(x), dt, A, static_cast<const IO *>(B), S,
+                           alpha, L, H, N, G, Q, nc);
+        e = hipGetLastError();
+    };
+    auto by_p = [&](auto io_tag) {
+        switch (P) {
+            case 16: go(io_tag, std::integral_constant<int, 16>{}); break;
+            case 32: go(io_tag, std::integral_constant<int, 32>{}); break;
+            case 64: go(io_tag, std::integral_constant<int, 64>{}); break;
+            case 128: go(io_tag, std::integral_constant<int, 128>{}); break;
+            default: break;
+        }
+    };
+    if (bf16) by_p(bf16_bits{}); else by_p(float{});
+    return e;
+}
+
+hipError_t launch_state_fold(const float *S, const float *alpha, float *state, float *alpha_total,
+                             int b, int H, int PN, int n, hipStream_t stream) {
+    if (b == 0) return hipSuccess;
+    const dim3 gpass((PN / 4 + kThreads - 1) / kThreads, H, b);
+    hipLaunchKernelGGL((k_state_pass<float>), gpass, dim3(kThreads), 0, stream, S, alpha, nullptr,
+                       static_cast<float *>(nullptr), state, alpha_total, H, PN, n);
+    return hipGetLastError();
 }
 
 hipError_t launch_copy_state(const float *init_state, float *final_state, size_t count,

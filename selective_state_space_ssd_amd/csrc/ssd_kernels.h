@@ -183,6 +183,39 @@ hipError_t launch_seq_apply(void *y, float *final_state, const float *dt, const 
                             const void *C, const float *h_in, int b, int L, int H, int P, int N,
                             int G, bool bf16, hipStream_t stream);
 
+// Step 2 alone over chunks of Q tokens (ssd_chunk_scan.hip): S fp32 [b, H, nc, P, N]
+// and the chunk decays alpha fp32 [b, H, nc]; LDS the kernel needs for a shape.
+size_t chunk_states_lds(int P, int N, int Q, bool bf16);
+hipError_t launch_chunk_states(const void *x, const float *dt, const float *A, const void *B,
+                               float *S, float *alpha, int b, int L, int H, int P, int N, int G,
+                               int Q, bool bf16, hipStream_t stream);
+// Step 3 over n pieces from a zero state, final state only: state = the fold of
+// S [b, H, n, P * N] by alpha [b, H, n]; alpha_total [b, H] = the product of alpha.
+hipError_t launch_state_fold(const float *S, const float *alpha, float *state, float *alpha_total,
+                             int b, int H, int PN, int n, hipStream_t stream);
+
+// The state a slice of the sequence leaves from a zero start, and its total decay
+// (the pair one device contributes to the sequence-parallel scan; ssd_slice_state.hip).
+// The slice is cut into `parts` runs of tokens; each run's state (from zero) and decay
+// go to the workspace, fp32 [b, H, parts, P, N] then fp32 [b, H, parts], and the scan
+// of step 3 folds them.  bf16 I/O with P = 64 and N in {64, 128, 256} has a kernel of
+// its own (runs of 128-token segments, the state kept in registers along a run); other
+// shapes take the chunk-state kernel of the three-kernel path, one run per chunk.
+struct SliceStatePlan {
+    bool fast = false;          // the dedicated kernel
+    int Q = 0;                  // generic path: chunk length (the longest that fits in LDS)
+    int segs_per_part = 0;      // dedicated kernel: 128-token segments per run
+    int parts = 0;              // runs folded by step 3
+    size_t off_alpha = 0;
+    size_t total = 0;           // workspace bytes (0 for an empty problem)
+    bool supported = false;
+};
+SliceStatePlan plan_slice_state(int b, int L, int H, int P, int N, int G, bool bf16);
+hipError_t launch_slice_state(const void *x, const float *dt, const float *A, const void *B,
+                              float *state, float *alpha_total, void *workspace, int b, int L,
+                              int H, int P, int N, int G, bool bf16, const SliceStatePlan &plan,
+                              hipStream_t stream);
+
 // final_state = init_state (or zeros) for an empty sequence.
 hipError_t launch_copy_state(const float *init_state, float *final_state, size_t count,
                              hipStream_t stream);

@@ -363,3 +363,41 @@ def test_seqpar_host_checks(lib):
     assert call(C=addr(5, 8)) == ALIGN
     assert call(y=addr(5)) == ALIAS                  # y on C
     assert call(f=addr(6)) == ALIAS                  # final_state on h_in
+
+
+def test_slice_state_host_checks(lib):
+    # b=1, L=512, H=4, P=64, N=128, G=1, bf16: the dedicated kernel, 4 runs of one
+    # 128-token segment per head (at most one run per segment, about 512 workgroups)
+    need = lib.ssd_seq_slice_state_workspace_bytes(1, 512, 4, 64, 128, 1, 1)
+    ws = lambda units, pn: ((units * pn * 4 + 255) // 256 + (units * 4 + 255) // 256) * 256
+    assert need == ws(1 * 4 * 4, 64 * 128)
+    # b=8, L=4096, H=32: 256 heads fill the 512 workgroups with 2 runs of 16 segments
+    assert lib.ssd_seq_slice_state_workspace_bytes(8, 4096, 32, 64, 128, 1, 1) == ws(8 * 32 * 2, 64 * 128)
+    # fp32 I/O takes the chunk-state kernel: 128-token chunks fit the LDS at N = 128
+    assert lib.ssd_seq_slice_state_workspace_bytes(1, 512, 4, 64, 128, 1, 0) == ws(4 * 4, 64 * 128)
+    assert lib.ssd_seq_slice_state_workspace_bytes(1, 0, 4, 64, 128, 1, 1) == 0
+    bad = ctypes.c_size_t(-1).value
+    assert lib.ssd_seq_slice_state_workspace_bytes(1, 512, 4, 48, 128, 1, 1) == bad   # P
+    assert lib.ssd_seq_slice_state_workspace_bytes(1, 512, 4, 64, 128, 3, 1) == bad   # G
+    assert lib.ssd_seq_slice_state_workspace_bytes(1, 512, 4, 64, 128, 1, 7) == bad   # dtype
+
+    def call(x=addr(1), dt=addr(2), A=addr(3), B=addr(4), s=addr(5), a=addr(6), ws=addr(7),
+             wsb=need, L=512, P=64, N=128, G=1, io=1, b=1):
+        return lib.ssd_seq_slice_state(x, dt, A, B, s, a, b, L, 4, P, N, G, io, ws, wsb, None)
+    assert call(b=-1) == DIM
+    assert call(io=5) == UNSUP
+    assert call(G=3) == GROUPS
+    assert call(P=48) == UNSUP
+    assert call(N=272) == UNSUP
+    assert call(b=0, x=None, dt=None, A=None, B=None, s=None, a=None, ws=None) == OK
+    assert call(x=None) == NULL
+    assert call(s=None) == NULL
+    assert call(B=addr(4, 8)) == ALIGN
+    assert call(s=addr(5, 4)) == ALIGN
+    assert call(ws=addr(7, 8)) == ALIGN
+    assert call(ws=None) == WS
+    assert call(wsb=need - 1) == WS
+    assert call(s=addr(4)) == ALIAS                  # state on B
+    assert call(a=addr(2)) == ALIAS                  # alpha on dt
+    assert call(ws=addr(1)) == ALIAS                 # workspace on x
+    assert call(a=addr(5)) == ALIAS                  # alpha on state

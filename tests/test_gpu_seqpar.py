@@ -1,16 +1,19 @@
-"""GPU parity of the sequence-parallel pieces (ssd_seq_total_decay, ssd_seq_combine,
-ssd_seq_apply_state) against the fp64 oracles (MI355X only).
+"""GPU parity of the sequence-parallel pieces (ssd_seq_slice_state, ssd_seq_total_decay,
+ssd_seq_combine, ssd_seq_apply_state) against the fp64 oracles (MI355X only).
 
-The slices of one sequence are scanned from zero by ssd_chunk_scan_fwd, their pairs
-(total decay, final state) combined into entering states, and every slice corrected:
-the result must equal the scan oracle of the whole sequence.  On one GPU the slices
-stand in for the devices of the sequence-parallel layout; the exchange between
-devices is not part of the library."""
+Both orders of work are run over the slices of one sequence.  Outputs first: every
+slice is scanned from zero by ssd_chunk_scan_fwd, the pairs (total decay, final
+state) are combined into entering states, and every slice is corrected.  States
+first: ssd_seq_slice_state gives every slice's pair, the pairs are combined, and every
+slice is scanned from its entering state.  Either way the result must equal the scan
+oracle of the whole sequence.  On one GPU the slices stand in for the devices of the
+sequence-parallel layout; the exchange between devices is not part of the library."""
 import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import TOL, oracle_scan, slice_err, to_f64
+import oracle
+from gpu_helpers import TOL, oracle_scan, scan_errors_all_units, slice_err, to_f64
 from oracle import cp
 from selective_state_space_ssd_amd import binding as bd
 from selective_state_space_ssd_amd import inputs
@@ -18,8 +21,37 @@ from selective_state_space_ssd_amd import inputs
 pytestmark = pytest.mark.gpu
 
 
-def _pipeline(inp, cuts):
+def _pipeline_states_first(inp, cuts):
+    """Slice states, combine, then a scan of every slice from its entering state;
+    returns (y, final_state)."""
+    d = inp.dims
+    dev = bd.to_device
+    x, dt, A, B, C, D = (dev(getattr(inp, n)) for n in ("x", "dt", "A", "B", "C", "D"))
+    init = dev(inp.init_state)
+    n = len(cuts) - 1
+    b, H, P, N = d["b"], d["H"], d["P"], d["N"]
+    S = torch.empty((n, b, H, P, N), dtype=torch.float32, device="cuda")
+    alpha = torch.empty((n, b, H), dtype=torch.float32, device="cuda")
+    parts = []
+    for j in range(n):
+        sl = slice(cuts[j], cuts[j + 1])
+        xs, dts, Bs, Cs = (t[:, sl].contiguous() for t in (x, dt, B, C))
+        S[j], alpha[j] = bd.seq_slice_state(xs, dts, A, Bs)
+        parts.append((xs, dts, Bs, Cs))
+    h_in = torch.empty_like(S)
+    bd.ssd_seq_combine(alpha, S, init, h_in)
+    ys, final = [], None
+    for j, (xs, dts, Bs, Cs) in enumerate(parts):
+        y_j, final = bd.chunk_scan_fwd(xs, dts, A, Bs, Cs, D, d["Q"], init_state=h_in[j])
+        ys.append(y_j)
+    torch.cuda.synchronize()
+    return torch.cat(ys, dim=1), final
+
+
+def _pipeline(inp, cuts, flow="outputs_first"):
     """Run the pieces over the slices [cuts[j], cuts[j+1]); returns (y, final_state)."""
+    if flow == "states_first":
+        return _pipeline_states_first(inp, cuts)
     d = inp.dims
     dev = bd.to_device
     x, dt, A, B, C, D = (dev(getattr(inp, n)) for n in ("x", "dt", "A", "B", "C", "D"))
@@ -59,12 +91,16 @@ SMALL = [
 ]
 
 
+FLOWS = ["outputs_first", "states_first"]
+
+
+@pytest.mark.parametrize("flow", FLOWS)
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "b{}L{}H{}P{}N{}G{}{}{}n{}".format(
     *c[:7], "init" if c[7] else "", len(c[8]) - 1))
-def test_slices_reproduce_whole_sequence(case):
+def test_slices_reproduce_whole_sequence(case, flow):
     b, L, H, P, N, G, io, init, cuts = case
     inp = inputs.make_scan_inputs(b, L, H, P, N, G, 64, io=io, init=init, seed=L + P)
-    y, fs = _pipeline(inp, cuts)
+    y, fs = _pipeline(inp, cuts, flow)
     yo, fo = oracle_scan(inp)
     ey, ef = slice_err(to_f64(y), yo, (1, 3)), slice_err(to_f64(fs), fo, (2, 3))
     print(f"  y err {ey:.2e}  final err {ef:.2e}", flush=True)
@@ -97,16 +133,48 @@ def test_pieces_against_their_oracles():
     assert slice_err(to_f64(f), f_o, (2, 3)) <= TOL["f32"]
 
 
-def test_long_context_layer_in_eight_slices_sampled_heads():
+# The slice state on its own.  bf16 with P = 64 and N in {64, 128, 256} takes the
+# dedicated kernel (runs of 128-token segments; about 512 workgroups, so many heads
+# make runs of several segments); the other shapes take the chunk-state kernel (fp32
+# at P = 128, N = 256 with the shortest chunk).  Ragged last segments, several groups.
+SLICE = [
+    # b,  L,   H,  P,   N,  G,  io
+    (2, 600, 4, 64, 128, 2, "bf16"),     # 5 runs of one segment per head
+    (4, 1000, 64, 64, 128, 4, "bf16"),   # 2 runs of 4 segments
+    (2, 700, 64, 64, 64, 4, "bf16"),     # N = 64: 3 runs of 2 segments
+    (1, 600, 256, 64, 256, 2, "bf16"),   # N = 256: runs of 3 and 2 segments
+    (1, 300, 2, 16, 16, 1, "f32"),
+    (2, 129, 4, 32, 48, 2, "f32"),
+    (1, 520, 2, 128, 256, 1, "bf16"),
+    (1, 200, 2, 128, 256, 2, "f32"),
+    (1, 1, 2, 64, 64, 1, "bf16"),       # one token
+    (1, 0, 2, 64, 64, 1, "bf16"),       # empty slice: zero state, decay 1
+]
+
+
+@pytest.mark.parametrize("b,L,H,P,N,G,io", SLICE)
+def test_slice_state_against_oracle(b, L, H, P, N, G, io):
+    inp = inputs.make_scan_inputs(b, L, H, P, N, G, 64, io=io, init=False, seed=7 * L + N)
+    dev = bd.to_device
+    state, alpha = bd.seq_slice_state(dev(inp.x), dev(inp.dt), dev(inp.A), dev(inp.B))
+    torch.cuda.synchronize()
+    f = lambda a: a.f64()
+    _, fo = oracle.scan_f64(f(inp.x), f(inp.dt), f(inp.A), f(inp.B), f(inp.C), f(inp.D), None)
+    ao = cp.total_decay_f64(f(inp.dt), f(inp.A))
+    es = slice_err(to_f64(state), fo, (2, 3)) if L > 0 else float(np.abs(to_f64(state)).max())
+    ea = float(np.abs(to_f64(alpha) - ao).max() / max(np.abs(ao).max(), 1e-30))
+    print(f"  state err {es:.2e}  alpha err {ea:.2e}", flush=True)
+    assert es <= TOL[io] and ea <= 1e-5
+
+
+@pytest.mark.parametrize("flow", FLOWS)
+def test_long_context_layer_in_eight_slices_every_head(flow):
     """The L=16384 layer (b=1, H=80, P=64, N=128, bf16, initial state) as 8 slices of
-    2048 tokens, one GPU's share each; checked on sampled heads."""
+    2048 tokens, one GPU's share each; every head compared with the oracle of the
+    whole sequence."""
     inp = inputs.make_workload("mamba2_2p7b_L16k")
-    y, fs = _pipeline(inp, list(range(0, 16385, 2048)))
-    yg, fg = to_f64(y), to_f64(fs)
-    ey = ef = 0.0
-    for u in (0, 41, 79):
-        yo, fo = oracle_scan(inp, bh_range=(u, u + 1))
-        ey = max(ey, slice_err(yg[0, :, u], yo[0, :, u], (0, 1)))
-        ef = max(ef, slice_err(fg[0, u], fo[0, u], (0, 1)))
-    print(f"  y err {ey:.2e}  final err {ef:.2e}", flush=True)
+    y, fs = _pipeline(inp, list(range(0, 16385, 2048)), flow)
+    ey, ef, n = scan_errors_all_units(inp, y, fs)
+    print(f"  {n} units: y err {ey:.2e}  final err {ef:.2e}", flush=True)
+    assert n == inp.dims["b"] * inp.dims["H"]
     assert ey <= TOL["bf16"] and ef <= TOL["bf16"]
