@@ -46,10 +46,13 @@ Printed: one JSON line with the contract fields plus
   verify_ring   one round of the multi-round verify on a ring of 8 states (K=4, every
                 draft accepted, fused softplus step), GB/s
   sequence_parallel
-                one device's share of the L=16k layer split into 8 slices: the slice's
-                scan from zero, its total decay, the combine of 8 pairs and the
-                correction by the entering state (the exchange between devices is not
-                measured: this build runs on one GPU)
+                one device's share of the L=16k layer split into 8 slices, in both
+                orders of work: states first (the slice's (decay, state) pair without
+                outputs, the combine of 8 pairs, the slice's scan from its entering
+                state) and outputs first (the slice's scan from zero, its total decay,
+                the combine, the correction by the entering state); share_us is the
+                faster (the exchange between devices is not measured: this build runs
+                on one GPU)
   backward      ssd_chunk_scan_bwd (all seven gradients, states recomputed) on the
                 L=2048 layer with upstream gradients for y and the final state:
                 tokens/s and algorithmic bytes / call time against 8 TB/s
