@@ -185,7 +185,7 @@ ssd_status_t ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, 
  * ends.  The call allocates and frees nothing and calls no allocating routine.
  * - A problem whose workspace (ssd_chunk_scan_workspace_bytes) exceeds that size is
  *   refused with SSD_ERR_WORKSPACE before anything is enqueued.  For scale: the
- *   2.7B-shaped layer (b 4, L 2048, H 80, P 64, N 128, bf16) needs 10.5 MB, and
+ *   2.7B-shaped layer (b 4, L 2048, H 80, P 64, N 128, bf16) needs 21 MB, and
  *   b 8, L 4096, H 32, P 64, N 256, Q 128 (bf16) needs 34 MB.
  * - The first call on a device prepares that device's buffer: it looks up the buffer's
  *   address and enqueues a fill kernel on hip_stream ahead of the scan.  That first
