@@ -28,7 +28,7 @@ def _both(inp):
 
 def test_noalloc_matches_workspace_entry_on_calls_in_a_row():
     cases = [
-        # the benchmark layer (10.5 MB of workspace), compared on every unit
+        # the benchmark layer (21 MB of workspace), compared on every unit
         ("full", inputs.make_workload("mamba2_2p7b_L2k")),
         # a smaller bf16 problem on the single-pass kernel, ragged, with an init state
         ("small", inputs.make_scan_inputs(2, 1100, 8, 64, 128, 2, 256, io="bf16", init=True,
