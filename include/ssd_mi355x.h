@@ -43,6 +43,11 @@
  *   check returns its status and enqueues nothing.  SSD_ERR_HIP reports a launch
  *   error returned by the HIP runtime.  No C++ exception crosses the ABI.
  * - NaN or Inf in the inputs propagate to the outputs; they are not checked.
+ * - The recurrence is taken to be a decay: dt >= 0 and A <= 0, so that every factor
+ *   exp(dt * A) is at most 1 (what the discretisation produces: A_h = -exp(.) and a
+ *   softplus step).  Kernels clamp decay exponents at 0 where a masked product could
+ *   otherwise overflow; inputs outside this domain give unspecified results and are
+ *   not checked.
  */
 #ifndef SSD_MI355X_H
 #define SSD_MI355X_H
