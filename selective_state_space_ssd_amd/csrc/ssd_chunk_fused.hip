@@ -840,7 +840,7 @@ void k_ssd_fused(
 // its HB heads one after another, so a larger HB amortises the item prologue (ticket,
 // B and C loads, score tiles) but makes fewer, longer work items.  With `slots`
 // workgroups resident at a time, the estimate in head-times is
-//   ceil(items / slots) * (prologue + HB)  +  (chunks of one head in flight - 1) * link,
+//   max(1, items / slots) * (prologue + HB)  +  (chunks of one head in flight - 1) * link,
 // the second term being the fill of the chunk-to-chunk hand-off chain.  With one
 // workgroup per CU nothing covers the prologue: timestamps put it at about 1.15 head
 // times and a chain link at about 0.2.  With two per CU the other workgroup covers part
@@ -857,7 +857,9 @@ int heads_per_workgroup(int b, int H, int G, int nc, int slots, int wg_per_cu) {
         if (hpg % hb) continue;
         const double chains = double(b) * (H / hb);
         const double items = chains * nc;
-        const double rounds = std::ceil(items / slots);
+        // items start as workgroups finish, not in lockstep rounds: a partial last
+        // round costs its share of a round
+        const double rounds = std::max(1.0, items / slots);
         const double inflight = std::min(double(nc), std::ceil(slots / chains));
         const double t = rounds * (prologue + hb) + (inflight - 1.0) * link;
         if (hb == 1 || t < best_t - 1e-9) {
