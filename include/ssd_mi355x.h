@@ -92,11 +92,11 @@ size_t ssd_chunk_scan_workspace_bytes(int b, int L, int H, int P, int N, int G, 
  *
  * Step 3 of the chunked scan (the state passed from chunk to chunk, Mamba-2 article,
  * «SSD 算法：分块和形态传递») runs as a hand-off between workgroups through the
- * workspace: a 256-byte header (a work-item ticket and call number, an error word, a
- * preparation marker) and one ready flag per (batch, head, chunk).  This call zeroes
- * the workspace and writes the marker.  Each ssd_chunk_scan_fwd call takes a new
- * call number, tags the flags it raises with it, and leaves the ticket at zero when it
- * completes; flags of earlier calls therefore never read as ready, and one prepared
+ * workspace: a 256-byte header (a work queue per XCD with its call number, an error
+ * word, a preparation marker) and one ready flag per (batch, head, chunk).  This call
+ * zeroes the workspace and writes the marker.  Each ssd_chunk_scan_fwd call takes a
+ * new call number, tags the flags it raises with it, and leaves the queues at zero
+ * when it completes; flags of earlier calls therefore never read as ready, and one prepared
  * workspace serves any number of later calls of any shape and I/O type that fits
  * (the fp32 / other-P path keeps its buffers after the header).  Calls that share a
  * workspace must run one at a time (same stream, or ordered by events): calls that
@@ -118,9 +118,10 @@ ssd_status_t ssd_chunk_scan_workspace_init(void *workspace, size_t workspace_byt
  *
  * The word is 0 while no chunk of any ssd_chunk_scan_fwd call on this workspace (since
  * it was prepared or last cleared) gave up waiting for the state of the chunk before
- * it; 1 once one did (its state and outputs were written as NaN).  A healthy device
- * never sets it: the wait only ends this way if the device breaks its forward-progress
- * guarantee.
+ * it; 1 once one did (its state and outputs were written as NaN); 2 if more
+ * workgroups of a call ran on one XCD than the launch placed there (the launch relies
+ * on the hardware placing workgroup i on XCD i mod the XCD count; outputs of that
+ * call may be incomplete).  A healthy device never sets it.
  *   workspace, workspace_bytes  the workspace (device, 16-byte aligned, at least the
  *                               256-byte header)
  *   err_out   device int32, written

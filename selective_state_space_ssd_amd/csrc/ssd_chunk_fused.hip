@@ -21,14 +21,17 @@
 //   * step 3 (state passing) is a chain between workgroups: the workgroup of
 //     chunk c waits until chunk c-1 of the same head has published its state,
 //     publishes H_c = exp(Acum_end) H_{c-1} + S_c, and only then needs H_{c-1} for
-//     its own outputs.  The hand-off uses device-coherent (agent-scope, relaxed)
-//     loads and stores for both the state and its ready flag, and the writer waits
-//     for its state stores to complete before it raises the flag; no cache-wide
-//     fence is needed.  Work items are taken from an atomic ticket in chunk-major
-//     order, so every item a workgroup waits for is held by a workgroup that is
-//     already running: the chain cannot deadlock whatever the dispatch order.  The
-//     wait is bounded; on time-out the state is poisoned with NaN and an error word
-//     in the workspace is set, so a failure is loud and never a hang.
+//     its own outputs.  Every chunk of a chain (batch row, block of heads) runs on
+//     one XCD: work items come from one queue per XCD, a workgroup takes its ticket
+//     from the queue of the XCD it runs on (read from the hardware), and a queue
+//     holds a run of chains, chunk-major.  The hand-off then stays in that XCD's L2:
+//     the state and its ready flag are stored write-back (a store completes at the
+//     L2) and read with coherent loads, which the L2 serves; the writer waits for
+//     its state stores to complete before it raises the flag, and no cache-wide
+//     fence is needed.  Within a queue every item a workgroup waits for has an
+//     earlier ticket, held by a workgroup that is already running: the chain cannot
+//     deadlock.  The wait is bounded; on time-out the state is poisoned with NaN and
+//     an error word in the workspace is set, so a failure is loud and never a hang.
 //
 // Step 1, 2 and 4 contractions use v_mfma_f32_16x16x32_bf16 with fp32 accumulation;
 // the in-chunk decay cumsum is a wavefront scan.
@@ -189,15 +192,27 @@ __device__ __forceinline__ void stage_B(const bf16_bits *__restrict__ src, size_
     }
 }
 
-// The chunk-to-chunk state hand-off is read by another workgroup, possibly on another
-// XCD: its loads and stores carry the device-scope cache policy (sc1), the same bits
-// an agent-scope relaxed atomic access gets.  In the ring the state is kept in the
-// accumulator layout: 16x16 tile (pt, nt) at float offset (pt * N/16 + nt) * 256, lane
-// l's four values (rows 4(l/16) + i, column l % 16) at l * 4 + i, so that each lane
-// moves 16 bytes per access.
-constexpr int kBufDevice = 16;   // cache-policy bits of a buffer access: sc1
+// The chunk-to-chunk state hand-off is read by another workgroup on the same XCD: it
+// is stored write-back (default policy; the store completes at the XCD's L2) and read
+// with the coherent policy (sc1), which the L2 serves for a line this XCD wrote (a
+// load with sc0 alone can be served stale by the CU's own cache; measured).  In the
+// ring the state is kept in the accumulator layout: 16x16 tile (pt, nt) at float
+// offset (pt * N/16 + nt) * 256, lane l's four values (rows 4(l/16) + i, column
+// l % 16) at l * 4 + i, so that each lane moves 16 bytes per access.
+constexpr int kBufL2 = 16;   // cache-policy bits of a buffer load: sc1 (coherent; served by
+                             // the XCD's L2 when the line was written on this XCD)
 // Wait until this wave's outstanding memory operations have completed.
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// A 32-bit word read coherently (from the XCD's L2 when this XCD wrote it; the asm
+// statement keeps a polling read inside its loop), and a word written to the XCD's L2
+// (write-back: the store completes at the L2, not at memory).
+__device__ __forceinline__ uint32_t ld_l2(const uint32_t *p) {
+    asm volatile("" ::: "memory");
+    return __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(p, 4u), 0, 0, kBufL2);
+}
+__device__ __forceinline__ void st_l2(uint32_t *p, uint32_t v) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, buffer_rsrc(p, 4u), 0, 0, 0);
+}
 
 template <int Q, int N>
 __global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(2 * Fz<Q, N>::kWgPerCu)))
@@ -206,7 +221,7 @@ void k_ssd_fused(
     const bf16_bits *__restrict__ B, const bf16_bits *__restrict__ C,
     const float *__restrict__ D, const float *__restrict__ init_state,
     bf16_bits *__restrict__ y, float *__restrict__ final_state, float *hbuf, uint32_t *flags,
-    uint32_t *hdr, int L, int H, int G, int HB, int nchains, int nc) {
+    uint32_t *hdr, int L, int H, int G, int HB, int nchains, int nc, int nq) {
     using F = Fz<Q, N>;
     constexpr int P = F::P;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -227,23 +242,47 @@ void k_ssd_fused(
     const int r16 = lane & 15, g4 = lane >> 4;
 
     if (tid == 0) {
-        // A prepared workspace carries the magic word.  The first 8 bytes of the
-        // header hold the work-item count (low half) and the call number ("epoch",
-        // high half); one 64-bit atomic add gives a workgroup both its ticket and
-        // the epoch, and the workgroup that takes the last ticket wraps the count
-        // back to 0 and advances the epoch for the next call.  Ready flags carry
-        // epoch + 1, so flags left by earlier calls (or other shapes' data in the
-        // flag region) never read as ready.  Without a prepared workspace every item
-        // runs at its own index and never waits (its handed-over states are NaN).
+        // A prepared workspace carries the magic word.  Work items are handed out by one
+        // queue per XCD: each queue takes a run of consecutive chains (batch row, block
+        // of heads), so that chains sharing a batch row's B and C share an L2 where they
+        // can, and a queue's items are its chains' chunks in chunk-major order,
+        // so every chunk of a chain runs on one XCD and the chain's hand-off stays in
+        // that XCD's L2.  A workgroup reads the XCD it runs on from the hardware and
+        // takes a ticket from that XCD's queue.  The hardware places workgroup i on XCD
+        // i mod nq, and the launch gives every XCD W = gridDim / nq workgroups, as many
+        // as the longest queue has items.  A queue is one 64-bit word: the tickets taken
+        // (low half) and the call number ("epoch", high half), so one atomic add gives
+        // a workgroup both; the workgroup that takes a queue's W-th ticket wraps the
+        // count back to 0 and advances that queue's epoch.  Every call advances every
+        // queue once, so all queues carry the same call number.  Ready flags carry
+        // epoch + 1, so flags left by earlier calls (or other shapes' data in the flag
+        // region) never read as ready.  A ticket beyond W (more workgroups on an XCD
+        // than the launch placed there) sets the error word.  Without a prepared
+        // workspace every item runs at its own index and never waits (its handed-over
+        // states are NaN).
         const uint32_t magic =
             __hip_atomic_load(&hdr[kWsMagicWord], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint64_t old = atomicAdd(reinterpret_cast<unsigned long long *>(hdr), 1ull);
-        const uint32_t count = uint32_t(old), epoch = uint32_t(old >> 32);
-        const bool prepared = magic == kWsMagic && count < gridDim.x;
-        if (prepared && count == gridDim.x - 1u)
-            atomicAdd(reinterpret_cast<unsigned long long *>(hdr), (1ull << 32) - gridDim.x);
-        const int ticket = prepared ? int(count) : int(blockIdx.x);
-        misc[0] = ticket;
+        const bool prepared = magic == kWsMagic;
+        int it = -1;
+        uint32_t epoch = 0;
+        if (prepared) {
+            uint32_t xcc;
+            asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+            const int x = int(xcc & 15u) % nq;
+            unsigned long long *q = reinterpret_cast<unsigned long long *>(hdr + kWsQueueWord + 2 * x);
+            const uint64_t old = atomicAdd(q, 1ull);
+            const uint32_t t = uint32_t(old), W = gridDim.x / unsigned(nq);
+            epoch = uint32_t(old >> 32);
+            if (t == W - 1u) atomicAdd(q, (1ull << 32) - W);
+            if (t >= W)
+                __hip_atomic_store(&hdr[kWsErrorWord], 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int per = (nchains + nq - 1) / nq;            // chains per queue
+            const int nchx = max(0, min(per, nchains - x * per));   // the last may hold fewer
+            if (t < uint32_t(nchx * nc)) it = int(t) / nchx * nchains + x * per + int(t) % nchx;
+        } else if (blockIdx.x < unsigned(nchains * nc)) {
+            it = int(blockIdx.x);
+        }
+        misc[0] = it;
         misc[2] = prepared;
         misc[3] = int(epoch + 1u);
     }
@@ -251,6 +290,7 @@ void k_ssd_fused(
     const int item = __builtin_amdgcn_readfirstlane(misc[0]);   // uniform: keep it scalar
     const bool ws_ok = __builtin_amdgcn_readfirstlane(misc[2]) != 0;
     const uint32_t ready = uint32_t(__builtin_amdgcn_readfirstlane(misc[3]));   // flag value
+    if (item < 0) return;   // more workgroups on this XCD than its queue has items
     const int c = item / nchains, chain = item % nchains;
     const int hblocks = H / HB;
     const int bi = chain / hblocks, h0 = (chain % hblocks) * HB;
@@ -442,7 +482,7 @@ void k_ssd_fused(
             uint32_t *flag = flags + bh * nc + (c - 1);
             uint32_t it = 0;
             int ok = ws_ok;
-            while (ok && __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != ready) {
+            while (ok && ld_l2(flag) != ready) {
                 __builtin_amdgcn_s_sleep(2);
                 if (++it > kSpinLimit) {
                     ok = 0;
@@ -499,7 +539,7 @@ void k_ssd_fused(
                     for (int j = 0; j < F::NTW; ++j) {
                         const int tile = (pt_base + PT_STEP * k) * F::NTN + nt_base + NT_STEP * j;
                         const f32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
-                            ring, (tile * 64 + lane) * 16, 0, kBufDevice);
+                            ring, (tile * 64 + lane) * 16, 0, kBufL2);
 #pragma unroll
                         for (int i = 0; i < 4; ++i) hp[k][j][i] = v[i];
                     }
@@ -599,8 +639,7 @@ void k_ssd_fused(
                     for (int j = 0; j < F::NTW; ++j) {
                         const int tile = (pt_base + PT_STEP * k) * F::NTN + nt_base + NT_STEP * j;
                         const f32x4 v = {hp[k][j][0], hp[k][j][1], hp[k][j][2], hp[k][j][3]};
-                        __builtin_amdgcn_raw_buffer_store_b128(v, ring, (tile * 64 + lane) * 16, 0,
-                                                               kBufDevice);
+                        __builtin_amdgcn_raw_buffer_store_b128(v, ring, (tile * 64 + lane) * 16, 0, 0);
                     }
             } else if (final_state) {
                 // the final state (last chunk only), offsets as for the initial state
@@ -619,8 +658,7 @@ void k_ssd_fused(
         }
         if (!last) wait_vm();   // this wave's state stores are complete and visible
         __syncthreads();
-        if (!last && tid == 0)
-            __hip_atomic_store(flags + bh * nc + c, ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!last && tid == 0) st_l2(flags + bh * nc + c, ready);
         if constexpr (kPrefetchX) {
             // loads for the heads ahead, issued after the hand-off so that its wait for
             // the state stores does not wait for them too: x of the next head, in
@@ -838,29 +876,31 @@ void k_ssd_fused(
 
 // Heads per workgroup.  A workgroup computes the chunk's score tiles once and then runs
 // its HB heads one after another, so a larger HB amortises the item prologue (ticket,
-// B and C loads, score tiles) but makes fewer, longer work items.  With `slots`
-// workgroups resident at a time, the estimate in head-times is
-//   max(1, items / slots) * (prologue + HB)  +  (chunks of one head in flight - 1) * link,
-// the second term being the fill of the chunk-to-chunk hand-off chain.  With one
-// workgroup per CU nothing covers the prologue: timestamps put it at about 1.15 head
-// times and a chain link at about 0.2.  With two per CU the other workgroup covers part
-// of the prologue, and 1.0 and 0.3 fit the measurements better.  HB ranges over the
+// B and C loads, score tiles) but makes fewer, longer work items.  Items run from nq
+// queues (one per XCD), each with slots / nq resident workgroups and at most
+// ceil(chains / nq) chains; the estimate in head-times is
+//   ceil(items of a queue / its slots) * (prologue + HB)
+//     + (chunks of one chain in flight - 1) * link,
+// the second term being the fill of the chunk-to-chunk hand-off chain.  A partial last
+// round costs a whole one (measured: at L2k, 8 heads per workgroup leave 40 items for
+// the 32 CUs of an XCD and take 118 us against 89 us with 10).  With one workgroup per
+// CU nothing covers the prologue: timestamps put it at about 1.15 head times and a
+// chain link at about 0.2.  With two per CU the other workgroup covers part of the
+// prologue and of the link, and 1.0 and 0.1 fit the measurements.  HB ranges over the
 // divisors of H / G up to 16 (a block never straddles two groups); ties go to the
 // smaller HB.
-int heads_per_workgroup(int b, int H, int G, int nc, int slots, int wg_per_cu) {
+int heads_per_workgroup(int b, int H, int G, int nc, int slots, int wg_per_cu, int nq) {
     const double prologue = wg_per_cu == 1 ? 1.15 : 1.0;
-    const double link = wg_per_cu == 1 ? 0.2 : 0.3;
+    const double link = wg_per_cu == 1 ? 0.2 : 0.1;
     const int hpg = H / G;
+    const double qslots = std::max(1.0, double(slots) / nq);
     int best = 1;
     double best_t = 0.0;
     for (int hb = 1; hb <= 16 && hb <= hpg; ++hb) {
         if (hpg % hb) continue;
-        const double chains = double(b) * (H / hb);
-        const double items = chains * nc;
-        // items start as workgroups finish, not in lockstep rounds: a partial last
-        // round costs its share of a round
-        const double rounds = std::max(1.0, items / slots);
-        const double inflight = std::min(double(nc), std::ceil(slots / chains));
+        const double qchains = std::ceil(double(b) * (H / hb) / nq);
+        const double rounds = std::ceil(qchains * nc / qslots);
+        const double inflight = std::min(double(nc), std::ceil(qslots / qchains));
         const double t = rounds * (prologue + hb) + (inflight - 1.0) * link;
         if (hb == 1 || t < best_t - 1e-9) {
             best = hb;
@@ -889,6 +929,26 @@ hipError_t device_cu_count(int dev, int *cus) {
     return e;
 }
 
+// The number of XCDs of the device (the work queues of the single-pass kernel): 1, 2, 4
+// or 8, as the runtime reports it; anything else counts as 1.
+std::atomic<int> g_xcc_count[kMaxDevices];
+
+hipError_t device_xcc_count(int dev, int *nq) {
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int c = g_xcc_count[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *nq = c;
+            return hipSuccess;
+        }
+    }
+    int n = 1;
+    const hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeNumberOfXccs, dev);
+    if (e != hipSuccess) return e;
+    *nq = (n == 1 || n == 2 || n == 4 || n == 8) ? n : 1;
+    if (dev >= 0 && dev < kMaxDevices) g_xcc_count[dev].store(*nq, std::memory_order_relaxed);
+    return hipSuccess;
+}
+
 template <int Q, int N>
 hipError_t launch_fused_qn(const ChunkScanArgs &a, const FusedPlan &fp, hipStream_t stream) {
     using F = Fz<Q, N>;
@@ -909,15 +969,19 @@ hipError_t launch_fused_qn(const ChunkScanArgs &a, const FusedPlan &fp, hipStrea
     }
     e = device_cu_count(dev, &cus);
     if (e != hipSuccess) return e;
+    int nq = 1;
+    e = device_xcc_count(dev, &nq);
+    if (e != hipSuccess) return e;
     const int HB = heads_per_workgroup(a.b, a.H, a.G, fp.nc, std::max(1, cus) * F::kWgPerCu,
-                                       F::kWgPerCu);
+                                       F::kWgPerCu, nq);
     const int nchains = a.b * (a.H / HB);
-    const unsigned items = unsigned(nchains) * unsigned(fp.nc);
+    // every XCD gets as many workgroups as the longest queue has items
+    const unsigned items = unsigned(nq) * unsigned((nchains + nq - 1) / nq) * unsigned(fp.nc);
     hipLaunchKernelGGL((k_ssd_fused<Q, N>), dim3(items), dim3(kFT), F::kLds, stream,
                        static_cast<const bf16_bits *>(a.x), a.dt, a.A,
                        static_cast<const bf16_bits *>(a.B), static_cast<const bf16_bits *>(a.C),
                        a.D, a.init_state, static_cast<bf16_bits *>(a.y), a.final_state, hbuf,
-                       flags, hdr, a.L, a.H, a.G, HB, nchains, fp.nc);
+                       flags, hdr, a.L, a.H, a.G, HB, nchains, fp.nc, nq);
     return hipGetLastError();
 }
 

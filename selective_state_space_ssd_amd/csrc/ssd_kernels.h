@@ -93,21 +93,23 @@ ChunkScanPlan plan_chunk_scan(int b, int L, int H, int P, int N, int G, int Q, b
 
 // Workspace of the single-pass kernel: a 256-byte header, one ready flag per (batch,
 // head, chunk) and a two-slot fp32 state ring per (batch, head) for the chunk-to-chunk
-// hand-off.  Header words: 0 = work-item count and 1 = call number (one 64-bit
-// word), 2 = time-out error word, 32 = magic word (its own cache line).
-// ssd_chunk_scan_workspace_init zeroes it and writes the magic word; every completed
-// call leaves the count at zero and advances the call number, and its ready flags
-// hold that call's tag (call number + 1), which no later call waits for.  The
-// three-kernel path keeps its buffers after the header, so a prepared workspace stays
-// prepared whichever path a call takes.
+// hand-off.  Header words: 2 = error word (1: a hand-off timed out; 2: more workgroups
+// ran on an XCD than the launch placed there), 32 = magic word, and at word 48 + 2 x
+// the 64-bit queue of XCD x (x < 8): tickets taken (low half) and call number (high
+// half).  ssd_chunk_scan_workspace_init zeroes it and writes the magic word; every
+// completed call leaves each queue's count at zero and advances its call number (all
+// queues together), and its ready flags hold that call's tag (call number + 1), which
+// no later call waits for.  The three-kernel path keeps its buffers after the header,
+// so a prepared workspace stays prepared whichever path a call takes.
 constexpr uint32_t kWsMagic = 0x55d5ca11u;
 constexpr size_t kWsHeaderBytes = 256;   // reserved by both chunk-scan layouts
 constexpr int kWsErrorWord = 2;
 constexpr int kWsMagicWord = 32;
+constexpr int kWsQueueWord = 48;  // XCD x's queue: 64-bit word at word 48 + 2 x, x < 8
 struct FusedPlan {
     int nc = 0;
     int HB = 1;                 // heads per workgroup (the launch picks it per device)
-    size_t off_hdr = 0;         // uint32 [64]: ticket count, call number, error, magic
+    size_t off_hdr = 0;         // uint32 [64]: error word, magic, per-XCD queues
     size_t off_flags = 0;       // uint32 [b, H, nc]
     size_t off_hbuf = 0;        // fp32   [b, H, 2, P, N]
     size_t total = 0;
