@@ -30,6 +30,8 @@
 //             (+ e^{cum_end} <Gh, Hin> + sum_s w_s v_s at the last token)
 //   d a_t = sum_{tau >= t} d cum_tau;  d dt_t += A d a_t;  dA = sum dt_t d a_t;
 //   dD = sum x . dy.
+#include <cmath>
+
 #include "ssd_device.h"
 #include "ssd_kernels.h"
 #include "ssd_stage.h"
@@ -40,6 +42,7 @@ namespace {
 
 constexpr int QB = 64;     // tokens per backward chunk
 constexpr int kPad = 4;    // fp32 LDS row padding (floats)
+constexpr double kBwdCus = 256.0;   // CUs of gfx950, for the heads-per-workgroup plan
 
 // Sum of one value per thread over the 256-thread block, in a fixed order; every
 // thread returns the total.  `red` is LDS scratch of 4 floats.  Starts with a barrier.
@@ -451,10 +454,24 @@ ChunkScanBwdPlan plan_chunk_scan_bwd(int b, int L, int H, int P, int N, int G, b
     const size_t units = size_t(b) * H * pl.nc;
     pl.bf16_path = bf16 && P == 64 && chunk_bwd_bf16_lds(N) != 0;
     if (pl.bf16_path) {
-        // heads per workgroup: the largest divisor of the group size up to 8
+        // heads per workgroup (a divisor of the group size): the chunk kernel runs one
+        // workgroup per CU, and a workgroup costs about hb + 0.75 head times (staging B
+        // and C and the C B^T tiles, shared by its heads, take 0.75), so the launch
+        // takes ceil(workgroups / CUs) (hb + 0.75) head times; the CU count is that of
+        // gfx950 (256), so that the plan depends on the shape only.  Ties go to the
+        // larger block (fewer dB / dC partials).  Measured at the L = 2048 layer (b 4,
+        // H 80): 8 heads 460 us per call, 10: 452, 16: 471, 20: 433, 40: 424.
         const int hpg = H / G;
-        for (int d = 1; d <= 8 && d <= hpg; ++d)
-            if (hpg % d == 0) pl.hb = d;
+        double best = 0.0;
+        for (int d = 1; d <= hpg; ++d) {
+            if (hpg % d != 0) continue;
+            const double wgs = double(pl.nc) * double(H / d) * double(b);
+            const double t = std::ceil(wgs / kBwdCus) * (d + 0.75);
+            if (d == 1 || t <= best) {
+                best = t;
+                pl.hb = d;
+            }
+        }
         pl.nparts = H / pl.hb;
         const size_t st = units * size_t(P) * N * 2;
         const size_t part = size_t(b) * L * pl.nparts * N * 4;

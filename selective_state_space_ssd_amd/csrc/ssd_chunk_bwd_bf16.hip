@@ -17,8 +17,8 @@
 //                  state ever goes to HBM in fp32.  The states are stored in bf16, in
 //                  MFMA accumulator tile order (contiguous stores; the next kernel
 //                  assembles its operands from two 8-byte pieces).
-//   k_bwd_chunk_bf one workgroup of 8 waves per (chunk, block of up to 8 heads of one
-//                  group, batch): C B^T once per block, then per head the score tiles, dx,
+//   k_bwd_chunk_bf one workgroup of 8 waves per (chunk, block of heads of one group,
+//                  batch): C B^T once per block, then per head the score tiles, dx,
 //                  and the head's dB / dC contributions, which stay in registers across
 //                  the block so only one fp32 partial per block reaches HBM.
 //

@@ -242,14 +242,26 @@ def test_bwd_workspace_bytes(lib):
     b, L, H, P, N, G = 4, 2048, 80, 64, 128, 1
     units = b * H * (L // 64)
     # bf16 I/O, P = 64: bf16 entering states and state gradients, fp32 dB / dC
-    # partials per block of 8 heads, two per-chunk scalars
+    # partials per block of heads, two per-chunk scalars.  At this shape the blocks hold
+    # 40 heads: 32 chunks x 2 blocks x 4 rows = 256 workgroups, one per CU of gfx950
     n = bd.ssd_chunk_scan_bwd_workspace_bytes(b, L, H, P, N, G, bd.SSD_DTYPE_BF16)
-    need = 2 * units * P * N * 2 + 2 * b * L * (H // 8) * N * 4 + 2 * units * 4
+    need = 2 * units * P * N * 2 + 2 * b * L * (H // 40) * N * 4 + 2 * units * 4
     assert need <= n < need + 6 * 256
     # fp32 I/O: fp32 states and state gradients, per-head partials, three scalars
     n32 = bd.ssd_chunk_scan_bwd_workspace_bytes(b, L, H, P, N, G, bd.SSD_DTYPE_F32)
     need32 = 2 * units * P * N * 4 + 2 * b * L * H * N * 4 + 3 * units * 4
     assert need32 <= n32 < need32 + 7 * 256
+    # the blocks of heads the plan takes, read back from the size of the dB / dC
+    # partials: the workgroups of a block of d heads cost about d + 0.75 head times and
+    # run ceil(workgroups / 256) rounds; the cheapest divisor of the group size wins
+    for (b2, L2, H2, G2), d in [((2, 300, 4, 2), 1), ((2, 1100, 12, 1), 2),
+                                ((4, 630, 48, 2), 8), ((8, 4096, 32, 4), 8),
+                                ((4, 2048, 80, 1), 40)]:
+        nc2 = -(-L2 // 64)
+        fixed = 2 * (b2 * H2 * nc2) * 64 * 64 * 2 + 2 * (b2 * H2 * nc2) * 4
+        m = bd.ssd_chunk_scan_bwd_workspace_bytes(b2, L2, H2, 64, 64, G2, bd.SSD_DTYPE_BF16)
+        parts = 2 * b2 * L2 * (H2 // d) * 64 * 4
+        assert fixed + parts <= m < fixed + parts + 6 * 256, (b2, L2, H2, G2, d)
     assert bd.ssd_chunk_scan_bwd_workspace_bytes(0, L, H, P, N, G, 1) == 0
     assert bd.ssd_chunk_scan_bwd_workspace_bytes(b, 0, H, P, N, G, 1) == 0
     with pytest.raises(bd.SSDError):

@@ -55,9 +55,10 @@ def _assert(errs, tol):
 # Several 64-token chunks with ragged last ones, initial states, final-state gradients
 # or none, P in {32, 64}, N from 16 to 128, groups of 1, 2, 3, 4 and 12 heads, both
 # dtypes; bf16 with P = 64 and N in {64, 128} takes the bf16 matrix-core path (blocks
-# of up to 8 heads of a group per workgroup; forward state walks over two heads of a
-# group when the group has an even number of heads, one otherwise), the rest the fp32
-# path.
+# of heads of a group per workgroup, sized by the launch's round model: one head at
+# the shortest shapes, 2 and 8 at the two longer ones below; forward state walks over
+# two heads of a group when the group has an even number of heads, one otherwise),
+# the rest the fp32 path.
 SMALL = [
     # b,  L,  H,  P,   N, G,  io,    init, final
     (2, 300, 4, 64, 128, 2, "bf16", True, True),
@@ -67,10 +68,12 @@ SMALL = [
     (1, 63, 4, 64, 48, 4, "f32", True, False),        # one group per head, short
     (1, 1, 2, 32, 16, 1, "f32", True, True),          # one token
     (2, 517, 4, 64, 128, 1, "f32", True, True),
-    (1, 190, 12, 64, 64, 1, "bf16", True, True),      # blocks of 6 heads
+    (1, 190, 12, 64, 64, 1, "bf16", True, True),      # twelve heads in one group
     (2, 129, 2, 64, 128, 2, "bf16", False, False),    # one head per group
     (1, 200, 3, 64, 64, 1, "bf16", True, True),       # odd group: one head per forward walk
     (2, 150, 6, 64, 128, 2, "bf16", True, False),     # odd groups of 3, two groups
+    (2, 1100, 12, 64, 128, 1, "bf16", True, False),   # blocks of 2 heads
+    (4, 630, 48, 64, 64, 2, "bf16", True, True),      # blocks of 8 heads, two groups
 ]
 
 
