@@ -243,10 +243,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chunk(
                 cr += r;
                 cglw += gl * Wt[i];
             }
-            cr += __shfl_xor(cr, 16, 64);
-            cr += __shfl_xor(cr, 32, 64);
-            cglw += __shfl_xor(cglw, 16, 64);
-            cglw += __shfl_xor(cglw, 32, 64);
+            cr = group4_sum(cr);
+            cglw = group4_sum(cglw);
             if (g4 == 0) {
                 colR[w * QB + s] = cr;
                 colGLW[w * QB + s] = cglw;

@@ -162,7 +162,7 @@ __device__ __forceinline__ void chain_walk(
 #pragma unroll
             for (int k = 0; k < WH; ++k) {
                 const float cs = wave_inclusive_scan(f.d[k] * Ah[k] * kLog2e);
-                const float aend = __shfl(cs, qlen - 1, 64);
+                const float aend = lane_value(cs, qlen - 1);
                 const float wv = lane < qlen ? (DIR == 0 ? exp2f(aend - cs) * f.d[k] : exp2f(cs)) : 0.f;
                 if (tid == 0) al_sh[buf * FH + k] = exp2f(aend);
                 const float wa = __shfl(wv, 2 * tpu, 64), wb = __shfl(wv, 2 * tpu + 1, 64);
@@ -500,7 +500,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_bwd_chunk_bf(
         const float dreg = dnext;
         const float Ah = A[h];
         const float cs = wave_inclusive_scan(dreg * Ah * kLog2e);
-        const float aend = __shfl(cs, qlen - 1, 64);
+        const float aend = lane_value(cs, qlen - 1);
         if (w == 0) {   // wave 0 reads the previous head's scalars until here
             const bool valid = lane < qlen;
             acum[lane] = valid ? cs : 0.f;
@@ -712,7 +712,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_bwd_chunk_bf(
             float dc = valid ? rr - cr + eac[t] * y - wt * v : 0.f;
             if (t == qlen - 1) dc += dend;
             const float inc = wave_inclusive_scan(dc);
-            const float da = __shfl(inc, 63, 64) - inc + dc;     // sum over tau >= t
+            const float da = lane_value(inc, 63) - inc + dc;     // sum over tau >= t
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(glw + exp2f(aend - cs) * v + Ah * da),
                                                   ddtres, (t * H + h) * 4, 0, 0);
             const float dA = wave_sum(valid ? dreg * da : 0.f);

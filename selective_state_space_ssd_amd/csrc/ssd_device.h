@@ -125,19 +125,38 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
+// v[l] + v[l ^ 16] in every lane l, on the vector ALU: v_permlane16_swap of v with
+// itself trades the odd rows (16 lanes each) of one copy for the even rows of the
+// other, so each lane holds its own value and its partner's (no LDS round trip, as a
+// lane shuffle through ds_bpermute would take).  Addition commutes, so every lane
+// gets the same bits as with the shuffle.
+__device__ __forceinline__ float xor16_sum(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto s = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// v[l] + v[l ^ 32] in every lane l (v_permlane32_swap: the upper half of one copy for
+// the lower half of the other).
+__device__ __forceinline__ float xor32_sum(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// The value of lane `src` (the same for the whole wave) in every lane (v_readlane).
+__device__ __forceinline__ float lane_value(float v, int src) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
 // Sum over the 64 lanes of a wave; every lane ends with the total.
 __device__ __forceinline__ float wave_sum(float v) {
-    v = row16_sum(v);
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
+    return xor32_sum(xor16_sum(row16_sum(v)));
 }
 
 // Sum over the 4 lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48) of a wave.
 __device__ __forceinline__ float group4_sum(float v) {
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
+    return xor32_sum(xor16_sum(v));
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves (no LDS

@@ -136,7 +136,7 @@ void k_slice_state_bf(const bf16_bits *__restrict__ x, const float *__restrict__
         // tokens: tokens 2 lane and 2 lane + 1, then a wave scan
         const float a0 = dq[0] * Al2, a01 = a0 + dq[1] * Al2;
         const float run = wave_inclusive_scan(a01);
-        const float aend = __shfl(run, 63, 64);
+        const float aend = lane_value(run, 63);
         if (w == 0) {
             // weight of token t: dt_t times the decay from t to the segment end (<= dt_t)
             const float c0 = run - a01 + a0;
