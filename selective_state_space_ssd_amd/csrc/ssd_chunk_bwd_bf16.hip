@@ -96,13 +96,24 @@ struct ChainPf {
 //        heads of one group at once (they share B, so one staged V serves both).
 // DIR 1: Gh_c for c = nc-1 .. 0 (as Gh^T tiles) from d_final, then d_init; it walks
 // one head.
-// With FH = 2 the LDS of a workgroup (76 KiB) stays under half of the CU's 160 KiB, so
+// With FH = 2 the LDS of a workgroup (72 KiB) stays under half of the CU's 160 KiB, so
 // two fit; the per-buffer decay factors live in the unused padding of the first AT row.
 template <int N, int FH>
 struct ChainLds {
     bf16_bits AT[2][FH][HP * RSA];  // [p][t] weighted u of each walked head, two buffers
-    bf16_bits VT[2][N * RS];        // [n][t] v, two buffers
+    bf16_bits VT[2][N * RSA];       // [n][t] v, two buffers
 };
+
+// The staged rows (64 tokens: eight 16-byte chunks of 8 tokens) hold chunk c of row r
+// at chunk position c ^ f(r).  The loaders store 4-byte token pairs, and the lanes of
+// a wave span 8 rows 36 dwords apart (16 rows for v), which without the swizzle fall
+// on 4 (v: 8 or 16) times fewer LDS banks than lanes; with it every store of a wave
+// touches 64 distinct banks.  f depends on r / 16 only, so it is uniform over each
+// 16-row MFMA operand read, which is a whole chunk (checked on the host for both
+// state sizes: placement and bank spread).
+__device__ __forceinline__ int swz_u(int r) { return 2 * ((r >> 4) & 3); }   // rows p of u
+template <int NG>
+__device__ __forceinline__ int swz_v(int r) { return (NG >= 16 ? r >> 4 : 2 * (r >> 4)) & 7; }
 
 template <int N, int DIR, int FH>
 __device__ __forceinline__ void chain_walk(
@@ -171,7 +182,9 @@ __device__ __forceinline__ void chain_walk(
                     const uint32_t ea = (&f.ua[k].x)[j >> 1], eb = (&f.ub[k].x)[j >> 1];
                     const float fa = (j & 1) ? bf16_hi(ea) : bf16_lo(ea);
                     const float fb = (j & 1) ? bf16_hi(eb) : bf16_lo(eb);
-                    *reinterpret_cast<uint32_t *>(&AT[buf][k][(8 * pgu + j) * RSA + 2 * tpu]) =
+                    const int p = 8 * pgu + j;
+                    *reinterpret_cast<uint32_t *>(
+                        &AT[buf][k][p * RSA + 8 * ((tpu >> 2) ^ swz_u(p)) + 2 * (tpu & 3)]) =
                         pack_bf16x2(fa * wa, fb * wb);
                 }
             }
@@ -185,7 +198,9 @@ __device__ __forceinline__ void chain_walk(
                         const uint32_t ea = (&f.va[k].x)[j >> 1], eb = (&f.vb[k].x)[j >> 1];
                         const uint32_t lo = (j & 1) ? (ea >> 16) : (ea & 0xffffu);
                         const uint32_t hi = (j & 1) ? (eb & 0xffff0000u) : (eb << 16);
-                        *reinterpret_cast<uint32_t *>(&VT[buf][(8 * ng + j) * RS + 2 * tp]) = lo | hi;
+                        const int n = 8 * ng + j;
+                        *reinterpret_cast<uint32_t *>(
+                            &VT[buf][n * RSA + 8 * ((tp >> 2) ^ swz_v<NG>(n)) + 2 * (tp & 3)]) = lo | hi;
                     }
                 }
             }
@@ -249,14 +264,17 @@ __device__ __forceinline__ void chain_walk(
 #pragma unroll
         for (int k = 0; k < WH; ++k) {
             const float al = al_sh[buf * FH + k];
-            const bf16_bits *at = AT[buf][k];
-            const bf16x8 a0 = lds16(at + (16 * sw + r16) * RSA + 8 * g4);
-            const bf16x8 a1 = lds16(at + (16 * sw + r16) * RSA + 32 + 8 * g4);
+            const bf16_bits *at = AT[buf][k] + (16 * sw + r16) * RSA;
+            const int fa = swz_u(16 * sw);
+            const bf16x8 a0 = lds16(at + 8 * (g4 ^ fa));
+            const bf16x8 a1 = lds16(at + 8 * ((4 + g4) ^ fa));
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
+                const bf16_bits *vr = vt + (16 * nt + r16) * RSA;
+                const int fv = swz_v<NG>(16 * nt);
                 f32x4 t = accP[k][nt] * al;
-                t = mfma_bf16(a0, lds16(vt + (16 * nt + r16) * RS + 8 * g4), t);
-                accP[k][nt] = mfma_bf16(a1, lds16(vt + (16 * nt + r16) * RS + 32 + 8 * g4), t);
+                t = mfma_bf16(a0, lds16(vr + 8 * (g4 ^ fv)), t);
+                accP[k][nt] = mfma_bf16(a1, lds16(vr + 8 * ((4 + g4) ^ fv)), t);
             }
         }
         __syncthreads();
@@ -280,7 +298,7 @@ __device__ __forceinline__ void chain_walk(
 // Both walks in one launch, so that the independent chains of every (head, batch) run
 // at the same time: workgroups 0 .. nfwd-1 walk forward over FH heads of one group
 // each (batch row, then head pair), the following b H workgroups walk one head each in
-// reverse.  With FH = 2 and 76 KiB of LDS per workgroup, all b H (1 + 1/FH) workgroups
+// reverse.  With FH = 2 and 72 KiB of LDS per workgroup, all b H (1 + 1/FH) workgroups
 // of the L=2048 layer (480) are resident at once on 256 CUs (two per CU), where one
 // head per forward walk (640) needed a second round.
 template <int N, int FH>
