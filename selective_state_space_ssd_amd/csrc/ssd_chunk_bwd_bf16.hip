@@ -109,8 +109,8 @@ struct ChainLds {
 // a wave span 8 rows 36 dwords apart (16 rows for v), which without the swizzle fall
 // on 4 (v: 8 or 16) times fewer LDS banks than lanes; with it every store of a wave
 // touches 64 distinct banks.  f depends on r / 16 only, so it is uniform over each
-// 16-row MFMA operand read, which is a whole chunk (checked on the host for both
-// state sizes: placement and bank spread).
+// 16-row MFMA operand read, which is a whole chunk (tests/test_chain_staging_layout.py
+// replays both sides' indexing on the host: placement and bank spread).
 __device__ __forceinline__ int swz_u(int r) { return 2 * ((r >> 4) & 3); }   // rows p of u
 template <int NG>
 __device__ __forceinline__ int swz_v(int r) { return (NG >= 16 ? r >> 4 : 2 * (r >> 4)) & 7; }
