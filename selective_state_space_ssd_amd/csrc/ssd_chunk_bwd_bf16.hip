@@ -104,16 +104,15 @@ struct ChainLds {
     bf16_bits VT[2][N * RSA];       // [n][t] v, two buffers
 };
 
-// The staged rows (64 tokens: eight 16-byte chunks of 8 tokens) hold chunk c of row r
-// at chunk position c ^ f(r).  The loaders store 4-byte token pairs, and the lanes of
-// a wave span 8 rows 36 dwords apart (16 rows for v), which without the swizzle fall
-// on 4 (v: 8 or 16) times fewer LDS banks than lanes; with it every store of a wave
-// touches 64 distinct banks.  f depends on r / 16 only, so it is uniform over each
-// 16-row MFMA operand read, which is a whole chunk (tests/test_chain_staging_layout.py
-// replays both sides' indexing on the host: placement and bank spread).
-__device__ __forceinline__ int swz_u(int r) { return 2 * ((r >> 4) & 3); }   // rows p of u
-template <int NG>
-__device__ __forceinline__ int swz_v(int r) { return (NG >= 16 ? r >> 4 : 2 * (r >> 4)) & 7; }
+// Transposed staging rows (64 tokens: eight 16-byte chunks of 8 tokens) hold chunk c
+// of row r at chunk position c ^ swz8(r).  A 4-byte LDS store of a wave is served in
+// two passes of 32 lanes over 32 banks (measured with the bank-conflict counter); the
+// 32 lanes of a pass store one token pair of 4 consecutive pairs (one chunk) in each
+// of 8 rows that lie a multiple of 32 dwords apart, so without the swizzle they meet
+// on 4 banks (8-way conflicts), and with it on 32.  An MFMA operand read is one
+// whole chunk per lane, found at its row's position (tests/test_chain_staging_layout.py
+// replays the stores and reads on the host: placement and bank spread).
+__device__ __forceinline__ int swz8(int r) { return (r >> 3) & 7; }
 
 template <int N, int DIR, int FH>
 __device__ __forceinline__ void chain_walk(
@@ -156,7 +155,7 @@ __device__ __forceinline__ void chain_walk(
 #pragma unroll
             for (int k = 0; k < kVItems; ++k) {
                 const int item = min(tid + k * kThreads, 32 * NG - 1);
-                const int tp = item / NG, ng = item % NG;
+                const int tp = (item >> 3) & 31, ng = (item & 7) | ((item >> 8) << 3);
                 const uint32_t vo = (uint32_t(2 * tp) * G + g) * N + 8 * ng;
                 f.va[k] = ld128(vr, vo * 2u);
                 f.vb[k] = ld128(vr, (vo + G * N) * 2u);
@@ -184,7 +183,7 @@ __device__ __forceinline__ void chain_walk(
                     const float fb = (j & 1) ? bf16_hi(eb) : bf16_lo(eb);
                     const int p = 8 * pgu + j;
                     *reinterpret_cast<uint32_t *>(
-                        &AT[buf][k][p * RSA + 8 * ((tpu >> 2) ^ swz_u(p)) + 2 * (tpu & 3)]) =
+                        &AT[buf][k][p * RSA + 8 * ((tpu >> 2) ^ swz8(p)) + 2 * (tpu & 3)]) =
                         pack_bf16x2(fa * wa, fb * wb);
                 }
             }
@@ -192,7 +191,8 @@ __device__ __forceinline__ void chain_walk(
             for (int k = 0; k < kVItems; ++k) {
                 const int item = tid + k * kThreads;
                 if (item < 32 * NG) {
-                    const int tp = item / NG, ng = item % NG;
+                    // lanes of a store pass: 4 token pairs (one chunk) x 8 channel groups
+                    const int tp = (item >> 3) & 31, ng = (item & 7) | ((item >> 8) << 3);
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         const uint32_t ea = (&f.va[k].x)[j >> 1], eb = (&f.vb[k].x)[j >> 1];
@@ -200,7 +200,7 @@ __device__ __forceinline__ void chain_walk(
                         const uint32_t hi = (j & 1) ? (eb & 0xffff0000u) : (eb << 16);
                         const int n = 8 * ng + j;
                         *reinterpret_cast<uint32_t *>(
-                            &VT[buf][n * RSA + 8 * ((tp >> 2) ^ swz_v<NG>(n)) + 2 * (tp & 3)]) = lo | hi;
+                            &VT[buf][n * RSA + 8 * ((tp >> 2) ^ swz8(n)) + 2 * (tp & 3)]) = lo | hi;
                     }
                 }
             }
@@ -265,13 +265,13 @@ __device__ __forceinline__ void chain_walk(
         for (int k = 0; k < WH; ++k) {
             const float al = al_sh[buf * FH + k];
             const bf16_bits *at = AT[buf][k] + (16 * sw + r16) * RSA;
-            const int fa = swz_u(16 * sw);
+            const int fa = swz8(16 * sw + r16);
             const bf16x8 a0 = lds16(at + 8 * (g4 ^ fa));
             const bf16x8 a1 = lds16(at + 8 * ((4 + g4) ^ fa));
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 const bf16_bits *vr = vt + (16 * nt + r16) * RSA;
-                const int fv = swz_v<NG>(16 * nt);
+                const int fv = swz8(16 * nt + r16);
                 f32x4 t = accP[k][nt] * al;
                 t = mfma_bf16(a0, lds16(vr + 8 * (g4 ^ fv)), t);
                 accP[k][nt] = mfma_bf16(a1, lds16(vr + 8 * ((4 + g4) ^ fv)), t);
@@ -536,7 +536,9 @@ __global__ __launch_bounds__(kChunkThreads) void k_bwd_chunk_bf(
                 for (int j = 0; j < 8; ++j) {
                     const int sh = 16 * (j & 1);
                     const uint32_t lo = ((&ra.x)[j >> 1] >> sh) & 0xffffu, hi = ((&rb.x)[j >> 1] >> sh) & 0xffffu;
-                    *reinterpret_cast<uint32_t *>(DYT + (8 * pgu + j) * RS + 2 * tpu) = lo | (hi << 16);
+                    const int p = 8 * pgu + j;   // chunk swizzle as in the state walks' staging
+                    *reinterpret_cast<uint32_t *>(DYT + p * RS + 8 * ((tpu >> 2) ^ swz8(p)) + 2 * (tpu & 3)) =
+                        lo | (hi << 16);
                 }
             }
         }
@@ -601,8 +603,9 @@ __global__ __launch_bounds__(kChunkThreads) void k_bwd_chunk_bf(
         // ---- dx^T[p][s] (rows p of block q) and U^T[p][s] = Gh[p] . B_s
         {
             const float Dh = D[h];
-            const bf16x8 e0 = lds16(DYT + (16 * q + r16) * RS + 8 * g4);
-            const bf16x8 e1 = lds16(DYT + (16 * q + r16) * RS + 32 + 8 * g4);
+            const int fd = swz8(16 * q + r16);
+            const bf16x8 e0 = lds16(DYT + (16 * q + r16) * RS + 8 * (g4 ^ fd));
+            const bf16x8 e1 = lds16(DYT + (16 * q + r16) * RS + 8 * ((4 + g4) ^ fd));
             const int p0 = 16 * q + 4 * g4;
 #pragma unroll
             for (int k = 0; k < 2; ++k) {

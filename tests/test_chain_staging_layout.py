@@ -1,54 +1,51 @@
-"""Host check of the LDS staging layout of the backward state walks (CPU only).
+"""Host check of the swizzled LDS staging of the backward kernels (CPU only).
 
-The loader waves of k_bwd_chain store 4-byte token pairs of the decay-weighted u
-(rows p, 64 per head) and of v (rows n, N of them) transposed into rows of 64 tokens
-with a row stride of 72 bf16 (36 dwords); chunk c (8 tokens, 16 bytes) of row r sits
-at chunk position c ^ f(r), with f(r) = 2 ((r / 16) mod 4) for u and
-(r / 16 or 2 (r / 16), by state size) mod 8 for v.  The state waves read 16-byte MFMA
-operands (row 16 t + lane % 16, chunk 4 kk + lane / 16).  This replays both sides'
-index arithmetic for N = 64 and 128: every read must find the token chunk it asks
-for, the decay factors kept in the padding of row 0 must not be overwritten, and the
-64 lanes of each store must fall on 64 distinct banks (64 banks of 4 bytes).
+The loader waves of k_bwd_chain store 4-byte token pairs of the decay-weighted u (rows
+p, 64 per head) and of v (rows n, N of them) transposed into rows of 64 tokens with a
+row stride of 72 bf16 (36 dwords); k_bwd_chunk_bf stores dy the same way with a row
+stride of 80 bf16.  Chunk c (8 tokens, 16 bytes) of row r sits at chunk position
+c ^ ((r / 8) mod 8).  The MFMA operand reads take one whole chunk per lane (row
+16 t + lane % 16, chunk 4 kk + lane / 16).  This replays both sides' index arithmetic
+for N = 64 and 128: every read must find the token chunk it asks for, the decay
+factors kept in the padding of row 0 must not be overwritten, and each pass of a
+4-byte store (32 lanes, as the LDS serves it: measured with the bank-conflict counter)
+must fall on 32 distinct banks of 4 bytes.
 """
 import pytest
 
-HP, RSA = 64, 72
-LOADERS = 256          # loader threads (4 waves)
+HP = 64
+LOADERS = 256          # loader threads of a state walk (4 waves)
 
 
-def swz_u(r):
-    return 2 * ((r >> 4) & 3)
+def swz8(r):
+    return (r >> 3) & 7
 
 
-def swz_v(r, NG):
-    return (r >> 4 if NG >= 16 else 2 * (r >> 4)) & 7
-
-
-def u_stores():
-    """(wave, j) -> list of (element offset, (p, token)) for the u staging stores."""
+def u_stores(stride, tid0=0):
+    """(wave, j) -> [(dword offset, (row, first token))] for the u (or dy) stores."""
     out = {}
-    for tid in range(LOADERS):
-        tpu, pgu = tid >> 3, tid & 7
+    for t in range(LOADERS):
+        tpu, pgu = t >> 3, t & 7
         for j in range(8):
             p = 8 * pgu + j
-            off = p * RSA + 8 * ((tpu >> 2) ^ swz_u(p)) + 2 * (tpu & 3)
-            out.setdefault((tid >> 6, j), []).append((off, (p, 2 * tpu)))
+            off = p * stride + 8 * ((tpu >> 2) ^ swz8(p)) + 2 * (tpu & 3)
+            out.setdefault((t >> 6, j), []).append((off, (p, 2 * tpu)))
     return out
 
 
-def v_stores(N):
+def v_stores(N, stride=72):
     NG = N // 8
     out = {}
-    for tid in range(LOADERS):
+    for t in range(LOADERS):
         for k in range((32 * NG + LOADERS - 1) // LOADERS):
-            item = tid + LOADERS * k
+            item = t + LOADERS * k
             if item >= 32 * NG:
                 continue
-            tp, ng = item // NG, item % NG
+            tp, ng = (item >> 3) & 31, (item & 7) | ((item >> 8) << 3)
             for j in range(8):
                 n = 8 * ng + j
-                off = n * RSA + 8 * ((tp >> 2) ^ swz_v(n, NG)) + 2 * (tp & 3)
-                out.setdefault((k, tid >> 6, j), []).append((off, (n, 2 * tp)))
+                off = n * stride + 8 * ((tp >> 2) ^ swz8(n)) + 2 * (tp & 3)
+                out.setdefault((k, t >> 6, j), []).append((off, (n, 2 * tp)))
     return out
 
 
@@ -62,29 +59,32 @@ def placed(stores):
     return cell
 
 
-@pytest.mark.parametrize("N", [64, 128])
-def test_reads_find_their_chunks(N):
-    NG = N // 8
-    cu, cv = placed(u_stores()), placed(v_stores(N))
-    assert len(cu) == HP * 64 and len(cv) == N * 64
-    assert not any(64 <= off < RSA for off in cu)        # row 0 padding: decay factors
+def check_reads(cell, rows, stride):
     for lane in range(64):
         r16, g4 = lane & 15, lane >> 4
         for kk in range(2):
             cc = 4 * kk + g4
-            for sw in range(4):                          # u: state wave sw, rows 16 sw + r16
-                p = 16 * sw + r16
-                base = p * RSA + 8 * (cc ^ swz_u(16 * sw))
-                assert [cu[base + e] for e in range(8)] == [(p, 8 * cc + e) for e in range(8)]
-            for nt in range(N // 16):                    # v: column tile nt
-                n = 16 * nt + r16
-                base = n * RSA + 8 * (cc ^ swz_v(16 * nt, NG))
-                assert [cv[base + e] for e in range(8)] == [(n, 8 * cc + e) for e in range(8)]
+            for t in range(rows // 16):
+                r = 16 * t + r16
+                base = r * stride + 8 * (cc ^ swz8(r))
+                assert [cell[base + e] for e in range(8)] == [(r, 8 * cc + e) for e in range(8)]
 
 
 @pytest.mark.parametrize("N", [64, 128])
-def test_every_store_spans_all_banks(N):
-    for stores in (u_stores(), v_stores(N)):
+def test_reads_find_their_chunks(N):
+    cu, cv = placed(u_stores(72)), placed(v_stores(N))
+    assert len(cu) == HP * 64 and len(cv) == N * 64
+    assert not any(64 <= off < 72 for off in cu)        # row 0 padding: decay factors
+    check_reads(cu, HP, 72)
+    check_reads(cv, N, 72)
+    cd = placed(u_stores(80))                            # dy^T of the chunk kernel
+    check_reads(cd, HP, 80)
+
+
+@pytest.mark.parametrize("N", [64, 128])
+def test_every_store_pass_spans_32_banks(N):
+    for stores in (u_stores(72), v_stores(N), u_stores(80)):
         for lst in stores.values():
-            banks = {(off // 2) % 64 for off, _ in lst}
-            assert len(lst) == 64 and len(banks) == 64
+            assert len(lst) == 64
+            for half in (lst[:32], lst[32:]):
+                assert len({(off // 2) % 32 for off, _ in half}) == 32
