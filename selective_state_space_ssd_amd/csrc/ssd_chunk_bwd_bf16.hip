@@ -480,16 +480,30 @@ __global__ __launch_bounds__(kChunkThreads) void k_bwd_chunk_bf(
                                                    gt, (tid + k * kChunkThreads) * 16, 0, 0));
     };
     load_gh(0);
+    // The LDS copy keeps element e of the tiles at gh_swz(e): within each tile the
+    // 16-byte groups of the 64-element row group m = (e / 64) mod 4 (lanes 16 m ..
+    // 16 m + 15 of the stored accumulator layout) are permuted by m.  The row reads
+    // below take one element per lane from the row groups of 4 lanes each, which
+    // without it meet on one bank per group (6 conflict cycles per read, measured with
+    // the bank-conflict counter) and with it spread over the banks; 8- and 16-byte
+    // pieces stay whole.
+    auto gh_swz = [](int e) { return e ^ (((e >> 6) & 3) << 3); };
     // 8 consecutive bf16 of the LDS copy at element stride 4: Gh[p][n0 .. n0+7] for the
     // lane's row p = 16 q + r16, n0 = 32 kq + 8 g4 (tile (n0 / 16) * 4 + q, lane
-    // 16 (r16 / 4) + n0 % 16 + j, element r16 % 4)
+    // 16 (r16 / 4) + n0 % 16 + j, element r16 % 4); the row group is m = r16 / 4, so
+    // element base + 8 j sits at base + 8 (j ^ m).  The addresses come from an opaque
+    // copy of the lane index, so they are formed at each use rather than held.
     auto gh_rows_p = [&](int kq) {
-        const int base = ((2 * kq + (g4 >> 1)) * 4 + q) * 256 + 4 * (16 * (r16 >> 2) + 8 * (g4 & 1)) +
-                         (r16 & 3);
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int rr = ln & 15, gg = ln >> 4, m = rr >> 2;
+        const int base = ((2 * kq + (gg >> 1)) * 4 + q) * 256 + 4 * (16 * m + 8 * (gg & 1)) + (rr & 3);
         uint32_t wv[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            wv[j] = uint32_t(GH[base + 8 * j]) | (uint32_t(GH[base + 8 * j + 4]) << 16);
+        for (int j = 0; j < 4; ++j) {
+            const int e = base + 8 * (j ^ m);
+            wv[j] = uint32_t(GH[e]) | (uint32_t(GH[e + 4]) << 16);
+        }
         return make_uint4(wv[0], wv[1], wv[2], wv[3]);
     };
     // Gh^T operand (rows n of tile ntw, k = p) from the LDS copy: the same two 8-byte
@@ -497,8 +511,8 @@ __global__ __launch_bounds__(kChunkThreads) void k_bwd_chunk_bf(
     auto gh_rows_n = [&](int kp) {
         const int tile = ntw * 4 + 2 * kp + (g4 >> 1);
         const int l = r16 + 32 * (g4 & 1);
-        const uint2 lo = *reinterpret_cast<const uint2 *>(GH + tile_off(tile, l));
-        const uint2 hi = *reinterpret_cast<const uint2 *>(GH + tile_off(tile, l + 16));
+        const uint2 lo = *reinterpret_cast<const uint2 *>(GH + gh_swz(tile_off(tile, l)));
+        const uint2 hi = *reinterpret_cast<const uint2 *>(GH + gh_swz(tile_off(tile, l + 16)));
         return make_uint4(lo.x, lo.y, hi.x, hi.y);
     };
 
@@ -514,7 +528,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_bwd_chunk_bf(
         // before its last barrier)
 #pragma unroll
         for (int k = 0; k < GPT; ++k)
-            *reinterpret_cast<uint4 *>(GH + (tid + k * kChunkThreads) * 8) = ghq[k];
+            *reinterpret_cast<uint4 *>(GH + gh_swz((tid + k * kChunkThreads) * 8)) = ghq[k];
         const float dreg = dnext;
         const float Ah = A[h];
         const float cs = wave_inclusive_scan(dreg * Ah * kLog2e);

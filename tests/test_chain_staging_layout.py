@@ -88,3 +88,58 @@ def test_every_store_pass_spans_32_banks(N):
             assert len(lst) == 64
             for half in (lst[:32], lst[32:]):
                 assert len({(off // 2) % 32 for off, _ in half}) == 32
+
+
+def gh_swz(e):
+    return e ^ (((e >> 6) & 3) << 3)
+
+
+@pytest.mark.parametrize("N", [64, 128])
+def test_gh_copy_swizzle(N):
+    """k_bwd_chunk_bf's LDS copy of a head's Gh^T tiles (accumulator layout: element
+    (p, n) of tile (n / 16) * 4 + p / 16 at 4 (16 ((p % 16) / 4) + n % 16) + p % 4)
+    is stored at gh_swz(e).  Both operand reads must find their elements, 16-byte copy
+    pieces and 8-byte read pieces must stay whole, and the 2-byte row reads of a
+    32-lane pass must not meet on a bank in more than one dword."""
+    total = 64 * N
+    assert sorted(gh_swz(e) for e in range(total)) == list(range(total))
+    for k in range(total // 8):
+        assert all(gh_swz(8 * k + i) == gh_swz(8 * k) + i for i in range(8))
+
+    def elem(p, n):
+        return ((n // 16) * 4 + p // 16) * 256 + 4 * (16 * ((p % 16) // 4) + n % 16) + p % 4
+
+    where = {gh_swz(elem(p, n)): (p, n) for p in range(64) for n in range(N)}
+    for q in range(4):
+        for kq in range(N // 32):
+            dwords = []
+            for lane in range(64):
+                rr, gg = lane & 15, lane >> 4
+                m = rr >> 2
+                base = ((2 * kq + (gg >> 1)) * 4 + q) * 256 + 4 * (16 * m + 8 * (gg & 1)) + (rr & 3)
+                p, n0 = 16 * q + rr, 32 * kq + 8 * gg
+                got = []
+                for j in range(4):
+                    e = base + 8 * (j ^ m)
+                    got += [where[e], where[e + 4]]
+                assert got == [(p, n0 + i) for i in range(8)]
+                dwords.append((base + 8 * (0 ^ m)) // 2)
+            for half in (dwords[:32], dwords[32:]):
+                banks = {}
+                for d in set(half):
+                    banks.setdefault(d % 32, set()).add(d)
+                assert max(len(v) for v in banks.values()) == 1
+    for ntw in range(N // 16):                     # rows n, k = p: two 8-byte pieces
+        for kp in range(2):
+            for lane in range(64):
+                r16, g4 = lane & 15, lane >> 4
+                tile = ntw * 4 + 2 * kp + (g4 >> 1)
+                l = r16 + 32 * (g4 & 1)
+                n = 16 * ntw + r16
+                p0 = 32 * kp + 8 * g4
+                got = []
+                for ll in (l, l + 16):
+                    e = gh_swz(tile * 256 + 4 * ll)
+                    assert gh_swz(tile * 256 + 4 * ll + 3) == e + 3
+                    got += [where[e + i] for i in range(4)]
+                assert got == [(p0 + i, n) for i in range(8)]
